@@ -1,0 +1,97 @@
+"""KV-cache append (scatter of this step's K/V rows into the cache), defined on the CPU.
+
+"[WebGPU] Add SparsePagedAttention", file summaries: the current K/V rows are scattered
+into the paged cache through a token-to-slot mapping derived from the block table.
+"[WebGPU] Add DynamicSparseAttention", Description: contiguous per-request caches are
+updated in place (alias-safe).  DynamicSparseAttention INT8 KV cache (onnxruntime PR
+33472), Key Changes table: INT8 caches carry per-channel fp32 key_scale / value_scale and
+the append quantises with them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .status import STATUS_CAPACITY, STATUS_BAD_BLOCK, STATUS_SHORT_KV
+
+
+def quantize_int8(x, s):
+    """Symmetric per-channel INT8 code of ``x`` with scale ``s``.
+
+    Reading taken (the pages give per-channel scales but no rounding rule): the value and
+    the scale are float32, the quotient is one IEEE float32 division, rounded to the
+    nearest integer with ties to even, then clamped to [-127, 127]; a NaN quotient gives 0.
+    Pinned by hand-worked values in the tests (ties, clamping, NaN).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    s = np.asarray(s, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        r = np.divide(x, s, dtype=np.float32)
+    r = np.rint(r)
+    r = np.where(np.isnan(r), np.float32(0), r)
+    r = np.clip(r, -127, 127)
+    return r.astype(np.int8)
+
+
+def _check_cu(cu, B, T):
+    if not (cu[0] == 0 and cu[B] == T and all(cu[b] <= cu[b + 1] for b in range(B))):
+        raise ValueError("oracle: kv_cache_append / attention need a well-formed cu_seqlens_q")
+
+
+def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
+                    block_table=None, block_size=None, key_scale=None, value_scale=None):
+    """Write row ``cu[b] + i`` of ``k_new`` / ``v_new`` (``[T, H_kv, D]``) at key position
+    ``p = (seqlens_k[b] + 1) - q_len_b + i`` of request ``b``.
+
+    Slot of position ``p``: paged cache ``[nb, bs, H_kv, D]`` ->
+    ``(block_table[b][p // bs], p % bs)``; contiguous cache ``[B, cap, H_kv, D]``
+    (``block_table is None``) -> ``(b, p)``.  Float caches store the row as is (same
+    dtype); INT8 caches store ``quantize_int8(row, scale[h][d])``.
+
+    Rows whose slot does not exist are skipped and flagged (parity unpinned): ``p < 0``
+    (STATUS_SHORT_KV), ``p // bs >= max_blocks_per_seq`` or ``p >= cap``
+    (STATUS_CAPACITY), a block id outside ``[0, nb)`` (STATUS_BAD_BLOCK).
+
+    Returns ``(k_cache_out, v_cache_out, status)``; the inputs are not modified.
+    """
+    cu = [int(x) for x in np.asarray(cu_seqlens_q).reshape(-1)]
+    sk = [int(x) for x in np.asarray(seqlens_k).reshape(-1)]
+    B = len(sk)
+    T = int(np.asarray(k_new).shape[0])
+    _check_cu(cu, B, T)
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    int8 = kc.dtype == np.int8
+    nb = kc.shape[0]
+    status = 0
+    for b in range(B):
+        q_len = cu[b + 1] - cu[b]
+        kv_len = sk[b] + 1
+        for i in range(q_len):
+            r = cu[b] + i
+            p = kv_len - q_len + i
+            if p < 0:
+                status |= STATUS_SHORT_KV
+                continue
+            if block_table is None:
+                if p >= kc.shape[1] or b >= nb:
+                    status |= STATUS_CAPACITY
+                    continue
+                blk, off = b, p
+            else:
+                bs = int(block_size)
+                lb = p // bs
+                if lb >= block_table.shape[1]:
+                    status |= STATUS_CAPACITY
+                    continue
+                blk = int(block_table[b][lb])
+                if blk < 0 or blk >= nb:
+                    status |= STATUS_BAD_BLOCK
+                    continue
+                off = p % bs
+            if int8:
+                kc[blk, off] = quantize_int8(np.asarray(k_new[r], np.float32), key_scale)
+                vc[blk, off] = quantize_int8(np.asarray(v_new[r], np.float32), value_scale)
+            else:
+                kc[blk, off] = k_new[r]
+                vc[blk, off] = v_new[r]
+    return kc, vc, status

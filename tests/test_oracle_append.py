@@ -1,0 +1,104 @@
+"""Pins of the oracle's cache append and INT8 code (CPU only).
+
+Against: hand-worked INT8 codes (golden fixture), the closed-form quantisation error
+bound, and the logical key sequence the inputs were laid out from (read back through
+the block table by this test's own walk).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_int8_hand_worked_codes():
+    with open(os.path.join(GOLDEN, "int8_codes.json")) as f:
+        data = json.load(f)
+    for case in data["cases"]:
+        x = np.float32(float(case["x"]))
+        s = np.float32(float(case["s"]))
+        assert int(oracle.quantize_int8(x, s)) == case["code"], case["note"]
+
+
+def test_int8_error_bound():
+    rng = np.random.default_rng(3)
+    s = rng.uniform(0.005, 0.02, size=4096).astype(np.float32)
+    x = (rng.uniform(-120, 120, size=4096) * s).astype(np.float32)
+    code = oracle.quantize_int8(x, s).astype(np.float64)
+    # in range: |code * s - x| <= s / 2 (plus float32 rounding of the quotient)
+    assert np.all(np.abs(code * s - x) <= 0.5 * s * (1 + 1e-6))
+
+
+def _walk(cache, block_table, bs, b, j):
+    if block_table is None:
+        return cache[b, j]
+    return cache[block_table[b][j // bs], j % bs]
+
+
+@pytest.mark.parametrize("contiguous", [False, True])
+def test_append_places_rows_at_their_positions(contiguous):
+    case = synth.paged_case(11, kv_lens=[5, 0, 40, 17], q_lens=[2, 0, 40, 1], H_q=4, H_kv=2,
+                            D=64, block_size=16, dtype=synth.F16, contiguous=contiguous,
+                            capacity=48, num_blocks=12, poison=True)
+    kc, vc, st = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, case.seqlens_k,
+                                        case.k_cache, case.v_cache, case.block_table, case.block_size)
+    assert st == 0
+    cu = case.cu_seqlens_q
+    for b in range(case.B):
+        q_len = int(cu[b + 1] - cu[b])
+        kv_len = int(case.seqlens_k[b]) + 1
+        for j in range(kv_len):
+            got_k = _walk(kc, case.block_table, case.block_size, b, j)
+            if j < kv_len - q_len:      # history untouched
+                want = _walk(case.k_cache, case.block_table, case.block_size, b, j)
+            else:                       # this step's rows
+                want = case.k_new[cu[b] + j - (kv_len - q_len)]
+            assert np.array_equal(got_k, want, equal_nan=True)
+    # nothing else changed: compare everything not written
+    written = np.zeros(kc.shape[:2], dtype=bool)
+    for b in range(case.B):
+        q_len = int(cu[b + 1] - cu[b])
+        kv_len = int(case.seqlens_k[b]) + 1
+        for j in range(kv_len - q_len, kv_len):
+            if case.block_table is None:
+                written[b, j] = True
+            else:
+                written[case.block_table[b][j // case.block_size], j % case.block_size] = True
+    assert np.array_equal(kc[~written], case.k_cache[~written], equal_nan=True)
+    assert np.array_equal(vc[~written], case.v_cache[~written], equal_nan=True)
+
+
+def test_append_int8_quantises_with_channel_scales():
+    case = synth.paged_case(12, kv_lens=[9, 33], q_lens=[3, 8], H_q=8, H_kv=2, D=128,
+                            block_size=16, dtype=synth.F16, cache_dtype=synth.I8)
+    kc, vc, st = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, case.seqlens_k,
+                                        case.k_cache, case.v_cache, case.block_table, case.block_size,
+                                        case.key_scale, case.value_scale)
+    assert st == 0
+    b, j, r = 1, 32, int(case.cu_seqlens_q[2]) - 1
+    code = _walk(kc, case.block_table, case.block_size, b, j).astype(np.float64)
+    x = case.k_new[r].astype(np.float64)
+    s = case.key_scale.astype(np.float64)
+    inside = np.abs(x / s) < 126.5
+    assert np.all(np.abs(code * s - x)[inside] <= 0.5 * s[inside] * (1 + 1e-6))
+    assert np.all(np.abs(code[~inside]) == 127)
+
+
+def test_append_skips_missing_slots():
+    case = synth.paged_case(13, kv_lens=[20, 20], q_lens=[4, 4], H_q=2, H_kv=1, D=64,
+                            block_size=16, dtype=synth.F32, num_blocks=4)
+    bt = case.block_table.copy()
+    bt[1, 1] = 99                      # block id beyond the pool
+    kc, vc, st = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, case.seqlens_k,
+                                        case.k_cache, case.v_cache, bt, case.block_size)
+    assert st & oracle.STATUS_BAD_BLOCK
+    sk = case.seqlens_k.copy()
+    sk[0] = 40                         # beyond 2 blocks of table
+    kc, vc, st = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, sk,
+                                        case.k_cache, case.v_cache, case.block_table, case.block_size)
+    assert st & oracle.STATUS_CAPACITY
