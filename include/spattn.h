@@ -1,0 +1,218 @@
+/*
+ * spattn.h - C ABI of the MI355X (gfx950) paged / selected-token attention library.
+ *
+ * Four operations and one sizing helper:
+ *
+ *   prepare_seqlens            per-request query/key lengths and per-token (request,
+ *                              position) derived on the device from cumulative offsets;
+ *   kv_cache_append            scatter of this step's K/V rows into the cache (INT8
+ *                              per-channel quantisation for INT8 caches);
+ *   paged_attention_fwd        causal attention over a paged (block table) or contiguous
+ *                              cache, GQA, local window, learned per-head sink;
+ *   sparse_attention_fwd       attention over selected cache rows (int32 indices padded
+ *                              with -1), or over a local window plus selected rows of an
+ *                              auxiliary store, with one joint softmax and sink;
+ *   attention_workspace_bytes  bytes of device workspace the attention calls need.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a device pointer unless stated otherwise; the caller owns
+ *   every buffer and keeps it alive until the enqueued work has finished.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Each call only enqueues
+ *   kernels on it: the library never allocates, frees, synchronises, copies between host
+ *   and device, or logs.  All calls can therefore be recorded into a HIP graph.
+ * - Return value: 0 = enqueued.  A negative value is a host-detectable argument error and
+ *   then NOTHING was enqueued: SPATTN_ERR_NULL (a required pointer is NULL),
+ *   SPATTN_ERR_SHAPE (a size is negative or inconsistent), SPATTN_ERR_DTYPE (dtype
+ *   combination not supported), SPATTN_ERR_UNSUPPORTED (e.g. is_causal = 0, head_dim not
+ *   64/128, H_q not a multiple of H_kv), SPATTN_ERR_WORKSPACE (workspace too small),
+ *   SPATTN_ERR_LAUNCH (the HIP launch itself failed; work before the failing launch of
+ *   the same call may have been enqueued).
+ * - `status` (optional, may be NULL): one int32 in device memory into which the kernels
+ *   OR the SPATTN_STATUS_* bits for malformed device-side data.  The caller clears it.
+ *   Affected keys are excluded and affected rows written as zeros; nothing is read or
+ *   written out of bounds.
+ * - Packed layouts (row-major): Q and out [T, H_q, D]; new K/V [T, H_kv, D]; paged cache
+ *   [num_blocks, block_size, H_kv, D] addressed through block_table [B,
+ *   max_blocks_per_seq] (int32, entries past a request's blocks unused); contiguous cache
+ *   [num_blocks >= B, capacity, H_kv, D] when block_table is NULL (then block_size is the
+ *   capacity and max_blocks_per_seq is ignored).
+ * - Row r of request b (cu_seqlens_q[b] <= r < cu_seqlens_q[b+1]) sits at key position
+ *   p = (seqlens_k[b] + 1) - q_len_b + (r - cu_seqlens_q[b]); seqlens_k[b] is the total
+ *   key count minus one (-1 = empty request).  cu_seqlens_q must be well formed
+ *   (0 = cu[0] <= ... <= cu[B] = T) for kv_cache_append and the attention calls; for a
+ *   malformed one their results are unspecified but every access stays in bounds.
+ *
+ * Citations are to web pages by title and section:
+ *   [PA]  "[WebGPU] Add PagedAttention metadata and GPT-OSS support" (onnxruntime PR 32277)
+ *   [SPA] "[WebGPU] Add SparsePagedAttention" (onnxruntime PR 32533)
+ *   [DSA] "[WebGPU] Add DynamicSparseAttention" (onnxruntime PR 32529)
+ *   [I8]  DynamicSparseAttention INT8 KV cache / grouped decode (onnxruntime PR 33472)
+ *   [LA]  "ai.onnx.LinearAttention" kernel page
+ */
+#ifndef SPATTN_H
+#define SPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SPATTN_API __attribute__((visibility("default")))
+#else
+#define SPATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define SPATTN_F32 0
+#define SPATTN_F16 1
+#define SPATTN_BF16 2
+#define SPATTN_I8 3 /* caches only */
+
+/* return codes */
+#define SPATTN_OK 0
+#define SPATTN_ERR_NULL (-1)
+#define SPATTN_ERR_SHAPE (-2)
+#define SPATTN_ERR_DTYPE (-3)
+#define SPATTN_ERR_UNSUPPORTED (-4)
+#define SPATTN_ERR_WORKSPACE (-5)
+#define SPATTN_ERR_LAUNCH (-6)
+
+/* device status bits (OR-ed into *status) */
+#define SPATTN_STATUS_BAD_CU (1 << 0)     /* cu_seqlens_q malformed, or past < 0 */
+#define SPATTN_STATUS_Q_BOUND (1 << 1)    /* q_len > max_seqlen_q: the request's rows are 0 */
+#define SPATTN_STATUS_K_BOUND (1 << 2)    /* key count > max_seqlen_k: the request's rows are 0 */
+#define SPATTN_STATUS_CAPACITY (1 << 3)   /* a needed position lies past the cache capacity */
+#define SPATTN_STATUS_BAD_BLOCK (1 << 4)  /* a needed block id is outside [0, num_blocks) */
+#define SPATTN_STATUS_BAD_INDEX (1 << 5)  /* a selected index (inside the count) is neither -1 nor in range */
+#define SPATTN_STATUS_BAD_COUNT (1 << 6)  /* a selected count outside [0, max_selected]; clamped */
+#define SPATTN_STATUS_SHORT_KV (1 << 7)   /* fewer keys than query rows: rows before key 0 see nothing */
+
+/* attention kinds for attention_workspace_bytes */
+#define SPATTN_KIND_PAGED 0
+#define SPATTN_KIND_SELECTED 1    /* sparse_attention_fwd mode 0 */
+#define SPATTN_KIND_LOCAL_AUX 2   /* sparse_attention_fwd mode 1 */
+
+/*
+ * prepare_seqlens - device-side sequence metadata ([PA] Description and Changes: exact
+ * per-request lengths are derived on the device from cumulative query offsets and past
+ * lengths, with no host readback; [PA] review finding T1 for the worked examples;
+ * [SPA] file summaries: per-token request/position metadata).
+ *
+ *   cu_seqlens_q [B+1] int32, past_seqlens [B] int32 (keys already cached), T = packed rows.
+ *   Outputs: seqlens_q[b] = cu[b+1] - cu[b]; seqlens_k[b] = past[b] + seqlens_q[b] - 1;
+ *   token_req[t] = request owning row t (or -1), token_pos[t] = its key position (or -1).
+ *   token_req / token_pos / status may be NULL.  Malformed cu (cu[0] != 0, decreasing,
+ *   cu[B] != T) or negative past: SPATTN_STATUS_BAD_CU, and each boundary is replaced by
+ *   the running maximum of cu[0..b] clamped to [0, T] (negative past by 0).
+ *   Limits: 0 <= B <= 8192, T >= 0.
+ */
+SPATTN_API int prepare_seqlens(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B, int T,
+                    int32_t* seqlens_q, int32_t* seqlens_k, int32_t* token_req,
+                    int32_t* token_pos, int32_t* status, void* stream);
+
+/*
+ * kv_cache_append - write this step's K/V rows into the cache in place ([SPA] file
+ * summaries: scatter of current K/V through the block table; [DSA] Description:
+ * alias-safe in-place update of contiguous caches; [I8] Key Changes: INT8 caches with
+ * per-channel key_scale / value_scale).
+ *
+ *   k_new, v_new [T, H_kv, D] of new_dtype; row r of request b goes to position
+ *   p = (seqlens_k[b] + 1) - q_len_b + i (seqlens_k as AFTER the append).
+ *   Float caches: cache_dtype == new_dtype, stored unchanged.  INT8 caches
+ *   (cache_dtype = SPATTN_I8, new_dtype F32/F16/BF16): code = clamp(rint_even(x / s),
+ *   -127, 127) with x, s float32 and an IEEE float32 division (NaN quotient -> 0);
+ *   key_scale / value_scale [H_kv, D] float32 are then required.
+ *   Rows without a slot are skipped: p < 0 (SHORT_KV), past the capacity (CAPACITY), a
+ *   block id outside [0, num_blocks) (BAD_BLOCK).
+ */
+SPATTN_API int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
+                    const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int B, int T,
+                    void* k_cache, void* v_cache, int cache_dtype, const int32_t* block_table,
+                    int max_blocks_per_seq, int block_size, int num_blocks,
+                    const float* key_scale, const float* value_scale, int H_kv, int D,
+                    int32_t* status, void* stream);
+
+/*
+ * attention_workspace_bytes - device workspace (bytes) an attention call with these
+ * arguments needs for its split-K partial softmax states ([SPA] file summaries and
+ * follow-up description: FP32 partial states merged by a finalize stage).  Pure host
+ * function; 0 means the call may pass workspace = NULL.  `kind` is SPATTN_KIND_*;
+ * max_seqlen_k is used by SPATTN_KIND_PAGED, max_selected by the sparse kinds,
+ * local_window by SPATTN_KIND_PAGED and SPATTN_KIND_LOCAL_AUX, dtype is the Q dtype.
+ * Returns (size_t)-1 for arguments the attention calls would reject.
+ */
+SPATTN_API size_t attention_workspace_bytes(int kind, int dtype, int B, int T, int max_seqlen_q,
+                                 int max_seqlen_k, int max_selected, int local_window,
+                                 int H_q, int H_kv, int D);
+
+/*
+ * paged_attention_fwd - causal attention of packed queries over a paged or contiguous
+ * KV cache ([PA] Description and Changes: paged attention with device-derived lengths,
+ * local-window masking and a learned head sink; [PA] Q2/Q3: window kept on the direct
+ * paged path, key loop started at the earliest window tile; [DSA] Description: GQA head
+ * mapping, joint FP32 softmax; [I8] Key Changes: INT8 per-channel K/V).
+ *
+ *   q, out [T, H_q, D] of dtype (F32, F16, BF16).  Cache dtype equals dtype, or is I8
+ *   (then key_scale / value_scale [H_kv, D] float32 are required).
+ *   Key set of the row at position p: cache positions lo..p with lo = max(0, p - W + 1)
+ *   when local_window = W > 0, else 0.  Query head h uses KV head h / (H_q / H_kv).
+ *   s = scale * <q, k> with scale = 1/sqrt(D) when 0 ([LA] Attributes).  The per-head
+ *   sink logit sinks[h] (float32 [H_q], may be NULL) joins the softmax maximum and
+ *   denominator only.  A row with no visible key is written as zeros.
+ *   max_seqlen_q / max_seqlen_k are host upper bounds of q_len / key count (a request
+ *   exceeding them gets zero rows and Q_BOUND / K_BOUND); they size the launch.
+ *   is_causal must be 1 ([PA] Changes: non-causal is rejected).  D in {64, 128}.
+ *   workspace: >= attention_workspace_bytes(SPATTN_KIND_PAGED, ...) bytes, 256-byte aligned.
+ */
+SPATTN_API int paged_attention_fwd(const void* q, int dtype, const void* k_cache, const void* v_cache,
+                        int cache_dtype, const int32_t* block_table, int max_blocks_per_seq,
+                        int block_size, int num_blocks, const float* key_scale,
+                        const float* value_scale, const int32_t* cu_seqlens_q,
+                        const int32_t* seqlens_k, int B, int T, int max_seqlen_q,
+                        int max_seqlen_k, int H_q, int H_kv, int D, float scale, int is_causal,
+                        int local_window, const float* sinks, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
+ * sparse_attention_fwd - attention over selected cache rows ([DSA] Description: selected
+ * main-cache mode and local-plus-auxiliary mode, guarded int32 indices, joint FP32 stable
+ * softmax with optional sink, shared auxiliary K/V storage; [DSA] review: the selection
+ * loop is bounded by the device count, not by max_selected; [SPA] overview: selected
+ * reads and local-plus-compressed attention over paged caches).
+ *
+ *   sel_idx [T, H_kv, max_selected] int32; sel_count [T, H_kv] int32 or NULL (NULL = all
+ *   max_selected entries); counts outside [0, max_selected] are clamped (BAD_COUNT).
+ *   Entry -1 is padding; any other entry outside its range is excluded (BAD_INDEX).
+ *   mode 0 (selected main): entry j is main-cache position j of the row's request, used
+ *     when 0 <= j < key count and j <= p (causal by position).  local_window must be <= 0.
+ *   mode 1 (local + auxiliary): main positions max(0, p - W + 1)..p (local_window = W > 0
+ *     required) plus auxiliary rows a (0 <= a < aux_len) of aux_k / aux_v, which are
+ *     [.., aux_len, H_kv, D] of aux_dtype (== dtype) with request b's rows starting at
+ *     element b * aux_batch_stride (0 = one store shared by every request); aux_k and
+ *     aux_v may alias.  Auxiliary rows carry no position and are not masked.
+ *   One softmax over every source and the sink; empty key set -> zero row.
+ *   Main-cache arguments as in paged_attention_fwd (paged or contiguous, F32/F16/BF16
+ *   equal to dtype, or I8 with scales).  D in {64, 128}.
+ *   workspace: >= attention_workspace_bytes(SPATTN_KIND_SELECTED or _LOCAL_AUX, ...).
+ */
+SPATTN_API int sparse_attention_fwd(const void* q, int dtype, int mode, const void* k_cache,
+                         const void* v_cache, int cache_dtype, const int32_t* block_table,
+                         int max_blocks_per_seq, int block_size, int num_blocks,
+                         const float* key_scale, const float* value_scale,
+                         const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int B, int T,
+                         int max_seqlen_q, const int32_t* sel_idx, const int32_t* sel_count,
+                         int max_selected, int local_window, const void* aux_k,
+                         const void* aux_v, int aux_dtype, int aux_len,
+                         int64_t aux_batch_stride, int H_q, int H_kv, int D, float scale,
+                         const float* sinks, void* out, void* workspace,
+                         size_t workspace_bytes, int32_t* status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPATTN_H */

@@ -1,0 +1,190 @@
+// C ABI entry points: argument validation on the host (nothing is enqueued when it fails),
+// then the launchers.  The declarations and their contracts are in include/spattn.h.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+using namespace spattn;
+
+namespace {
+
+bool float_dtype(int t) { return t == SPATTN_F32 || t == SPATTN_F16 || t == SPATTN_BF16; }
+
+// Shared checks of a KV cache description; returns SPATTN_OK or an error code.
+int check_cache(const void* k_cache, const void* v_cache, int dtype, int cache_dtype,
+                const int32_t* block_table, int max_blocks, int block_size, int num_blocks,
+                const float* key_scale, const float* value_scale, int B, int H_kv, int D) {
+  if (k_cache == nullptr || v_cache == nullptr) return SPATTN_ERR_NULL;
+  if (cache_dtype == SPATTN_I8) {
+    if (key_scale == nullptr || value_scale == nullptr) return SPATTN_ERR_NULL;
+  } else if (cache_dtype != dtype) {
+    return SPATTN_ERR_DTYPE;
+  }
+  if (block_size < 1 || num_blocks < 1) return SPATTN_ERR_SHAPE;
+  if (block_table != nullptr) {
+    if (max_blocks < 1) return SPATTN_ERR_SHAPE;
+  } else if (num_blocks < B) {
+    return SPATTN_ERR_SHAPE;
+  }
+  // cache rows (of D elements) are indexed with 32-bit integers
+  if ((int64_t)num_blocks * block_size * H_kv >= (int64_t)1 << 31) return SPATTN_ERR_SHAPE;
+  (void)D;
+  return SPATTN_OK;
+}
+
+int check_heads(int H_q, int H_kv, int D) {
+  if (H_q < 1 || H_kv < 1) return SPATTN_ERR_SHAPE;
+  if (H_q % H_kv != 0) return SPATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return SPATTN_ERR_UNSUPPORTED;
+  return SPATTN_OK;
+}
+
+float resolve_scale(float scale, int D) { return scale == 0.0f ? 1.0f / sqrtf((float)D) : scale; }
+
+}  // namespace
+
+extern "C" {
+
+int prepare_seqlens(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B, int T,
+                    int32_t* seqlens_q, int32_t* seqlens_k, int32_t* token_req,
+                    int32_t* token_pos, int32_t* status, void* stream) {
+  if (cu_seqlens_q == nullptr) return SPATTN_ERR_NULL;
+  if (B > 0 && (past_seqlens == nullptr || seqlens_q == nullptr || seqlens_k == nullptr))
+    return SPATTN_ERR_NULL;
+  if (B < 0 || T < 0) return SPATTN_ERR_SHAPE;
+  return launch_prepare_seqlens(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k, token_req,
+                                token_pos, status, (hipStream_t)stream);
+}
+
+int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
+                    const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int B, int T,
+                    void* k_cache, void* v_cache, int cache_dtype, const int32_t* block_table,
+                    int max_blocks_per_seq, int block_size, int num_blocks,
+                    const float* key_scale, const float* value_scale, int H_kv, int D,
+                    int32_t* status, void* stream) {
+  if (B < 0 || T < 0 || H_kv < 1 || D < 8 || D % 8 != 0) return SPATTN_ERR_SHAPE;
+  if (!float_dtype(new_dtype)) return SPATTN_ERR_DTYPE;
+  if (cache_dtype != SPATTN_I8 && !float_dtype(cache_dtype)) return SPATTN_ERR_DTYPE;
+  if (T == 0) return SPATTN_OK;
+  if (B == 0) return SPATTN_ERR_SHAPE;
+  if (k_new == nullptr || v_new == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
+    return SPATTN_ERR_NULL;
+  int rc = check_cache(k_cache, v_cache, new_dtype, cache_dtype, block_table, max_blocks_per_seq,
+                       block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+  return launch_kv_cache_append(k_new, v_new, new_dtype, cu_seqlens_q, seqlens_k, B, T, k_cache,
+                                v_cache, cache_dtype, block_table, max_blocks_per_seq, block_size,
+                                num_blocks, key_scale, value_scale, H_kv, D, status,
+                                (hipStream_t)stream);
+}
+
+size_t attention_workspace_bytes(int kind, int dtype, int B, int T, int max_seqlen_q,
+                                 int max_seqlen_k, int max_selected, int local_window,
+                                 int H_q, int H_kv, int D) {
+  const size_t bad = (size_t)-1;
+  if (kind < SPATTN_KIND_PAGED || kind > SPATTN_KIND_LOCAL_AUX) return bad;
+  if (!float_dtype(dtype)) return bad;
+  if (B < 0 || T < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_selected < 0) return bad;
+  if (check_heads(H_q, H_kv, D) != SPATTN_OK) return bad;
+  if (kind == SPATTN_KIND_LOCAL_AUX && local_window <= 0) return bad;
+  if (kind == SPATTN_KIND_PAGED && use_prefill_path(kind, dtype, max_seqlen_q)) return 0;
+  return make_split_plan(kind, dtype, B, T, max_seqlen_q, max_seqlen_k, max_selected,
+                         local_window, H_q, H_kv, D).ws_bytes;
+}
+
+int paged_attention_fwd(const void* q, int dtype, const void* k_cache, const void* v_cache,
+                        int cache_dtype, const int32_t* block_table, int max_blocks_per_seq,
+                        int block_size, int num_blocks, const float* key_scale,
+                        const float* value_scale, const int32_t* cu_seqlens_q,
+                        const int32_t* seqlens_k, int B, int T, int max_seqlen_q,
+                        int max_seqlen_k, int H_q, int H_kv, int D, float scale, int is_causal,
+                        int local_window, const float* sinks, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t* status, void* stream) {
+  if (!float_dtype(dtype)) return SPATTN_ERR_DTYPE;
+  if (is_causal != 1) return SPATTN_ERR_UNSUPPORTED;
+  int rc = check_heads(H_q, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+  if (B < 0 || T < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return SPATTN_ERR_SHAPE;
+  if (T == 0) return SPATTN_OK;
+  if (B == 0) return SPATTN_ERR_SHAPE;
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
+    return SPATTN_ERR_NULL;
+  rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
+                   block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+
+  AttnArgs a{};
+  a.kind = SPATTN_KIND_PAGED;
+  a.q = q; a.dtype = dtype; a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+  a.block_table = block_table; a.max_blocks = max_blocks_per_seq; a.block_size = block_size;
+  a.num_blocks = num_blocks; a.key_scale = key_scale; a.value_scale = value_scale;
+  a.cu = cu_seqlens_q; a.seqlens_k = seqlens_k; a.B = B; a.T = T;
+  a.max_q = max_seqlen_q; a.max_k = max_seqlen_k;
+  a.window = local_window > 0 ? local_window : 0;
+  a.H_q = H_q; a.H_kv = H_kv; a.D = D;
+  a.scale = resolve_scale(scale, D);
+  a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
+  hipStream_t st = (hipStream_t)stream;
+  if (use_prefill_path(a.kind, dtype, max_seqlen_q)) return launch_prefill_attention(a, st);
+  const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, max_seqlen_k, 0,
+                                         a.window, H_q, H_kv, D);
+  if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
+    return SPATTN_ERR_WORKSPACE;
+  return launch_split_attention(a, plan, st);
+}
+
+int sparse_attention_fwd(const void* q, int dtype, int mode, const void* k_cache,
+                         const void* v_cache, int cache_dtype, const int32_t* block_table,
+                         int max_blocks_per_seq, int block_size, int num_blocks,
+                         const float* key_scale, const float* value_scale,
+                         const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int B, int T,
+                         int max_seqlen_q, const int32_t* sel_idx, const int32_t* sel_count,
+                         int max_selected, int local_window, const void* aux_k,
+                         const void* aux_v, int aux_dtype, int aux_len,
+                         int64_t aux_batch_stride, int H_q, int H_kv, int D, float scale,
+                         const float* sinks, void* out, void* workspace,
+                         size_t workspace_bytes, int32_t* status, void* stream) {
+  if (!float_dtype(dtype)) return SPATTN_ERR_DTYPE;
+  if (mode != 0 && mode != 1) return SPATTN_ERR_UNSUPPORTED;
+  if (mode == 0 && local_window > 0) return SPATTN_ERR_UNSUPPORTED;
+  if (mode == 1 && local_window <= 0) return SPATTN_ERR_UNSUPPORTED;
+  int rc = check_heads(H_q, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+  if (B < 0 || T < 0 || max_seqlen_q < 0 || max_selected < 0) return SPATTN_ERR_SHAPE;
+  if (T == 0) return SPATTN_OK;
+  if (B == 0) return SPATTN_ERR_SHAPE;
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
+    return SPATTN_ERR_NULL;
+  if (max_selected > 0 && sel_idx == nullptr) return SPATTN_ERR_NULL;
+  rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
+                   block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+  if (mode == 1) {
+    if (aux_k == nullptr || aux_v == nullptr) return SPATTN_ERR_NULL;
+    if (aux_dtype != dtype) return SPATTN_ERR_DTYPE;
+    if (aux_len < 0 || aux_batch_stride < 0 || aux_batch_stride % D != 0) return SPATTN_ERR_SHAPE;
+    const int64_t rows = (int64_t)(B - 1) * (aux_batch_stride / D) + (int64_t)aux_len * H_kv;
+    if (rows >= (int64_t)1 << 31) return SPATTN_ERR_SHAPE;
+  }
+  AttnArgs a{};
+  a.kind = mode == 0 ? SPATTN_KIND_SELECTED : SPATTN_KIND_LOCAL_AUX;
+  a.q = q; a.dtype = dtype; a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+  a.block_table = block_table; a.max_blocks = max_blocks_per_seq; a.block_size = block_size;
+  a.num_blocks = num_blocks; a.key_scale = key_scale; a.value_scale = value_scale;
+  a.cu = cu_seqlens_q; a.seqlens_k = seqlens_k; a.B = B; a.T = T;
+  a.max_q = max_seqlen_q; a.max_k = -1;
+  a.sel_idx = sel_idx; a.sel_count = sel_count; a.max_selected = max_selected;
+  a.window = mode == 1 ? local_window : 0;
+  a.aux_k = aux_k; a.aux_v = aux_v; a.aux_len = aux_len; a.aux_stride = aux_batch_stride;
+  a.H_q = H_q; a.H_kv = H_kv; a.D = D;
+  a.scale = resolve_scale(scale, D);
+  a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
+  const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, 0, max_selected,
+                                         a.window, H_q, H_kv, D);
+  if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
+    return SPATTN_ERR_WORKSPACE;
+  return launch_split_attention(a, plan, (hipStream_t)stream);
+}
+
+}  // extern "C"

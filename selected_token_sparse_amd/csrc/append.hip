@@ -1,0 +1,106 @@
+// kv_cache_append: scatter this step's K/V rows into the cache in place ("[WebGPU] Add
+// SparsePagedAttention", file summaries: scatter through the token-to-slot mapping;
+// "[WebGPU] Add DynamicSparseAttention", Description: alias-safe in-place update of
+// contiguous caches; INT8 per-channel quantisation per the Key Changes table of the
+// DynamicSparseAttention INT8 KV cache page).
+//
+// A cache row (all KV heads of one position) is contiguous in both the packed input and
+// the cache, so a float append is a 16-byte vector copy per lane; an INT8 append turns
+// eight input elements into eight codes per lane.
+#include "common.h"
+#include "launch.h"
+
+namespace spattn {
+
+constexpr int kAppendThreads = 256;
+
+__device__ __forceinline__ int8_t quantize_one(float x, float s) {
+  float r = __builtin_rintf(x / s);  // IEEE float32 division, ties to even
+  if (r != r) return 0;              // NaN quotient
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int8_t)(int)r;
+}
+
+template <typename NewT>
+__device__ __forceinline__ void quantize8(const NewT* __restrict__ src, const float* __restrict__ scale,
+                                          int8_t* __restrict__ dst) {
+  // eight consecutive elements of one KV head (D is a multiple of 8)
+  union { int8_t c[8]; int2 v; } u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) u.c[e] = quantize_one(to_f32(src[e]), scale[e]);
+  *reinterpret_cast<int2*>(dst) = u.v;
+}
+
+template <typename NewT, bool kInt8>
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
+    const NewT* __restrict__ k_new, const NewT* __restrict__ v_new, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ seqlens_k, int B, void* __restrict__ k_cache,
+    void* __restrict__ v_cache, CacheDesc cd, const float* __restrict__ key_scale,
+    const float* __restrict__ value_scale, int32_t* status) {
+  const int r = blockIdx.x;
+  int flags = 0;
+  const int b = find_request(cu, B, r);
+  int64_t dst = -1;
+  if (b < 0) {
+    flags |= SPATTN_STATUS_BAD_CU;
+  } else {
+    const int q_len = cu[b + 1] - cu[b];
+    const int kv_len = seqlens_k[b] + 1;
+    const int p = kv_len - q_len + (r - cu[b]);
+    if (p < 0) flags |= SPATTN_STATUS_SHORT_KV;
+    else dst = cache_row(cd, b, p, 0, flags);
+  }
+  if (threadIdx.x == 0) raise_status(status, flags);
+  if (dst < 0) return;
+  const int row_elems = cd.H_kv * cd.D;
+  const int64_t src = (int64_t)r * row_elems;
+  if constexpr (kInt8) {
+    int8_t* kc = reinterpret_cast<int8_t*>(k_cache) + dst;
+    int8_t* vc = reinterpret_cast<int8_t*>(v_cache) + dst;
+    for (int e = threadIdx.x * 8; e < row_elems; e += kAppendThreads * 8) {
+      quantize8(k_new + src + e, key_scale + e, kc + e);
+      quantize8(v_new + src + e, value_scale + e, vc + e);
+    }
+  } else {
+    constexpr int kPer = 16 / sizeof(NewT);
+    NewT* kc = reinterpret_cast<NewT*>(k_cache) + dst;
+    NewT* vc = reinterpret_cast<NewT*>(v_cache) + dst;
+    for (int e = threadIdx.x * kPer; e < row_elems; e += kAppendThreads * kPer) {
+      store16(kc + e, load16(k_new + src + e));
+      store16(vc + e, load16(v_new + src + e));
+    }
+  }
+}
+
+int launch_kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
+                           const int32_t* cu, const int32_t* seqlens_k, int B, int T,
+                           void* k_cache, void* v_cache, int cache_dtype,
+                           const int32_t* block_table, int max_blocks, int block_size,
+                           int num_blocks, const float* key_scale, const float* value_scale,
+                           int H_kv, int D, int32_t* status, hipStream_t stream) {
+  if (T == 0) return SPATTN_OK;
+  CacheDesc cd;
+  cd.block_table = block_table;
+  cd.max_blocks = max_blocks;
+  cd.block_size = block_size;
+  cd.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(block_size) : -1;
+  cd.num_blocks = num_blocks;
+  cd.H_kv = H_kv;
+  cd.D = D;
+  dim3 grid(T), block(kAppendThreads);
+  const bool i8 = cache_dtype == SPATTN_I8;
+#define SPATTN_APPEND(NT, I8)                                                              \
+  hipLaunchKernelGGL((kv_append_kernel<NT, I8>), grid, block, 0, stream,                   \
+                     reinterpret_cast<const NT*>(k_new), reinterpret_cast<const NT*>(v_new), \
+                     cu, seqlens_k, B, k_cache, v_cache, cd, key_scale, value_scale, status)
+  switch (new_dtype) {
+    case SPATTN_F32: if (i8) SPATTN_APPEND(float, true); else SPATTN_APPEND(float, false); break;
+    case SPATTN_F16: if (i8) SPATTN_APPEND(f16, true); else SPATTN_APPEND(f16, false); break;
+    case SPATTN_BF16: if (i8) SPATTN_APPEND(bf16, true); else SPATTN_APPEND(bf16, false); break;
+    default: return SPATTN_ERR_DTYPE;
+  }
+#undef SPATTN_APPEND
+  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_ERR_LAUNCH;
+}
+
+}  // namespace spattn

@@ -1,0 +1,145 @@
+// Device-side helpers shared by the gfx950 kernels of this library: element types and
+// conversions, 16-byte vector loads, MFMA operand types, wave reductions, status flags
+// and per-row metadata.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spattn.h"
+
+namespace spattn {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------------------------------
+// element conversions
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(int8_t x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// ---------------------------------------------------------------------------------------
+// status flags (only written when a malformed input is seen)
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void raise_status(int32_t* status, int bits) {
+  if (status != nullptr && bits != 0) atomicOr(status, bits);
+}
+
+// ---------------------------------------------------------------------------------------
+// wave64 reductions over lanes that differ in bits 4 and 5 (the four 16-lane groups)
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float xor_sum(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+
+// exp2 that maps -inf to 0 and never produces NaN from (-inf) - (-inf): callers pass
+// differences whose minuend is finite or -inf.
+__device__ __forceinline__ float exp2_safe(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------------------
+// Request lookup for a packed row.  Returns the request b with cu[b] <= r < cu[b+1], found
+// by binary search (exact for a well-formed cu), or -1 if the candidate does not own the
+// row.  Uniform across the workgroup when r is.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int find_request(const int32_t* __restrict__ cu, int B, int r) {
+  int lo = 0, hi = B - 1;  // largest b in [0, B) with cu[b] <= r
+  if (B <= 0 || cu[0] > r) return -1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  if (r < cu[lo + 1]) return lo;
+  return -1;
+}
+
+// Per-row view used by every attention kernel.
+struct RowInfo {
+  int b;        // request, or -1 when the row is dead (zero output)
+  int q_len;
+  int kv_len;   // total key count of the request
+  int p;        // key position of the row
+};
+
+// Resolves row r; applies the host-bound rules (q_len <= max_q, kv_len <= max_k when
+// max_k >= 0) and reports malformed rows through `flags` (status bits).
+__device__ __forceinline__ RowInfo resolve_row(const int32_t* __restrict__ cu,
+                                               const int32_t* __restrict__ seqlens_k, int B,
+                                               int r, int max_q, int max_k, int& flags) {
+  RowInfo ri;
+  ri.b = find_request(cu, B, r);
+  ri.q_len = 0; ri.kv_len = 0; ri.p = -1;
+  if (ri.b < 0) { flags |= SPATTN_STATUS_BAD_CU; return ri; }
+  const int c0 = cu[ri.b];
+  ri.q_len = cu[ri.b + 1] - c0;
+  ri.kv_len = seqlens_k[ri.b] + 1;
+  if (ri.q_len > max_q) { flags |= SPATTN_STATUS_Q_BOUND; ri.b = -1; return ri; }
+  if (max_k >= 0 && ri.kv_len > max_k) { flags |= SPATTN_STATUS_K_BOUND; ri.b = -1; return ri; }
+  if (ri.kv_len < ri.q_len) flags |= SPATTN_STATUS_SHORT_KV;
+  ri.p = ri.kv_len - ri.q_len + (r - c0);
+  return ri;
+}
+
+// ---------------------------------------------------------------------------------------
+// Cache addressing: paged [nb, bs, H_kv, D] through a block table, or contiguous
+// [nb >= B, cap, H_kv, D].  Returns the element offset of (position j, KV head c) row, or
+// -1 (with a status bit in `flags`) when the slot does not exist.
+// ---------------------------------------------------------------------------------------
+struct CacheDesc {
+  const int32_t* block_table;  // nullptr -> contiguous
+  int max_blocks;              // table width
+  int block_size;              // block size or capacity
+  int bs_shift;                // log2(block_size) when a power of two, else -1
+  int num_blocks;
+  int H_kv;
+  int D;
+};
+
+__device__ __forceinline__ int64_t cache_row(const CacheDesc& cd, int b, int j, int c, int& flags) {
+  int blk, off;
+  if (cd.block_table == nullptr) {
+    if (j >= cd.block_size || b >= cd.num_blocks) { flags |= SPATTN_STATUS_CAPACITY; return -1; }
+    blk = b; off = j;
+  } else {
+    int lb, o;
+    if (cd.bs_shift >= 0) { lb = j >> cd.bs_shift; o = j & (cd.block_size - 1); }
+    else { lb = j / cd.block_size; o = j - lb * cd.block_size; }
+    if (lb >= cd.max_blocks) { flags |= SPATTN_STATUS_CAPACITY; return -1; }
+    blk = cd.block_table[(int64_t)b * cd.max_blocks + lb];
+    if (blk < 0 || blk >= cd.num_blocks) { flags |= SPATTN_STATUS_BAD_BLOCK; return -1; }
+    off = o;
+  }
+  return (((int64_t)blk * cd.block_size + off) * cd.H_kv + c) * cd.D;
+}
+
+// ---------------------------------------------------------------------------------------
+// 16-byte loads / stores
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ i32x4 load16(const void* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, i32x4 v) { *reinterpret_cast<i32x4*>(p) = v; }
+
+}  // namespace spattn

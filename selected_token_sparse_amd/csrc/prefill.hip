@@ -1,0 +1,386 @@
+// MFMA prefill: causal paged attention for long query blocks, fp16/bf16 operands, fp32
+// softmax and accumulation ("[WebGPU] Add PagedAttention metadata and GPT-OSS support":
+// paged attention with local window and learned sink; review finding Q3: start the key
+// loop at the tile holding the earliest window key of the workgroup's first row, so the
+// traversal is about one window plus one query tile instead of the whole history).
+//
+// Workgroup = 4 waves = 32*RW query rows x HW query heads of one KV head (RW * HW = 4);
+// every wave owns 32 rows of one head.  All waves share each 32-key K/V tile, staged
+// through LDS (two stages, one barrier per tile).  Per wave and tile:
+//   S^T[32 keys x 32 rows] = K Q^T      (v_mfma_f32_32x32x16, D/16 steps)
+//   online softmax per row (a lane holds 16 keys of its row; one cross-lane exchange)
+//   O^T[D x 32 rows] += V^T P^T         (V^T from LDS via ds_read_b64_tr_b16)
+// Masks: key j is visible to the row at position p when lo(p) <= j <= p and its cache
+// slot exists.  The sink joins the normaliser once at the end of the row.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace spattn {
+
+constexpr int kPfThreads = 256;
+constexpr int kPfTile = 32;
+
+template <typename T> struct Op32;
+template <> struct Op32<f16> { typedef f16x8 v8; typedef f16x4 v4; };
+template <> struct Op32<bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+struct PrefillParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* key_scale;
+  const float* value_scale;
+  const int32_t* cu;
+  const int32_t* seqlens_k;
+  const float* sinks;
+  void* out;
+  int32_t* status;
+  CacheDesc cd;
+  int B, T, H_q, H_kv, D, group;
+  int max_q, max_k, window;
+  int n_rt;        // row tiles per request (host bound)
+  int n_hg;        // head groups per KV head
+  int total;       // workgroups
+  float scale_log2;
+};
+
+template <int D>
+struct PfLds {
+  static constexpr int kKld = D + 8;     // K tile row (elements)
+  static constexpr int kVld = D + 16;    // V tile row (elements)
+  static constexpr int kKBytes = kPfTile * kKld * 2;
+  static constexpr int kVBytes = kPfTile * kVld * 2;
+  static constexpr int kStage = kKBytes + kVBytes + kPfTile * 4;  // + key validity words
+  static constexpr int kTotal = 2 * kStage;
+};
+
+template <typename QT, typename KT, int D, int RW>
+__global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
+  constexpr int HW = 4 / RW;
+  constexpr int KC = D / 16;          // QK k-steps
+  constexpr int MT = D / 32;          // PV m-tiles
+  constexpr int CH = D / 8;           // 8-element chunks per row
+  constexpr int NCH = kPfTile * CH / kPfThreads;
+  constexpr bool kI8 = sizeof(KT) == 1;
+  typedef typename std::conditional<kI8, f16, QT>::type OpT;
+  typedef typename Op32<OpT>::v8 V8;
+  typedef typename Op32<OpT>::v4 V4;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rw = wave / HW;
+  const int hw = wave - rw * HW;
+  const int h = lane >> 5;            // lane half
+  const int l32 = lane & 31;
+
+  // XCD-aware order: consecutive logical workgroups land on the same XCD
+  int logical;
+  {
+    const int i = blockIdx.x;
+    const int n = P.total;
+    const int x = i & 7, k = i >> 3;
+    const int q = n >> 3, rem = n & 7;
+    logical = x * q + min(x, rem) + k;
+  }
+  const int hg = logical % P.n_hg;
+  int t = logical / P.n_hg;
+  const int c = t % P.H_kv;
+  t /= P.H_kv;
+  const int b = t % P.B;
+  const int rt = P.n_rt - 1 - t / P.B;   // heaviest (last) row tiles first
+
+  int flags = 0;
+  const int c0 = P.cu[b];
+  int q_len = P.cu[b + 1] - c0;
+  const int kv_len = P.seqlens_k[b] + 1;
+  bool dead = false;
+  if (q_len < 0 || c0 < 0 || c0 + q_len > P.T) { flags |= SPATTN_STATUS_BAD_CU; q_len = 0; }
+  else if (q_len > P.max_q) { flags |= SPATTN_STATUS_Q_BOUND; dead = true; }
+  else if (kv_len > P.max_k) { flags |= SPATTN_STATUS_K_BOUND; dead = true; }
+  else if (kv_len < q_len) flags |= SPATTN_STATUS_SHORT_KV;
+
+  const int head_local = hg * HW + hw;
+  const bool head_ok = head_local < P.group;
+  const int head = c * P.group + head_local;
+
+  if (dead) {
+    // the request's rows are zero; rows past the host bound are covered by striding
+    if (head_ok) {
+      for (int i = rt * 32 * RW + rw * 32 + (lane & 31); i < q_len; i += P.n_rt * 32 * RW) {
+        QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + i) * P.H_q + head) * D;
+        for (int d = h; d < D; d += 2) o[d] = from_f32<QT>(0.f);
+      }
+    }
+    if (tid == 0) raise_status(P.status, flags);
+    return;
+  }
+  const int row_base = rt * 32 * RW;                 // first row (within the request) of the WG
+  if (row_base >= q_len) { if (tid == 0) raise_status(P.status, flags); return; }
+  const int wg_rows = min(32 * RW, q_len - row_base);
+  const int pos0 = kv_len - q_len;                   // position of row 0
+  const int p_first = pos0 + row_base;
+  const int p_last = pos0 + row_base + wg_rows - 1;
+  const int j_lo = P.window > 0 ? max(0, p_first - P.window + 1) : 0;
+  const int j_hi = min(p_last, kv_len - 1);
+  // this wave's rows
+  const int wrow0 = row_base + rw * 32;
+  const int my_row = wrow0 + l32;                    // row (within the request) of this lane
+  const bool row_ok = my_row < q_len && head_ok;
+  const int my_p = pos0 + my_row;
+  const int my_lo = P.window > 0 ? my_p - P.window + 1 : INT32_MIN;
+  const int wave_rows = max(0, min(32, q_len - wrow0));
+  const int w_p_first = pos0 + wrow0;
+  const int w_p_last = pos0 + wrow0 + wave_rows - 1;
+  const int w_lo = P.window > 0 ? max(0, w_p_first - P.window + 1) : 0;
+  const bool wave_active = head_ok && wave_rows > 0;
+
+  // query operand (B of S^T = K Q^T): row my_row, dims 16*kc + 8*h .. +7
+  V8 qop[KC];
+  {
+    const QT* qr = reinterpret_cast<const QT*>(P.q) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int col = kc * 16 + h * 8;
+      if (row_ok) {
+        if constexpr (kI8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            qop[kc][e] = (OpT)(to_f32(qr[col + e]) * P.key_scale[c * D + col + e]);
+        } else {
+          qop[kc] = __builtin_bit_cast(V8, load16(qr + col));
+        }
+      } else {
+        qop[kc] = V8{};
+      }
+    }
+  }
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  const int kt_begin = (j_lo / kPfTile) * kPfTile;
+  const int n_tiles = j_hi >= j_lo ? (j_hi - kt_begin) / kPfTile + 1 : 0;
+
+  const KT* kcache = reinterpret_cast<const KT*>(P.k_cache);
+  const KT* vcache = reinterpret_cast<const KT*>(P.v_cache);
+
+  // ---- tile loader: global -> registers -> LDS stage ----
+  typedef typename std::conditional<kI8, int2, i32x4>::type Raw;
+  Raw kraw[NCH], vraw[NCH];
+  bool kok[NCH];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) {
+      const int qi = tid + n * kPfThreads;
+      const int key = qi / CH, col = (qi % CH) * 8;
+      const int j = kt + key;
+      int64_t off = -1;
+      if (j >= j_lo && j <= j_hi) off = cache_row(P.cd, b, j, c, flags);
+      kok[n] = off >= 0;
+      if (off >= 0) {
+        kraw[n] = *reinterpret_cast<const Raw*>(kcache + off + col);
+        vraw[n] = *reinterpret_cast<const Raw*>(vcache + off + col);
+      } else {
+        kraw[n] = Raw{};
+        vraw[n] = Raw{};
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    unsigned char* base = smem + stage * PfLds<D>::kStage;
+    OpT* kl = reinterpret_cast<OpT*>(base);
+    OpT* vl = reinterpret_cast<OpT*>(base + PfLds<D>::kKBytes);
+    int32_t* vb = reinterpret_cast<int32_t*>(base + PfLds<D>::kKBytes + PfLds<D>::kVBytes);
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) {
+      const int qi = tid + n * kPfThreads;
+      const int key = qi / CH, col = (qi % CH) * 8;
+      V8 kv, vv;
+      if constexpr (kI8) {
+        const int8_t* kc8 = reinterpret_cast<const int8_t*>(&kraw[n]);
+        const int8_t* vc8 = reinterpret_cast<const int8_t*>(&vraw[n]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kv[e] = (OpT)(float)kc8[e]; vv[e] = (OpT)(float)vc8[e]; }
+      } else {
+        kv = __builtin_bit_cast(V8, kraw[n]);
+        vv = __builtin_bit_cast(V8, vraw[n]);
+      }
+      *reinterpret_cast<V8*>(kl + key * PfLds<D>::kKld + col) = kv;
+      *reinterpret_cast<V8*>(vl + key * PfLds<D>::kVld + col) = vv;
+      if (col == 0) vb[key] = kok[n] ? 1 : 0;
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(kt_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kt = kt_begin + it * kPfTile;
+    const int stage = it & 1;
+    const bool has_next = it + 1 < n_tiles;
+    if (has_next) load_tile(kt + kPfTile);
+    // skip tiles outside this wave's key range (fully masked for every row it owns)
+    if (wave_active && kt + kPfTile - 1 >= w_lo && kt <= w_p_last) {
+      const unsigned char* base = smem + stage * PfLds<D>::kStage;
+      const OpT* kl = reinterpret_cast<const OpT*>(base);
+      const OpT* vl = reinterpret_cast<const OpT*>(base + PfLds<D>::kKBytes);
+      const int32_t* vb = reinterpret_cast<const int32_t*>(base + PfLds<D>::kKBytes + PfLds<D>::kVBytes);
+      // S^T: A = K[key l32][16kc + 8h ..], B = qop
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        V8 a = *reinterpret_cast<const V8*>(kl + l32 * PfLds<D>::kKld + kc * 16 + h * 8);
+        s = mfma32(a, qop[kc], s);
+      }
+      // masks; lane holds keys 8*(i/4) + 4*h + i%4 of row l32
+      float mt = kNegInf;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int k0 = 8 * g4 + 4 * h;
+        const i32x4 ok = *reinterpret_cast<const i32x4*>(vb + k0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = kt + k0 + e;
+          const bool vis = row_ok && ok[e] && j <= my_p && j >= my_lo;
+          const float v = vis ? s[4 * g4 + e] * P.scale_log2 : kNegInf;
+          s[4 * g4 + e] = v;
+          mt = fmaxf(mt, v);
+        }
+      }
+      mt = xor_max(mt, 32);
+      const float m_new = fmaxf(m_run, mt);
+      // Every lane runs the update and the MFMAs (they read operands of all 64 lanes);
+      // a row with no visible key so far keeps m = -inf, l = 0, acc = 0.
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      {
+        const float alpha = exp2_safe(m_run - m_use);
+        float psum = 0.f;
+        V8 pop[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_safe(s[i] - m_use);
+          psum += p;
+          pop[i >> 3][i & 7] = (OpT)p;
+        }
+        psum = xor_sum(psum, 32);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] *= alpha;
+        const int grp = lane >> 4, lam = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const OpT* a0 = vl + (16 * ks + 4 * h + (lam >> 2)) * PfLds<D>::kVld + 32 * m +
+                            16 * (grp & 1) + 4 * (lam & 3);
+            const OpT* a1 = a0 + 8 * PfLds<D>::kVld;
+            s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(a0));
+            s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(a1));
+            V4 x0 = __builtin_bit_cast(V4, r0);
+            V4 x1 = __builtin_bit_cast(V4, r1);
+            V8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            acc[m] = mfma32(av, pop[ks], acc[m]);
+          }
+      }
+    }
+    if (has_next) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- finalise: sink, normalise, store (lane: row l32, dims 32m + 8(i/4) + 4h + i%4) ----
+  if (row_ok) {
+    QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
+    float f = 0.f, inv = 0.f;
+    if (m_run != kNegInf) {
+      const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
+      const float M2 = fmaxf(m_run, sg);
+      f = exp2_safe(m_run - M2);
+      inv = f / (l_run * f + exp2_safe(sg - M2));
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * m + 8 * g4 + 4 * h;
+        typename Op32<QT>::v4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = acc[m][4 * g4 + e] * inv;
+          if constexpr (kI8) x *= P.value_scale[c * D + d0 + e];
+          w[e] = from_f32<QT>(x);
+        }
+        *reinterpret_cast<typename Op32<QT>::v4*>(o + d0) = w;
+      }
+  }
+  // flags from the loaders (keys visible to some row of the workgroup) and the row checks
+  int wave_flags = 0;
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit)
+    if (__ballot(flags & (1 << bit))) wave_flags |= 1 << bit;
+  if (wave_flags && lane == 0) raise_status(P.status, wave_flags);
+}
+
+template <typename QT, typename KT, int D>
+static void launch_prefill_typed(const PrefillParams& P, int RW, hipStream_t stream) {
+  const size_t lds = PfLds<D>::kTotal;
+  dim3 grid(P.total), block(kPfThreads);
+  if (RW == 1) hipLaunchKernelGGL((prefill_kernel<QT, KT, D, 1>), grid, block, lds, stream, P);
+  else if (RW == 2) hipLaunchKernelGGL((prefill_kernel<QT, KT, D, 2>), grid, block, lds, stream, P);
+  else hipLaunchKernelGGL((prefill_kernel<QT, KT, D, 4>), grid, block, lds, stream, P);
+}
+
+int launch_prefill_attention(const AttnArgs& a, hipStream_t stream) {
+  if (a.T == 0 || a.B == 0) return SPATTN_OK;
+  PrefillParams P;
+  P.q = a.q; P.k_cache = a.k_cache; P.v_cache = a.v_cache;
+  P.key_scale = a.key_scale; P.value_scale = a.value_scale;
+  P.cu = a.cu; P.seqlens_k = a.seqlens_k; P.sinks = a.sinks; P.out = a.out; P.status = a.status;
+  P.cd.block_table = a.block_table;
+  P.cd.max_blocks = a.max_blocks;
+  P.cd.block_size = a.block_size;
+  P.cd.bs_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz(a.block_size) : -1;
+  P.cd.num_blocks = a.num_blocks;
+  P.cd.H_kv = a.H_kv;
+  P.cd.D = a.D;
+  P.B = a.B; P.T = a.T; P.H_q = a.H_q; P.H_kv = a.H_kv; P.D = a.D;
+  P.group = a.H_q / a.H_kv;
+  P.max_q = a.max_q; P.max_k = a.max_k; P.window = a.window;
+  P.scale_log2 = a.scale * kLog2e;
+  const int RW = P.group >= 4 ? 1 : (P.group == 1 ? 4 : 2);
+  const int HW = 4 / RW;
+  P.n_hg = (P.group + HW - 1) / HW;
+  P.n_rt = (a.max_q + 32 * RW - 1) / (32 * RW);
+  const long total = (long)P.n_rt * a.B * a.H_kv * P.n_hg;
+  if (total <= 0) return SPATTN_OK;
+  if (total > 0x7fffffffL) return SPATTN_ERR_SHAPE;
+  P.total = (int)total;
+  const bool i8 = a.cache_dtype == SPATTN_I8;
+  if (a.D == 64) {
+    if (a.dtype == SPATTN_F16) { if (i8) launch_prefill_typed<f16, int8_t, 64>(P, RW, stream); else launch_prefill_typed<f16, f16, 64>(P, RW, stream); }
+    else { if (i8) launch_prefill_typed<bf16, int8_t, 64>(P, RW, stream); else launch_prefill_typed<bf16, bf16, 64>(P, RW, stream); }
+  } else {
+    if (a.dtype == SPATTN_F16) { if (i8) launch_prefill_typed<f16, int8_t, 128>(P, RW, stream); else launch_prefill_typed<f16, f16, 128>(P, RW, stream); }
+    else { if (i8) launch_prefill_typed<bf16, int8_t, 128>(P, RW, stream); else launch_prefill_typed<bf16, bf16, 128>(P, RW, stream); }
+  }
+  return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_ERR_LAUNCH;
+}
+
+}  // namespace spattn

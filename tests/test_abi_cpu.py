@@ -1,0 +1,127 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments before touching a device.
+Only calls that fail host validation are made here, so nothing is ever launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selected_token_sparse_amd import _lib
+
+HEADER = _lib.HEADER_PATH
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"SPATTN_API\s+\w+\s+(\w+)\s*\(", text)
+
+
+def test_header_declares_the_abi():
+    names = _declared()
+    assert set(names) == {"prepare_seqlens", "kv_cache_append", "paged_attention_fwd",
+                          "sparse_attention_fwd", "attention_workspace_bytes"}
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libspattn.so not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_lib._SIGNATURES) == set(_declared())
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libspattn.so not built")
+    return _lib.load()
+
+
+def test_workspace_bytes(lib):
+    f = lib.attention_workspace_bytes
+    bad = (1 << 64) - 1
+    # paged decode, 32 rows, key bound 8192, H 64/8, D 64: split partials needed
+    n = f(0, 1, 32, 32, 1, 8192, 0, -1, 64, 8, 64)
+    assert 0 < n < 64 << 20
+    # prefill regime (max_seqlen_q > 8, fp16) needs none
+    assert f(0, 1, 4, 5120, 2048, 2048, 0, 128, 64, 8, 64) == 0
+    # a single short split needs none
+    assert f(0, 1, 2, 2, 1, 100, 0, -1, 4, 2, 64) == 0
+    # invalid arguments
+    assert f(0, 1, 2, 2, 1, 100, 0, -1, 6, 4, 64) == bad      # H_q % H_kv
+    assert f(0, 1, 2, 2, 1, 100, 0, -1, 4, 2, 96) == bad      # head_dim
+    assert f(2, 1, 2, 2, 1, 0, 64, 0, 4, 2, 64) == bad        # local+aux without a window
+    assert f(7, 1, 2, 2, 1, 100, 0, -1, 4, 2, 64) == bad      # kind
+    # more keys never need less workspace
+    assert f(1, 1, 16, 128, 8, 0, 4096, 0, 48, 4, 128) >= f(1, 1, 16, 128, 8, 0, 2048, 0, 48, 4, 128)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _paged(lib, **kw):
+    a = dict(q=FAKE, dtype=1, k=FAKE, v=FAKE, cdt=1, bt=FAKE, mbps=4, bs=16, nb=8, ks=None, vs=None,
+             cu=FAKE, sk=FAKE, B=2, T=2, mq=1, mk=64, Hq=4, Hkv=2, D=64, scale=0.0, causal=1,
+             win=-1, sinks=None, out=FAKE, ws=None, wsb=0, st=None, stream=None)
+    a.update(kw)
+    return lib.paged_attention_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(causal=0), -4), (dict(D=96), -4), (dict(Hq=6, Hkv=4), -4), (dict(dtype=3), -3),
+    (dict(cdt=0), -3), (dict(cdt=3), -1), (dict(q=None), -1), (dict(out=None), -1),
+    (dict(k=None), -1), (dict(B=-1), -2), (dict(bs=0), -2), (dict(mbps=0), -2),
+    (dict(bt=None, nb=1), -2), (dict(nb=1 << 28, bs=1 << 4), -2),
+    (dict(B=0), -2), (dict(mk=-5), -2),
+    (dict(T=32, mq=1, mk=8192, Hq=64, Hkv=8, ws=None), -5),
+])
+def test_paged_argument_errors(lib, kw, rc):
+    assert _paged(lib, **kw) == rc
+
+
+def test_paged_empty_batch_is_a_no_op(lib):
+    assert _paged(lib, T=0) == 0
+
+
+def _sparse(lib, **kw):
+    a = dict(q=FAKE, dtype=1, mode=0, k=FAKE, v=FAKE, cdt=1, bt=None, mbps=0, bs=100, nb=2, ks=None,
+             vs=None, cu=FAKE, sk=FAKE, B=2, T=2, mq=1, sel=FAKE, cnt=FAKE, msel=16, win=-1,
+             ak=None, av=None, adt=1, alen=0, astride=0, Hq=4, Hkv=2, D=64, scale=0.0, sinks=None,
+             out=FAKE, ws=None, wsb=0, st=None, stream=None)
+    a.update(kw)
+    return lib.sparse_attention_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(mode=2), -4), (dict(win=8), -4), (dict(mode=1, win=-1), -4), (dict(sel=None), -1),
+    (dict(mode=1, win=8), -1), (dict(mode=1, win=8, ak=FAKE, av=FAKE, adt=2), -3),
+    (dict(mode=1, win=8, ak=FAKE, av=FAKE, alen=10, astride=100), -2), (dict(D=32), -4),
+    (dict(msel=-1), -2),
+])
+def test_sparse_argument_errors(lib, kw, rc):
+    assert _sparse(lib, **kw) == rc
+
+
+def test_append_argument_errors(lib):
+    f = lib.kv_cache_append
+    base = [FAKE, FAKE, 1, FAKE, FAKE, 2, 4, FAKE, FAKE, 1, FAKE, 4, 16, 8, None, None, 2, 64, None, None]
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(2, 3) == -3          # int8 new rows
+    assert call(9, 2) == -3          # cache dtype differs from the rows'
+    assert call(9, 3) == -1          # int8 cache without scales
+    assert call(0, None) == -1
+    assert call(17, 60) == -2        # head_dim not a multiple of 8
+    assert call(12, 0) == -2         # block size
+    assert call(6, 0) == 0           # nothing to append
+
+
+def test_prepare_argument_errors(lib):
+    f = lib.prepare_seqlens
+    assert f(None, FAKE, 2, 4, FAKE, FAKE, None, None, None, None) == -1
+    assert f(FAKE, FAKE, -1, 4, FAKE, FAKE, None, None, None, None) == -2
+    assert f(FAKE, FAKE, 9000, 4, FAKE, FAKE, None, None, None, None) == -2

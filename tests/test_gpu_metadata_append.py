@@ -1,0 +1,157 @@
+"""GPU parity: prepare_seqlens and kv_cache_append against the oracle, bit for bit."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selected_token_sparse_amd as sta
+import synth
+from synth.device import TORCH_DTYPE, case_tensors, tensor
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gpu_meta(cu, past, T):
+    cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    past_t = torch.tensor(past, dtype=torch.int32, device="cuda")
+    B = len(past)
+    sq = torch.full((B,), 12345, dtype=torch.int32, device="cuda")
+    sk = torch.full((B,), 12345, dtype=torch.int32, device="cuda")
+    req = torch.full((max(T, 1),), 12345, dtype=torch.int32, device="cuda")
+    pos = torch.full((max(T, 1),), 12345, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sta.prepare_seqlens(cu_t, past_t, T, sq, sk, req[:T] if T else None, pos[:T] if T else None, st)
+    torch.cuda.synchronize()
+    return (sq.cpu().numpy(), sk.cpu().numpy(), req[:T].cpu().numpy(), pos[:T].cpu().numpy(),
+            int(st.item()))
+
+
+def _check_meta(cu, past, T):
+    g = _gpu_meta(cu, past, T)
+    o = oracle.prepare_seqlens(cu, past, T)
+    for name, a, b in zip(["seqlens_q", "seqlens_k", "token_req", "token_pos"], g[:4], o[:4]):
+        assert np.array_equal(a, b), (name, a, b)
+    assert g[4] == o[4]
+
+
+def test_metadata_page_examples():
+    with open(os.path.join(GOLDEN, "metadata_examples.json")) as f:
+        for case in json.load(f)["cases"]:
+            print("metadata example", case["cu_seqlens_q"], flush=True)
+            g = _gpu_meta(case["cu_seqlens_q"], case["past_seqlens"], case["T"])
+            assert g[0].tolist() == case["seqlens_q"]
+            assert g[1].tolist() == case["seqlens_k"]
+            _check_meta(case["cu_seqlens_q"], case["past_seqlens"], case["T"])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_metadata_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 3000 if seed % 2 else 40))
+    q_lens = rng.integers(0, 9 if seed % 3 else 300, size=B)
+    past = rng.integers(0, 70000, size=B)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    print("metadata random", seed, B, int(cu[-1]), flush=True)
+    _check_meta(cu, past.astype(np.int32), int(cu[-1]))
+
+
+@pytest.mark.parametrize("cu,past,T", [
+    ([1, 2, 3], [0, 0], 3), ([0, 3, 2, 4], [0, 0, 0], 4), ([0, 2, 9], [0, 0], 5),
+    ([0, 2, 3], [0, 0], 5), ([0, 1, 2], [-4, 0], 2), ([-3, 5, 1, 7], [1, 2, 3], 6), ([0], [], 0),
+    ([0], [], 4),
+])
+def test_metadata_malformed(cu, past, T):
+    print("metadata malformed", cu, past, T, flush=True)
+    _check_meta(cu, past, T)
+
+
+def test_metadata_max_batch():
+    rng = np.random.default_rng(7)
+    q_lens = rng.integers(0, 3, size=8192)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    _check_meta(cu, rng.integers(0, 100, size=8192).astype(np.int32), int(cu[-1]))
+    # beyond the limit: rejected on the host
+    with pytest.raises(sta.SpattnError):
+        _gpu_meta(np.zeros(8194, dtype=np.int32), np.zeros(8193, dtype=np.int32), 0)
+
+
+APPEND_CASES = [
+    dict(name="paged_f16", kv_lens=[5, 0, 40, 17, 1], q_lens=[2, 0, 40, 1, 1], dtype=synth.F16),
+    dict(name="paged_bf16_bs12", kv_lens=[30, 7], q_lens=[9, 7], dtype=synth.BF16, block_size=12),
+    dict(name="paged_f32", kv_lens=[3, 64], q_lens=[3, 2], dtype=synth.F32, D=128),
+    dict(name="contig_f16", kv_lens=[5, 48, 20], q_lens=[2, 8, 20], dtype=synth.F16, contiguous=True, capacity=48),
+    dict(name="paged_i8_from_f16", kv_lens=[9, 33, 3], q_lens=[3, 8, 3], dtype=synth.F16, cache_dtype=synth.I8, D=128),
+    dict(name="paged_i8_from_bf16", kv_lens=[20], q_lens=[20], dtype=synth.BF16, cache_dtype=synth.I8),
+    dict(name="contig_i8_from_f32", kv_lens=[16, 4], q_lens=[16, 4], dtype=synth.F32, cache_dtype=synth.I8, contiguous=True, capacity=16),
+]
+
+
+@pytest.mark.parametrize("spec", APPEND_CASES, ids=[c["name"] for c in APPEND_CASES])
+def test_append_bit_exact(spec):
+    spec = dict(spec)
+    name = spec.pop("name")
+    D = spec.pop("D", 64)
+    print("append", name, flush=True)
+    case = synth.paged_case(21, H_q=4, H_kv=2, D=D, poison=True, **spec)
+    t = case_tensors(case)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], t["seqlens_k"], t["k_cache"], t["v_cache"],
+                        t["block_table"], t["key_scale"], t["value_scale"], status=st)
+    torch.cuda.synchronize()
+    kc, vc, ost = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, case.seqlens_k,
+                                         case.k_cache, case.v_cache, case.block_table, case.block_size,
+                                         case.key_scale, case.value_scale)
+    for got, want in ((t["k_cache"], kc), (t["v_cache"], vc)):
+        g = got.cpu()
+        w = tensor(want, case.cache_dtype, "cpu")
+        assert torch.equal(g.view(torch.int8) if g.dtype == torch.int8 else g.view(torch.int16) if g.element_size() == 2 else g.view(torch.int32),
+                           w.view(torch.int8) if w.dtype == torch.int8 else w.view(torch.int16) if w.element_size() == 2 else w.view(torch.int32))
+    assert int(st.item()) == ost
+
+
+def test_append_missing_slots_flagged_and_skipped():
+    case = synth.paged_case(22, kv_lens=[20, 20, 20], q_lens=[4, 4, 4], H_q=2, H_kv=1, D=64,
+                            block_size=16, dtype=synth.F16, num_blocks=6)
+    bt = case.block_table.copy()
+    bt[1, 1] = 99
+    sk = case.seqlens_k.copy()
+    sk[2] = 40
+    t = case_tensors(case)
+    t["block_table"] = tensor(bt, None)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], tensor(sk, None), t["k_cache"], t["v_cache"],
+                        t["block_table"], status=st)
+    torch.cuda.synchronize()
+    kc, vc, ost = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, sk, case.k_cache,
+                                         case.v_cache, bt, case.block_size)
+    assert ost == oracle.STATUS_BAD_BLOCK | oracle.STATUS_CAPACITY
+    assert int(st.item()) == ost
+    assert np.array_equal(t["k_cache"].cpu().numpy().view(np.int16), kc.view(np.int16))
+
+
+def test_append_quantisation_hand_worked_codes():
+    # one row of eight hand-worked values through the device quantiser
+    with open(os.path.join(GOLDEN, "int8_codes.json")) as f:
+        cases = json.load(f)["cases"]
+    n = len(cases)
+    D = 64
+    x = np.zeros((1, 1, D), dtype=np.float32)
+    s = np.ones((1, D), dtype=np.float32)
+    want = np.zeros(D, dtype=np.int8)
+    for i, c in enumerate(cases):
+        x[0, 0, i] = np.float32(float(c["x"]))
+        s[0, i] = np.float32(float(c["s"]))
+        want[i] = c["code"]
+    cu = tensor(np.array([0, 1], dtype=np.int32), None)
+    sk = tensor(np.array([0], dtype=np.int32), None)
+    kc = torch.zeros((1, 1, 1, D), dtype=torch.int8, device="cuda")
+    vc = torch.zeros_like(kc)
+    xt = tensor(x, None)
+    st_ = tensor(s, None)
+    sta.kv_cache_append(xt, xt, cu, sk, kc, vc, None, st_, st_)
+    torch.cuda.synchronize()
+    assert kc.cpu().numpy().reshape(-1)[:n].tolist() == want[:n].tolist()

@@ -1,0 +1,205 @@
+"""GPU parity: the paged step (prepare_seqlens -> kv_cache_append -> paged_attention_fwd)
+against the oracle, at small sizes in full and at the workloads' full sizes on sampled
+rows; decode (split-K) and prefill (MFMA tile) regimes, windows, sinks, GQA groups,
+INT8 caches, empty and degenerate requests."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selected_token_sparse_amd as sta
+import synth
+from synth.device import case_tensors, tensor
+
+from harness import assert_close, oracle_paged_step, run_paged_step, status_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(case, what):
+    print("paged", what, flush=True)
+    out, _, _, st = run_paged_step(case)
+    torch.cuda.synchronize()
+    ref, ost, mag = oracle_paged_step(case)
+    err = assert_close(out, ref, case.dtype, what, mag)
+    assert int(st.item()) == ost, (int(st.item()), ost)
+    return err
+
+
+def test_tiny_paged_decode_f32():
+    _check_full(synth.config_tiny_paged_decode(poison=True), "tiny_paged_decode_f32")
+
+
+def test_gqa_paged_decode_reduced():
+    _check_full(synth.config_gqa_paged_decode(poison=True, B=8, max_len=1500, seed=77),
+                "gqa_paged_decode_f16_reduced")
+
+
+DECODE = [
+    # name, kwargs
+    ("f16_g8_sink", dict(kv_lens=[1, 2, 17, 33, 200, 0, 511], q_lens=[1, 1, 1, 1, 1, 0, 1], H_q=16, H_kv=2, D=64, dtype=synth.F16, sinks=True)),
+    ("bf16_g8_w5", dict(kv_lens=[40, 3, 129], q_lens=[1, 1, 1], H_q=16, H_kv=2, D=64, dtype=synth.BF16, sinks=True, local_window=5)),
+    ("f16_d128_g12", dict(kv_lens=[300, 77], q_lens=[1, 1], H_q=24, H_kv=2, D=128, dtype=synth.F16, sinks=True)),
+    ("f16_g1_mtp4", dict(kv_lens=[9, 100], q_lens=[4, 4], H_q=3, H_kv=3, D=64, dtype=synth.F16)),
+    ("f16_g20_two_tiles", dict(kv_lens=[64, 5], q_lens=[2, 1], H_q=40, H_kv=2, D=64, dtype=synth.F16, sinks=True)),
+    ("f16_g3_bs12", dict(kv_lens=[50, 13], q_lens=[8, 1], H_q=6, H_kv=2, D=64, dtype=synth.F16, block_size=12)),
+    ("f16_i8_cache", dict(kv_lens=[70, 260], q_lens=[1, 3], H_q=12, H_kv=1, D=128, dtype=synth.F16, cache_dtype=synth.I8, sinks=True)),
+    ("bf16_i8_cache_w9", dict(kv_lens=[70, 33], q_lens=[2, 1], H_q=8, H_kv=2, D=64, dtype=synth.BF16, cache_dtype=synth.I8, local_window=9)),
+    ("f32_g4_w3_sink", dict(kv_lens=[31, 2, 90], q_lens=[1, 2, 3], H_q=8, H_kv=2, D=128, dtype=synth.F32, sinks=True, local_window=3)),
+    ("f32_i8_cache", dict(kv_lens=[45], q_lens=[2], H_q=4, H_kv=2, D=64, dtype=synth.F32, cache_dtype=synth.I8)),
+    ("f16_contig", dict(kv_lens=[120, 7, 64], q_lens=[1, 1, 1], H_q=8, H_kv=1, D=64, dtype=synth.F16, contiguous=True, capacity=128, sinks=True)),
+    ("f16_long_splits", dict(kv_lens=[8192, 4000, 1], q_lens=[1, 1, 1], H_q=64, H_kv=8, D=64, dtype=synth.F16, sinks=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", DECODE, ids=[d[0] for d in DECODE])
+def test_decode_variants(name, kw):
+    case = synth.paged_case(zlib.crc32(name.encode()) % 1000, poison=True, **kw)
+    _check_full(case, name)
+
+
+PREFILL = [
+    ("f16_w128_sink", dict(kv_lens=[160, 64, 300, 97], q_lens=[160, 64, 300, 97], H_q=16, H_kv=2, D=64, dtype=synth.F16, sinks=True, local_window=128)),
+    ("f16_causal", dict(kv_lens=[130, 33, 257], q_lens=[130, 33, 257], H_q=8, H_kv=2, D=64, dtype=synth.F16, sinks=True)),
+    ("bf16_causal_d128", dict(kv_lens=[100, 70], q_lens=[100, 70], H_q=8, H_kv=2, D=128, dtype=synth.BF16)),
+    ("f16_chunked_prefill", dict(kv_lens=[300, 90], q_lens=[45, 90], H_q=8, H_kv=1, D=64, dtype=synth.F16, sinks=True, local_window=50)),
+    ("f16_g1", dict(kv_lens=[200, 9], q_lens=[150, 9], H_q=2, H_kv=2, D=64, dtype=synth.F16)),
+    ("f16_g2", dict(kv_lens=[100], q_lens=[77], H_q=4, H_kv=2, D=128, dtype=synth.F16, local_window=16)),
+    ("f16_g12_d128", dict(kv_lens=[64, 40], q_lens=[64, 40], H_q=24, H_kv=2, D=128, dtype=synth.F16, sinks=True)),
+    ("f16_i8_prefill", dict(kv_lens=[90, 40], q_lens=[90, 20], H_q=8, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.I8, sinks=True)),
+    ("f16_w1", dict(kv_lens=[40], q_lens=[40], H_q=8, H_kv=2, D=64, dtype=synth.F16, local_window=1)),
+    ("f16_bs5", dict(kv_lens=[61, 20], q_lens=[61, 12], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=5, sinks=True)),
+    ("f16_empty_mixed", dict(kv_lens=[0, 50, 0, 9], q_lens=[0, 50, 0, 9], H_q=8, H_kv=2, D=64, dtype=synth.F16, sinks=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", PREFILL, ids=[d[0] for d in PREFILL])
+def test_prefill_variants(name, kw):
+    case = synth.paged_case(zlib.crc32(name.encode()) % 1000, poison=True, **kw)
+    assert case.max_seqlen_q > 8
+    _check_full(case, name)
+
+
+def test_single_visible_key_is_the_value_row():
+    # window 1, no sink: the softmax weight is exactly 1, so out == the row's own V (bit-exact)
+    for q_lens, dt in (([1, 1], synth.F16), ([30, 12], synth.F16), ([1, 3], synth.BF16), ([20], synth.BF16)):
+        kv = [x + 5 for x in q_lens]
+        case = synth.paged_case(5, kv_lens=kv, q_lens=q_lens, H_q=8, H_kv=2, D=64, dtype=dt,
+                                local_window=1, poison=True)
+        print("single key", q_lens, dt, flush=True)
+        out, _, _, _ = run_paged_step(case)
+        torch.cuda.synchronize()
+        g = out.cpu()
+        want = tensor(np.repeat(case.v_new, 4, axis=1), dt, "cpu")
+        assert torch.equal(g.view(torch.int16), want.view(torch.int16))
+
+
+def test_block_table_permutation_gives_identical_bits():
+    case = synth.paged_case(9, kv_lens=[300, 45], q_lens=[1, 1], H_q=16, H_kv=2, D=64,
+                            dtype=synth.F16, sinks=True, num_blocks=40)
+    out1, _, _, _ = run_paged_step(case)
+    perm = np.random.default_rng(3).permutation(case.num_blocks)
+    kc = np.empty_like(case.k_cache)
+    vc = np.empty_like(case.v_cache)
+    kc[perm] = case.k_cache
+    vc[perm] = case.v_cache
+    case.block_table = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)], -1).astype(np.int32)
+    case.k_cache, case.v_cache = kc, vc
+    out2, _, _, _ = run_paged_step(case)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.cpu().view(torch.int16), out2.cpu().view(torch.int16))
+
+
+def test_deterministic_repeat():
+    case = synth.config_gqa_paged_decode(B=6, max_len=3000, seed=5)
+    t = case_tensors(case)
+    a, _, _, _ = run_paged_step(case, t=t)
+    b, _, _, _ = run_paged_step(case, t=t)
+    torch.cuda.synchronize()
+    assert torch.equal(a.cpu().view(torch.int16), b.cpu().view(torch.int16))
+
+
+def test_bound_violations_zero_rows():
+    for mq in (4, 40):
+        case = synth.paged_case(31, kv_lens=[40, 100, 30], q_lens=[10, 1, 30], H_q=8, H_kv=2, D=64,
+                                dtype=synth.F16, sinks=True)
+        case.max_seqlen_q = 30 if mq == 40 else 4    # request 0 (and 2) exceed the bound
+        case.max_seqlen_k = 60                        # request 1 exceeds the key bound
+        print("bounds", mq, flush=True)
+        _check_full(case, f"bounds_{mq}")
+
+
+def test_short_kv_and_bad_blocks():
+    case = synth.paged_case(32, kv_lens=[40, 100, 30], q_lens=[10, 1, 30], H_q=8, H_kv=2, D=64,
+                            dtype=synth.F16, sinks=True, num_blocks=20)
+    case.block_table = case.block_table.copy()
+    case.block_table[1, 2] = 77       # beyond the pool
+    case.block_table[1, 4] = -5
+    print("short kv / bad blocks", flush=True)
+    # request 2 holds fewer keys than rows: seqlens_k passed directly (no metadata kernel)
+    sk = case.seqlens_k.copy()
+    sk[2] = 19
+    t = case_tensors(case)
+    t["seqlens_k"] = tensor(sk, None)
+    st = status_tensor()
+    out = torch.empty((case.T, case.H_q, case.D), dtype=torch.float16, device="cuda")
+    sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], t["seqlens_k"],
+                            case.max_seqlen_q, case.max_seqlen_k, out, block_table=t["block_table"],
+                            scale=case.scale, sinks=t["sinks"], status=st)
+    torch.cuda.synchronize()
+    ref, ost = oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.cu_seqlens_q, sk,
+                                      H_kv=2, block_table=case.block_table, block_size=16,
+                                      max_seqlen_q=case.max_seqlen_q, max_seqlen_k=case.max_seqlen_k,
+                                      scale=case.scale, sinks=case.sinks)
+    assert_close(out, ref, synth.F16, "short_kv_bad_blocks")
+    assert int(st.item()) == ost
+    assert ost & oracle.STATUS_BAD_BLOCK and ost & oracle.STATUS_SHORT_KV
+
+
+def test_argument_errors_enqueue_nothing():
+    case = synth.config_tiny_paged_decode()
+    t = case_tensors(case)
+    out = torch.full((case.T, case.H_q, case.D), 7.0, device="cuda")
+    with pytest.raises(sta.SpattnError) as e:
+        sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], t["seqlens_k"], 1, 100,
+                                out, block_table=t["block_table"], is_causal=0)
+    assert e.value.rc == -4
+    with pytest.raises(sta.SpattnError) as e:
+        sta.paged_attention_fwd(t["q"].half(), t["k_cache"], t["v_cache"], t["cu"], t["seqlens_k"], 1,
+                                100, out.half(), block_table=t["block_table"])
+    assert e.value.rc == -3
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
+# ---------------- full-size workloads, sampled rows ----------------
+
+def _sampled(case, rows, what):
+    print("paged full-size", what, flush=True)
+    out, _, _, st = run_paged_step(case)
+    torch.cuda.synchronize()
+    ref, _, mag = oracle_paged_step(case, rows=rows)
+    return assert_close(out[rows], ref, case.dtype, what, mag)
+
+
+def test_full_gqa_paged_decode_sampled_rows():
+    case = synth.config_gqa_paged_decode(poison=False)
+    rng = np.random.default_rng(0)
+    rows = sorted(rng.choice(case.T, size=8, replace=False).tolist())
+    _sampled(case, rows, "gqa_paged_decode_f16 (full)")
+
+
+def test_full_windowed_prefill_sampled_rows():
+    case = synth.config_paged_prefill_window()
+    rng = np.random.default_rng(1)
+    rows = sorted(set(rng.choice(case.T, size=24, replace=False).tolist()) | {0, case.T - 1, 1023, 1024})
+    _sampled(case, rows, "paged_prefill_w128_f16 (full)")
+
+
+def test_full_causal_prefill_sampled_rows():
+    case = synth.config_paged_prefill_window(window=-1)
+    rng = np.random.default_rng(2)
+    rows = sorted(set(rng.choice(case.T, size=12, replace=False).tolist()) | {3583, 5119})
+    _sampled(case, rows, "paged_prefill_f16 no window (full)")
