@@ -1,0 +1,248 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: prepare_seqlens (device metadata)
+-> kv_cache_append (this step's K/V rows into the paged cache) -> paged_attention_fwd
+(split-K decode over the block table, merge with sinks).  Workload: GQA paged decode,
+fp16, B=32 requests with key counts ~ U{0..8192} (one forced empty), H_q=64, H_kv=8,
+head_dim 64, block 16, a 20000-block pool, sinks ~ N(0,1).  Inputs are resident in HBM
+before the timed region; three copies of the KV pool are rotated so that consecutive
+steps never find their 260 MB of keys/values in the 256 MB Infinity Cache.
+
+value = decode KV bytes per step / time per step (GB/s, 1 GB = 1e9 B).  The prefill
+TFLOP/s of the windowed paged prefill workload (B=4, lengths 1024/512/2048/1536, W=128)
+and of the same without a window are reported alongside, as the metric names both.
+
+`--gpus N` with N > 1 is not supported: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2516.6    # MI355X dense fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged attn"
+
+
+def _kv_bytes(case):
+    """Algorithmic K+V bytes the decode step must read: every visible key of every row,
+    once per (row, KV head); the GQA group shares it."""
+    esize = 2 if case.cache_dtype in (1, 2) else (4 if case.cache_dtype == 0 else 1)
+    total = 0
+    cu = case.cu_seqlens_q
+    for b in range(case.B):
+        q_len = int(cu[b + 1] - cu[b])
+        kv = int(case.seqlens_k[b]) + 1
+        for i in range(q_len):
+            p = kv - q_len + i
+            lo = max(0, p - case.local_window + 1) if case.local_window > 0 else 0
+            total += max(0, p - lo + 1)
+    return total * case.H_kv * case.D * esize * 2
+
+
+def _prefill_flops(case):
+    """4*D flops per visible (row, query head, key): QK^T and PV."""
+    pairs = 0
+    cu = case.cu_seqlens_q
+    for b in range(case.B):
+        q_len = int(cu[b + 1] - cu[b])
+        kv = int(case.seqlens_k[b]) + 1
+        for i in range(q_len):
+            p = kv - q_len + i
+            lo = max(0, p - case.local_window + 1) if case.local_window > 0 else 0
+            pairs += max(0, p - lo + 1)
+    return pairs * case.H_q * 4 * case.D
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_decode(steps, warmup, copies=3):
+    import torch
+
+    import selected_token_sparse_amd as sta
+    import synth
+    from synth.device import case_tensors, tensor
+
+    case = synth.config_gqa_paged_decode()
+    base = case_tensors(case)
+    sets = [base]
+    for _ in range(copies - 1):
+        sets.append(dict(base, k_cache=base["k_cache"].clone(), v_cache=base["v_cache"].clone()))
+    B, T = case.B, case.T
+    sq = torch.empty(B, dtype=torch.int32, device="cuda")
+    sk = torch.empty(B, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, case.H_q, case.D), dtype=torch.float16, device="cuda")
+    need = sta.attention_workspace_bytes(sta.KIND_PAGED, sta.F16, B, T, case.max_seqlen_q,
+                                         case.max_seqlen_k, 0, case.local_window, case.H_q,
+                                         case.H_kv, case.D)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")  # counters start at zero
+
+    def step(i, ev=None):
+        t = sets[i % copies]
+        sta.prepare_seqlens(t["cu"], t["past"], T, sq, sk, status=status)
+        sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], sk, t["k_cache"], t["v_cache"],
+                            t["block_table"], status=status)
+        if ev is not None:
+            ev[0].record()
+        sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], sk, case.max_seqlen_q,
+                                case.max_seqlen_k, out, block_table=t["block_table"],
+                                scale=case.scale, sinks=t["sinks"], workspace=ws, status=status)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [_events() for _ in range(steps)]
+    t0, t1 = _events()
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step(i, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    attn_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    st = int(status.item())
+    return case, total_ms / steps, attn_ms, st
+
+
+def bench_prefill(window, steps, warmup):
+    import torch
+
+    import selected_token_sparse_amd as sta
+    import synth
+    from synth.device import case_tensors
+
+    case = synth.config_paged_prefill_window(window=window)
+    t = case_tensors(case)
+    # the prompt rows are appended once, outside the timed region
+    sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], t["seqlens_k"], t["k_cache"], t["v_cache"],
+                        t["block_table"])
+    out = torch.empty((case.T, case.H_q, case.D), dtype=torch.float16, device="cuda")
+
+    def call():
+        sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], t["seqlens_k"],
+                                case.max_seqlen_q, case.max_seqlen_k, out,
+                                block_table=t["block_table"], scale=case.scale,
+                                local_window=case.local_window, sinks=t["sinks"])
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [_events() for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ms[len(ms) // 2]
+    flops = _prefill_flops(case)
+    qo_bytes = 2 * case.T * case.H_q * case.D * 2
+    tfl = flops / (med * 1e-3) / 1e12
+    return {
+        "workload": case.name, "window": window, "median_us": round(med * 1e3, 2),
+        "tflops": round(tfl, 2), "frac_mfma_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
+        "algorithmic_gflop": round(flops / 1e9, 3),
+        "qo_gbs": round(qo_bytes / (med * 1e-3) / 1e9, 1),
+    }
+
+
+def cpu_baseline(target_s=12.0):
+    """The oracle (numpy float64, BLAS limited to one thread) on the decode step of the same
+    workload: metadata, append and attention for the first rows, repeated until ~target_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+
+    case = synth.config_gqa_paged_decode()
+    cu = case.cu_seqlens_q
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        done_bytes, rows_done, passes = 0, 0, 0
+        _, sk, _, _, _ = oracle.prepare_seqlens(cu, case.past_seqlens, case.T)
+        kc, vc, _ = oracle.kv_cache_append(case.k_new, case.v_new, cu, sk, case.k_cache,
+                                           case.v_cache, case.block_table, case.block_size)
+        per_row = []
+        for r in range(case.T):
+            b = int(np.searchsorted(cu, r, side="right") - 1)
+            per_row.append((int(sk[b]) + 1) * case.H_kv * case.D * 2 * 2)
+        while time.perf_counter() - t0 < target_s:
+            r = rows_done % case.T
+            oracle.paged_attention(case.q, kc, vc, cu, sk, H_kv=case.H_kv,
+                                   block_table=case.block_table, block_size=case.block_size,
+                                   max_seqlen_q=case.max_seqlen_q, max_seqlen_k=case.max_seqlen_k,
+                                   scale=case.scale, sinks=case.sinks, rows=[r])
+            done_bytes += per_row[r]
+            rows_done += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} decode rows of the GQA paged decode workload (oracle attention, "
+                      f"after one oracle metadata + append pass), {dt:.1f} s, KV bytes of those rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+              "(the path needs no cross-GPU exchange; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    case, ms_step, attn_ms, st = bench_decode(args.steps, args.warmup)
+    kv = _kv_bytes(case)
+    gbs = kv / (ms_step * 1e-3) / 1e9
+    attn_med = attn_ms[len(attn_ms) // 2]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    # algorithmic bytes of one attention call: K/V of visible keys, Q, out, block-table entries
+    q_bytes = case.T * case.H_q * case.D * 2
+    bt_bytes = sum((int(s) + 1 + 15) // 16 for s in case.seqlens_k if s >= 0) * 4
+    alg = kv + 2 * q_bytes + bt_bytes
+    achieved = alg / (attn_avg * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "GQA paged decode fp16: B=32, S_q=1, H_q=64, H_kv=8, D=64, "
+                               "block 16, key counts U{0..8192} (one empty), 20000-block pool, sinks",
+                   "kv_bytes_per_step": kv, "global_batch": case.B, "rows": case.T,
+                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "status": st},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attention_fwd (split-K decode + merge)",
+                     "avg_us": round(attn_avg * 1e3, 2), "median_us": round(attn_med * 1e3, 2),
+                     "algorithmic_bytes": alg},
+    }
+    if not args.no_prefill:
+        line["prefill"] = bench_prefill(128, 50, 5)
+        line["prefill_no_window"] = bench_prefill(-1, 30, 3)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

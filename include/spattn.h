@@ -33,10 +33,12 @@
  *   Affected keys are excluded and affected rows written as zeros; nothing is read or
  *   written out of bounds.
  * - Packed layouts (row-major): Q and out [T, H_q, D]; new K/V [T, H_kv, D]; paged cache
- *   [num_blocks, block_size, H_kv, D] addressed through block_table [B,
- *   max_blocks_per_seq] (int32, entries past a request's blocks unused); contiguous cache
- *   [num_blocks >= B, capacity, H_kv, D] when block_table is NULL (then block_size is the
- *   capacity and max_blocks_per_seq is ignored).
+ *   [num_blocks, H_kv, block_size, D] (each block holds its slots head by head, so the
+ *   keys of one KV head in a block are one contiguous run) addressed through block_table
+ *   [B, max_blocks_per_seq] (int32, entries past a request's blocks unused); contiguous
+ *   cache [num_blocks >= B, H_kv, capacity, D] when block_table is NULL (then block_size is
+ *   the capacity and max_blocks_per_seq is ignored).  Auxiliary stores (sparse mode 1) are
+ *   token-major: [.., aux_len, H_kv, D].
  * - Row r of request b (cu_seqlens_q[b] <= r < cu_seqlens_q[b+1]) sits at key position
  *   p = (seqlens_k[b] + 1) - q_len_b + (r - cu_seqlens_q[b]); seqlens_k[b] is the total
  *   key count minus one (-1 = empty request).  cu_seqlens_q must be well formed
@@ -140,10 +142,14 @@ SPATTN_API int kv_cache_append(const void* k_new, const void* v_new, int new_dty
  * attention_workspace_bytes - device workspace (bytes) an attention call with these
  * arguments needs for its split-K partial softmax states ([SPA] file summaries and
  * follow-up description: FP32 partial states merged by a finalize stage).  Pure host
- * function; 0 means the call may pass workspace = NULL.  `kind` is SPATTN_KIND_*;
+ * function; 0 means the call may pass workspace = NULL.  The workspace also holds
+ * per-(row, KV head) arrival counters that must be ZERO before the first call that uses
+ * it (allocate it zeroed once); every call leaves them zero again.  Calls that may run
+ * at the same time need separate workspaces.  `kind` is SPATTN_KIND_*;
  * max_seqlen_k is used by SPATTN_KIND_PAGED, max_selected by the sparse kinds,
  * local_window by SPATTN_KIND_PAGED and SPATTN_KIND_LOCAL_AUX, dtype is the Q dtype.
- * Returns (size_t)-1 for arguments the attention calls would reject.
+ * Returns (size_t)-1 for arguments the attention calls would reject (including key
+ * ranges longer than 256 splits of 4096 keys).
  */
 SPATTN_API size_t attention_workspace_bytes(int kind, int dtype, int B, int T, int max_seqlen_q,
                                  int max_seqlen_k, int max_selected, int local_window,

@@ -42,10 +42,11 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
     """Write row ``cu[b] + i`` of ``k_new`` / ``v_new`` (``[T, H_kv, D]``) at key position
     ``p = (seqlens_k[b] + 1) - q_len_b + i`` of request ``b``.
 
-    Slot of position ``p``: paged cache ``[nb, bs, H_kv, D]`` ->
-    ``(block_table[b][p // bs], p % bs)``; contiguous cache ``[B, cap, H_kv, D]``
-    (``block_table is None``) -> ``(b, p)``.  Float caches store the row as is (same
-    dtype); INT8 caches store ``quantize_int8(row, scale[h][d])``.
+    Slot of position ``p``: paged cache ``[nb, H_kv, bs, D]`` (each block holds its
+    slots head by head) -> block ``block_table[b][p // bs]``, slot ``p % bs``; contiguous
+    cache ``[B, H_kv, cap, D]`` (``block_table is None``) -> block ``b``, slot ``p``.  The
+    row of KV head ``c`` goes to ``cache[block, c, slot]``.  Float caches store the row as
+    is (same dtype); INT8 caches store ``quantize_int8(row, scale[c][d])``.
 
     Rows whose slot does not exist are skipped and flagged (parity unpinned): ``p < 0``
     (STATUS_SHORT_KV), ``p // bs >= max_blocks_per_seq`` or ``p >= cap``
@@ -73,7 +74,7 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
                 status |= STATUS_SHORT_KV
                 continue
             if block_table is None:
-                if p >= kc.shape[1] or b >= nb:
+                if p >= kc.shape[2] or b >= nb:
                     status |= STATUS_CAPACITY
                     continue
                 blk, off = b, p
@@ -89,9 +90,9 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
                     continue
                 off = p % bs
             if int8:
-                kc[blk, off] = quantize_int8(np.asarray(k_new[r], np.float32), key_scale)
-                vc[blk, off] = quantize_int8(np.asarray(v_new[r], np.float32), value_scale)
+                kc[blk, :, off] = quantize_int8(np.asarray(k_new[r], np.float32), key_scale)
+                vc[blk, :, off] = quantize_int8(np.asarray(v_new[r], np.float32), value_scale)
             else:
-                kc[blk, off] = k_new[r]
-                vc[blk, off] = v_new[r]
+                kc[blk, :, off] = k_new[r]
+                vc[blk, :, off] = v_new[r]
     return kc, vc, status

@@ -56,12 +56,13 @@ def _eff_scale(scale, D):
 
 
 class _Cache:
-    """Addressing of a K/V cache: paged ``[nb, bs, H_kv, D]`` through a block table, or
-    contiguous ``[B, cap, H_kv, D]``; rows come back dequantised in float64."""
+    """Addressing of a K/V cache: paged ``[nb, H_kv, bs, D]`` through a block table, or
+    contiguous ``[B, H_kv, cap, D]``; rows come back dequantised in float64.  (The pages
+    do not fix a layout; this library keeps each block's slots head by head.)"""
 
     def __init__(self, k, v, block_table, block_size, key_scale, value_scale):
         self.k, self.v, self.bt = k, v, block_table
-        self.bs = int(block_size) if block_table is not None else int(k.shape[1])
+        self.bs = int(block_size) if block_table is not None else int(k.shape[2])
         self.nb = int(k.shape[0])
         self.int8 = k.dtype == np.int8
         self.ks, self.vs = key_scale, value_scale
@@ -91,8 +92,8 @@ class _Cache:
             ok = in_table & good_blk
             off = js % self.bs
         blk, off = blk[ok], off[ok]
-        K = self.k[blk, off, c].astype(np.float64)
-        V = self.v[blk, off, c].astype(np.float64)
+        K = self.k[blk, c, off].astype(np.float64)
+        V = self.v[blk, c, off].astype(np.float64)
         if self.int8:
             K = K * self.ks[c].astype(np.float64)
             V = V * self.vs[c].astype(np.float64)

@@ -72,8 +72,9 @@ def _check(fn: str, rc: int) -> int:
 
 
 def _cache_dims(k_cache: torch.Tensor, block_table: Optional[torch.Tensor]):
-    """(num_blocks, block_size or capacity, max_blocks_per_seq) of a cache tensor."""
-    nb, bs = int(k_cache.shape[0]), int(k_cache.shape[1])
+    """(num_blocks, block_size or capacity, max_blocks_per_seq) of a cache tensor laid out
+    [num_blocks, H_kv, block_size, D] (paged) or [B, H_kv, capacity, D] (contiguous)."""
+    nb, bs = int(k_cache.shape[0]), int(k_cache.shape[2])
     mbps = int(block_table.shape[1]) if block_table is not None else 0
     return nb, bs, mbps
 
@@ -132,7 +133,8 @@ def _workspace(ws: Optional[torch.Tensor], nbytes: int, like: torch.Tensor):
     if nbytes == 0:
         return None, 0
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+        # zeroed: the workspace's arrival counters must start at zero (calls leave them zero)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=like.device)
     return ws, int(ws.numel() * ws.element_size())
 
 
@@ -148,7 +150,7 @@ def paged_attention_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
                         status: Optional[torch.Tensor] = None) -> None:
     """Causal attention of packed q [T, H_q, D] over a paged/contiguous cache into out."""
     T, H_q, D = (int(x) for x in q.shape)
-    H_kv = int(k_cache.shape[2])
+    H_kv = int(k_cache.shape[1])
     B = int(seqlens_k.shape[0])
     nb, bs, mbps = _cache_dims(k_cache, block_table)
     lib = _lib.load()
@@ -179,7 +181,7 @@ def sparse_attention_fwd(q: torch.Tensor, mode: int, k_cache: torch.Tensor, v_ca
                          status: Optional[torch.Tensor] = None) -> None:
     """Selected-token attention (mode 0) or local window plus auxiliary rows (mode 1)."""
     T, H_q, D = (int(x) for x in q.shape)
-    H_kv = int(k_cache.shape[2])
+    H_kv = int(k_cache.shape[1])
     B = int(seqlens_k.shape[0])
     max_sel = int(sel_idx.shape[2])
     nb, bs, mbps = _cache_dims(k_cache, block_table)

@@ -89,8 +89,9 @@ size_t attention_workspace_bytes(int kind, int dtype, int B, int T, int max_seql
   if (check_heads(H_q, H_kv, D) != SPATTN_OK) return bad;
   if (kind == SPATTN_KIND_LOCAL_AUX && local_window <= 0) return bad;
   if (kind == SPATTN_KIND_PAGED && use_prefill_path(kind, dtype, max_seqlen_q)) return 0;
-  return make_split_plan(kind, dtype, B, T, max_seqlen_q, max_seqlen_k, max_selected,
-                         local_window, H_q, H_kv, D).ws_bytes;
+  const SplitPlan plan = make_split_plan(kind, dtype, B, T, max_seqlen_q, max_seqlen_k,
+                                         max_selected, local_window, H_q, H_kv, D);
+  return plan.n_splits < 0 ? bad : plan.ws_bytes;
 }
 
 int paged_attention_fwd(const void* q, int dtype, const void* k_cache, const void* v_cache,
@@ -129,6 +130,7 @@ int paged_attention_fwd(const void* q, int dtype, const void* k_cache, const voi
   if (use_prefill_path(a.kind, dtype, max_seqlen_q)) return launch_prefill_attention(a, st);
   const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, max_seqlen_k, 0,
                                          a.window, H_q, H_kv, D);
+  if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
     return SPATTN_ERR_WORKSPACE;
   return launch_split_attention(a, plan, st);
@@ -182,6 +184,7 @@ int sparse_attention_fwd(const void* q, int dtype, int mode, const void* k_cache
   a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
   const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, 0, max_selected,
                                          a.window, H_q, H_kv, D);
+  if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
     return SPATTN_ERR_WORKSPACE;
   return launch_split_attention(a, plan, (hipStream_t)stream);

@@ -4,9 +4,10 @@
 // contiguous caches; INT8 per-channel quantisation per the Key Changes table of the
 // DynamicSparseAttention INT8 KV cache page).
 //
-// A cache row (all KV heads of one position) is contiguous in both the packed input and
-// the cache, so a float append is a 16-byte vector copy per lane; an INT8 append turns
-// eight input elements into eight codes per lane.
+// The packed input row holds all KV heads of one position; in the cache each head's row
+// of D elements sits in its own head-major run of the block ([nb, H_kv, bs, D]), so lanes
+// copy 16-byte pieces to slot `off` of every head (an INT8 append turns eight input
+// elements into eight codes per lane).
 #include "common.h"
 #include "launch.h"
 
@@ -54,20 +55,23 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
   if (dst < 0) return;
   const int row_elems = cd.H_kv * cd.D;
   const int64_t src = (int64_t)r * row_elems;
+  const int64_t head_stride = (int64_t)cd.block_size * cd.D;  // between heads in a block
   if constexpr (kInt8) {
     int8_t* kc = reinterpret_cast<int8_t*>(k_cache) + dst;
     int8_t* vc = reinterpret_cast<int8_t*>(v_cache) + dst;
     for (int e = threadIdx.x * 8; e < row_elems; e += kAppendThreads * 8) {
-      quantize8(k_new + src + e, key_scale + e, kc + e);
-      quantize8(v_new + src + e, value_scale + e, vc + e);
+      const int c = e / cd.D, d = e - c * cd.D;
+      quantize8(k_new + src + e, key_scale + e, kc + c * head_stride + d);
+      quantize8(v_new + src + e, value_scale + e, vc + c * head_stride + d);
     }
   } else {
     constexpr int kPer = 16 / sizeof(NewT);
     NewT* kc = reinterpret_cast<NewT*>(k_cache) + dst;
     NewT* vc = reinterpret_cast<NewT*>(v_cache) + dst;
     for (int e = threadIdx.x * kPer; e < row_elems; e += kAppendThreads * kPer) {
-      store16(kc + e, load16(k_new + src + e));
-      store16(vc + e, load16(v_new + src + e));
+      const int c = e / cd.D, d = e - c * cd.D;
+      store16(kc + c * head_stride + d, load16(k_new + src + e));
+      store16(vc + c * head_stride + d, load16(v_new + src + e));
     }
   }
 }

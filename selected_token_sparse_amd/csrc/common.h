@@ -103,8 +103,9 @@ __device__ __forceinline__ RowInfo resolve_row(const int32_t* __restrict__ cu,
 }
 
 // ---------------------------------------------------------------------------------------
-// Cache addressing: paged [nb, bs, H_kv, D] through a block table, or contiguous
-// [nb >= B, cap, H_kv, D].  Returns the element offset of (position j, KV head c) row, or
+// Cache addressing: paged [nb, H_kv, bs, D] through a block table (each block holds its
+// slots head by head, so one head's keys of a block are one contiguous run), or contiguous
+// [nb >= B, H_kv, cap, D].  Returns the element offset of (position j, KV head c) row, or
 // -1 (with a status bit in `flags`) when the slot does not exist.
 // ---------------------------------------------------------------------------------------
 struct CacheDesc {
@@ -131,7 +132,26 @@ __device__ __forceinline__ int64_t cache_row(const CacheDesc& cd, int b, int j, 
     if (blk < 0 || blk >= cd.num_blocks) { flags |= SPATTN_STATUS_BAD_BLOCK; return -1; }
     off = o;
   }
-  return (((int64_t)blk * cd.block_size + off) * cd.H_kv + c) * cd.D;
+  return (((int64_t)blk * cd.H_kv + c) * cd.block_size + off) * cd.D;
+}
+
+// Same addressing as cache_row, returned as the index of the D-element cache row (fits
+// in 32 bits: the host rejects caches with 2^31 or more rows), or -1.
+__device__ __forceinline__ int cache_row_index(const CacheDesc& cd, int b, int j, int c, int& flags) {
+  int blk, off;
+  if (cd.block_table == nullptr) {
+    if (j >= cd.block_size || b >= cd.num_blocks) { flags |= SPATTN_STATUS_CAPACITY; return -1; }
+    blk = b; off = j;
+  } else {
+    int lb, o;
+    if (cd.bs_shift >= 0) { lb = j >> cd.bs_shift; o = j & (cd.block_size - 1); }
+    else { lb = j / cd.block_size; o = j - lb * cd.block_size; }
+    if (lb >= cd.max_blocks) { flags |= SPATTN_STATUS_CAPACITY; return -1; }
+    blk = cd.block_table[(int64_t)b * cd.max_blocks + lb];
+    if (blk < 0 || blk >= cd.num_blocks) { flags |= SPATTN_STATUS_BAD_BLOCK; return -1; }
+    off = o;
+  }
+  return (blk * cd.H_kv + c) * cd.block_size + off;
 }
 
 // ---------------------------------------------------------------------------------------

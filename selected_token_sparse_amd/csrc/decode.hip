@@ -12,16 +12,23 @@
 // loop, joint softmax with sink; DynamicSparseAttention INT8 page: per-channel INT8 K/V.)
 //
 // Per workgroup:
-//  1. the row's request and key position are resolved from cu_seqlens_q / seqlens_k;
+//  1. cu_seqlens_q / seqlens_k are staged in LDS in one parallel round and the row's
+//     request and key position are found by binary search there;
 //  2. the split's keys are turned into cache-row indices in LDS (one pass, guarded);
-//  3. each wave takes 32-key tiles: S^T = K Q^T with v_mfma_f32_16x16x32 (K rows loaded
-//     straight into the A operand with 16-byte loads), an online softmax in the log2
-//     domain, then O^T += V^T P^T where V^T comes from LDS through ds_read_b64_tr_b16;
-//  4. the four wave states are merged in LDS and written either as a partial (m, l, acc)
-//     for the merge kernel or, with a single split, as the final normalised output.
+//  3. each wave takes 32-key tiles, double-buffered (the next tile's loads are in flight
+//     while the current one is computed): S^T = K Q^T with v_mfma_f32_16x16x32 (K rows
+//     loaded straight into the A operand with 16-byte loads), an online softmax in the
+//     log2 domain (the accumulator is rescaled only when a running maximum moved), then
+//     O^T += V^T P^T where V^T comes from LDS through ds_read_b64_tr_b16;
+//  4. the four wave states are merged in LDS.  With one split the workgroup writes the
+//     normalised output; otherwise it writes its partial (m, l, acc) and bumps the item's
+//     arrival counter, and the last workgroup to arrive merges every split of the item,
+//     applies the sink, writes the output and resets the counter to zero.
 //
 // INT8 caches: key_scale is folded into the query operand (f16), value_scale is applied
 // to the accumulator before it leaves the workgroup.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -31,8 +38,13 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 32;          // keys per wave iteration
 constexpr int kWgStep = kWaves * kTile;
-constexpr int kMaxChunk = 2048;    // keys per split (LDS row-index buffer)
+constexpr int kMaxChunk = 2048;    // keys per split while there are enough workgroups
+constexpr int kChunkCap = 4096;    // keys per split, hard limit (LDS row-index buffer)
+constexpr int kMaxSplits = 256;    // splits per item (LDS merge coefficients)
 constexpr int kTargetWorkgroups = 4096;
+constexpr bool kFusedMerge = false;  // last-arriving workgroup merges (else a merge kernel)
+constexpr bool kPipelined = false;  // next tile's loads in flight during the current tile
+constexpr int kMetaLdsMax = 512;   // cu entries staged in LDS (more: binary search in memory)
 
 enum Src { SRC_RANGE = 0, SRC_SELECT = 1, SRC_AUX = 2 };
 
@@ -81,12 +93,14 @@ struct SplitParams {
   void* out;
   float* ws_acc;    // [n_splits][T][H_q][D]
   float2* ws_ml;    // [n_splits][T][H_q]
+  int32_t* counters;  // [T][H_kv][head_tiles], zero between calls
   int32_t* status;
   CacheDesc cd;
   int B, T, H_q, H_kv, D, group, head_tiles;
   int max_q, max_k, max_sel, window, aux_len;
   int64_t aux_row_stride;   // rows (of D elements) between requests in the aux store
   int chunk, n_main, n_splits;
+  int meta_lds;             // 1: cu / seqlens_k staged in LDS
   float scale_log2;         // scale * log2(e)
 };
 
@@ -103,138 +117,217 @@ __device__ __forceinline__ void flush_flags(int flags, int32_t* status) {
   }
 }
 
-// LDS layout (bytes): row indices of the split's keys, then per-wave V tiles (reused as
-// the combine area after the key loop).
+// LDS layout (bytes): per-wave V tiles (reused as the combine / merge area after the key
+// loop), then the split's cache-row indices, then the staged metadata.
 template <int D>
 struct SplitLds {
   static constexpr int kVld = D + 16;                       // padded V tile row (elements)
   static constexpr int kVTileBytes = kTile * kVld * 2;
   static constexpr int kCombineBytes = kWaves * 16 * (D + 2) * 4;
   static constexpr int kAreaBytes = (kWaves * kVTileBytes > kCombineBytes) ? kWaves * kVTileBytes : kCombineBytes;
-  static constexpr int kRowsBytes = kMaxChunk * 4;
-  static constexpr int kTotal = kRowsBytes + kAreaBytes;
 };
 
-// The key loop of one wave over one source.  `rows` holds the cache-row index (row of D
-// elements counted from kbase / vbase) of each key of the split, or -1.
+template <int D>
+static size_t split_lds_bytes(int chunk, int meta_ints) {
+  return SplitLds<D>::kAreaBytes + (size_t)chunk * 4 + (size_t)meta_ints * 4;
+}
+
+// K and V of one 32-key tile for one lane: rows 16*st + (lane & 15), dims 32*kc + 8*(lane >> 4).
+template <typename OpT, int D>
+struct KvTile {
+  typename OpVec<OpT>::v8 k[2][D / 32];
+  typename OpVec<OpT>::v8 v[2][D / 32];
+  uint32_t valid;  // bit i: key i of the tile exists
+};
+
+template <typename OpT, typename KT, int D>
+__device__ __forceinline__ void load_tile(KvTile<OpT, D>& t, const KT* __restrict__ kbase,
+                                          const KT* __restrict__ vbase, const int32_t* rows,
+                                          int n_keys, int base, int lam, int grp) {
+  typedef typename OpVec<OpT>::v8 V8;
+  const int row0 = (base + lam < n_keys) ? rows[base + lam] : -1;
+  const int row1 = (base + 16 + lam < n_keys) ? rows[base + 16 + lam] : -1;
+#pragma unroll
+  for (int kc = 0; kc < D / 32; ++kc) {
+    const int col = kc * 32 + grp * 8;
+    V8 z = {};
+    t.k[0][kc] = row0 >= 0 ? load_op8<OpT>(kbase + (int64_t)row0 * D + col) : z;
+    t.k[1][kc] = row1 >= 0 ? load_op8<OpT>(kbase + (int64_t)row1 * D + col) : z;
+    t.v[0][kc] = row0 >= 0 ? load_op8<OpT>(vbase + (int64_t)row0 * D + col) : z;
+    t.v[1][kc] = row1 >= 0 ? load_op8<OpT>(vbase + (int64_t)row1 * D + col) : z;
+  }
+  const uint64_t b0 = __ballot(row0 >= 0);
+  const uint64_t b1 = __ballot(row1 >= 0);
+  t.valid = (uint32_t)(b0 & 0xFFFFu) | ((uint32_t)(b1 & 0xFFFFu) << 16);
+}
+
+// One tile of the online softmax and the two products (every lane runs it: the MFMAs
+// read operands of all 64 lanes).
+template <typename OpT, int D>
+__device__ __forceinline__ void compute_tile(const KvTile<OpT, D>& t,
+                                             const typename OpVec<OpT>::v8 (&qop)[D / 32],
+                                             float scale_log2, OpT* vtile, float& m_run,
+                                             float& l_run, f32x4 (&acc)[D / 16], int lam, int grp) {
+  typedef typename OpVec<OpT>::v8 V8;
+  constexpr int KC = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int VLD = SplitLds<D>::kVld;
+  // S^T[key][head] for keys 16*st + 4*grp + i, head lam
+  f32x4 s[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) c = mfma16(t.k[st][kc], qop[kc], c);
+    s[st] = c;
+  }
+  // V tile -> LDS (row-major, padded), read back transposed below
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      *reinterpret_cast<V8*>(vtile + (16 * st + lam) * VLD + kc * 32 + grp * 8) = t.v[st][kc];
+
+  float mt = kNegInf;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 16 * st + 4 * grp + i;
+      const float v = ((t.valid >> key) & 1u) ? s[st][i] * scale_log2 : kNegInf;
+      s[st][i] = v;
+      mt = fmaxf(mt, v);
+    }
+  mt = xor_max(mt, 16);
+  mt = xor_max(mt, 32);
+  const float m_new = fmaxf(m_run, mt);
+  // a head with no visible key so far keeps m = -inf, l = 0, acc = 0
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
+  if (__ballot(m_new > m_run)) {
+    const float alpha = exp2_safe(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] *= alpha;
+  }
+  m_run = m_new;
+  float psum = 0.f;
+  V8 pop;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = exp2_safe(s[st][i] - m_use);
+      psum += p;
+      pop[st * 4 + i] = (OpT)p;
+    }
+  psum = xor_sum(psum, 16);
+  psum = xor_sum(psum, 32);
+  l_run += psum;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    // lane (grp, lam) provides rows 4*grp + lam/4 (+16), columns 16*m + 4*(lam%4)
+    const OpT* a0 = vtile + (4 * grp + (lam >> 2)) * VLD + 16 * m + 4 * (lam & 3);
+    const OpT* a1 = a0 + 16 * VLD;
+    s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
+    s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
+    typename OpVec<OpT>::v4 h0 = __builtin_bit_cast(typename OpVec<OpT>::v4, r0);
+    typename OpVec<OpT>::v4 h1 = __builtin_bit_cast(typename OpVec<OpT>::v4, r1);
+    V8 aop = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    acc[m] = mfma16(aop, pop, acc[m]);
+  }
+}
+
+// The key loop of one wave over one source, with the next tile's loads in flight while the
+// current tile is computed.  `rows` holds the cache-row index (row of D elements counted
+// from kbase / vbase) of each key of the split, or -1.
 template <typename OpT, typename KT, int D>
 __device__ __forceinline__ void wave_keys(const KT* __restrict__ kbase, const KT* __restrict__ vbase,
                                           const int32_t* rows, int n_keys,
                                           const typename OpVec<OpT>::v8 (&qop)[D / 32],
                                           float scale_log2, OpT* vtile, float& m_run,
                                           float& l_run, f32x4 (&acc)[D / 16]) {
-  typedef typename OpVec<OpT>::v8 V8;
-  constexpr int KC = D / 32;
-  constexpr int MT = D / 16;
-  constexpr int VLD = SplitLds<D>::kVld;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lam = lane & 15;
   const int grp = lane >> 4;
   const int n_tiles = (n_keys + kTile - 1) / kTile;
-  for (int tile = wave; tile < n_tiles; tile += kWaves) {
-    const int base = tile * kTile;
-    int row0 = (base + lam < n_keys) ? rows[base + lam] : -1;
-    int row1 = (base + 16 + lam < n_keys) ? rows[base + 16 + lam] : -1;
-    V8 kop[2][KC];
-    V8 vop[2][KC];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int col = kc * 32 + grp * 8;
-      V8 z = {};
-      kop[0][kc] = row0 >= 0 ? load_op8<OpT>(kbase + (int64_t)row0 * D + col) : z;
-      kop[1][kc] = row1 >= 0 ? load_op8<OpT>(kbase + (int64_t)row1 * D + col) : z;
-      vop[0][kc] = row0 >= 0 ? load_op8<OpT>(vbase + (int64_t)row0 * D + col) : z;
-      vop[1][kc] = row1 >= 0 ? load_op8<OpT>(vbase + (int64_t)row1 * D + col) : z;
+  KvTile<OpT, D> ta, tb;
+  int tile = wave;
+  if constexpr (!kPipelined) {
+    for (; tile < n_tiles; tile += kWaves) {
+      load_tile<OpT, KT, D>(ta, kbase, vbase, rows, n_keys, tile * kTile, lam, grp);
+      compute_tile<OpT, D>(ta, qop, scale_log2, vtile, m_run, l_run, acc, lam, grp);
     }
-    const uint64_t b0 = __ballot(row0 >= 0);
-    const uint64_t b1 = __ballot(row1 >= 0);
-    const uint32_t valid = (uint32_t)(b0 & 0xFFFFu) | ((uint32_t)(b1 & 0xFFFFu) << 16);
-
-    // S^T[key][head] for keys 16*st + 4*grp + i, head lam
-    f32x4 s[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) c = mfma16(kop[st][kc], qop[kc], c);
-      s[st] = c;
-    }
-    float mt = kNegInf;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * st + 4 * grp + i;
-        float v = ((valid >> key) & 1u) ? s[st][i] * scale_log2 : kNegInf;
-        s[st][i] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = xor_max(mt, 16);
-    mt = xor_max(mt, 32);
-    const float m_new = fmaxf(m_run, mt);
-
-    // V tile -> LDS (row-major, padded), read back transposed below
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        *reinterpret_cast<V8*>(vtile + (16 * st + lam) * VLD + kc * 32 + grp * 8) = vop[st][kc];
-
-    // Every lane runs the update and the MFMAs (they read operands of all 64 lanes); a
-    // head with no visible key so far keeps m = -inf, l = 0, acc = 0.
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    {
-      const float alpha = exp2_safe(m_run - m_use);
-      float psum = 0.f;
-      V8 pop;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2_safe(s[st][i] - m_use);
-          psum += p;
-          pop[st * 4 + i] = (OpT)p;
-        }
-      psum = xor_sum(psum, 16);
-      psum = xor_sum(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] *= alpha;
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the V tile writes have landed
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        // lane (grp, lam) provides rows 4*grp + lam/4 (+16), columns 16*m + 4*(lam%4)
-        const OpT* a0 = vtile + (4 * grp + (lam >> 2)) * VLD + 16 * m + 4 * (lam & 3);
-        const OpT* a1 = a0 + 16 * VLD;
-        s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(a0));
-        s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(a1));
-        typename OpVec<OpT>::v4 h0 = __builtin_bit_cast(typename OpVec<OpT>::v4, r0);
-        typename OpVec<OpT>::v4 h1 = __builtin_bit_cast(typename OpVec<OpT>::v4, r1);
-        V8 aop = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        acc[m] = mfma16(aop, pop, acc[m]);
-      }
-    }
+    return;
+  }
+  if (tile < n_tiles) load_tile<OpT, KT, D>(ta, kbase, vbase, rows, n_keys, tile * kTile, lam, grp);
+  for (; tile < n_tiles; tile += 2 * kWaves) {
+    const int t1 = tile + kWaves;
+    if (t1 < n_tiles) load_tile<OpT, KT, D>(tb, kbase, vbase, rows, n_keys, t1 * kTile, lam, grp);
+    compute_tile<OpT, D>(ta, qop, scale_log2, vtile, m_run, l_run, acc, lam, grp);
+    if (t1 >= n_tiles) break;
+    const int t2 = t1 + kWaves;
+    if (t2 < n_tiles) load_tile<OpT, KT, D>(ta, kbase, vbase, rows, n_keys, t2 * kTile, lam, grp);
+    compute_tile<OpT, D>(tb, qop, scale_log2, vtile, m_run, l_run, acc, lam, grp);
   }
 }
 
-// Cache-row index of key v of the split (or -1), for each source.
-__device__ __forceinline__ int key_row_range(const SplitParams& P, int b, int c, int lo, int v,
-                                             int& flags) {
-  const int64_t off = cache_row(P.cd, b, lo + v, c, flags);
-  return off < 0 ? -1 : (int)(off / P.D);
+// The split's source and key range for a resolved row.
+struct SplitRange {
+  int src, v0, n_keys, lo;
+  const int32_t* sel;
+};
+
+template <int KIND>
+__device__ __forceinline__ SplitRange split_range(const SplitParams& P, const RowInfo& ri, int r,
+                                                  int c, int split, int& flags) {
+  SplitRange sr{SRC_RANGE, 0, 0, 0, nullptr};
+  if (ri.b < 0) return sr;
+  int s = split, cnt;
+  if (KIND == SPATTN_KIND_LOCAL_AUX && split >= P.n_main) { sr.src = SRC_AUX; s = split - P.n_main; }
+  else if (KIND == SPATTN_KIND_SELECTED) sr.src = SRC_SELECT;
+  if (sr.src == SRC_RANGE) {
+    sr.lo = P.window > 0 ? max(0, ri.p - P.window + 1) : 0;
+    cnt = ri.p - sr.lo + 1;
+  } else {
+    sr.sel = P.sel_idx + ((int64_t)r * P.H_kv + c) * P.max_sel;
+    if (P.sel_count != nullptr) {
+      cnt = P.sel_count[(int64_t)r * P.H_kv + c];
+      if (cnt < 0 || cnt > P.max_sel) flags |= SPATTN_STATUS_BAD_COUNT;
+      cnt = min(max(cnt, 0), P.max_sel);
+    } else {
+      cnt = P.max_sel;
+    }
+  }
+  sr.v0 = s * P.chunk;
+  sr.n_keys = max(0, min(sr.v0 + P.chunk, cnt) - sr.v0);
+  return sr;
 }
 
-template <int KIND, typename QT, typename KT, typename AT, int D, bool DIRECT>
+// Cache-row index of key v of the split, or -1 (guards raise status bits).
+__device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRange& sr,
+                                             const RowInfo& ri, int c, int v, int& flags) {
+  if (sr.src == SRC_RANGE) return cache_row_index(P.cd, ri.b, sr.lo + sr.v0 + v, c, flags);
+  const int j = sr.sel[sr.v0 + v];
+  if (sr.src == SRC_SELECT) {
+    if (j != -1 && (j < 0 || j >= ri.kv_len)) { flags |= SPATTN_STATUS_BAD_INDEX; return -1; }
+    if (j >= 0 && j <= ri.p) return cache_row_index(P.cd, ri.b, j, c, flags);
+    return -1;
+  }
+  if (j != -1 && (j < 0 || j >= P.aux_len)) { flags |= SPATTN_STATUS_BAD_INDEX; return -1; }
+  if (j >= 0) return (int)(ri.b * P.aux_row_stride + (int64_t)j * P.H_kv + c);
+  return -1;
+}
+
+template <int KIND, typename QT, typename KT, typename AT, int D>
 __global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
   typedef typename std::conditional<sizeof(KT) == 1, f16, KT>::type OpM;  // main operand
   typedef QT OpA;                                                          // aux operand
   extern __shared__ __align__(16) unsigned char smem[];
-  int32_t* rows = reinterpret_cast<int32_t*>(smem);
-  unsigned char* area = smem + SplitLds<D>::kRowsBytes;
+  unsigned char* area = smem;
+  int32_t* rows = reinterpret_cast<int32_t*>(smem + SplitLds<D>::kAreaBytes);
+  int32_t* meta = rows + P.chunk;
+  __shared__ int last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -253,104 +346,70 @@ __global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
   const int h0 = c * P.group + ht * 16;                 // first query head of the tile
   const int nh = min(16, P.group - ht * 16);            // heads in the tile
 
+  // ---- 1. the row's request and position ----
+  const int32_t* cu = P.cu;
+  const int32_t* skl = P.seqlens_k;
+  if (P.meta_lds) {
+    for (int i = tid; i <= P.B; i += kThreads) {
+      meta[i] = P.cu[i];
+      if (i < P.B) meta[P.B + 1 + i] = P.seqlens_k[i];
+    }
+    __syncthreads();
+    cu = meta;
+    skl = meta + P.B + 1;
+  }
   int flags = 0;
-  RowInfo ri = resolve_row(P.cu, P.seqlens_k, P.B, r, P.max_q, P.max_k, flags);
+  const RowInfo ri = resolve_row(cu, skl, P.B, r, P.max_q, P.max_k, flags);
 
-  // ---- the split's source and key range ----
-  int src = SRC_RANGE, v0 = 0, v1 = 0, lo = 0, cnt = 0;
-  const int32_t* sel = nullptr;
-  if (ri.b >= 0) {
-    int s = split;
-    if (KIND == SPATTN_KIND_LOCAL_AUX && split >= P.n_main) { src = SRC_AUX; s = split - P.n_main; }
-    else if (KIND == SPATTN_KIND_SELECTED) src = SRC_SELECT;
-    if (src == SRC_RANGE) {
-      lo = P.window > 0 ? max(0, ri.p - P.window + 1) : 0;
-      cnt = ri.p - lo + 1;
-    } else {
-      sel = P.sel_idx + ((int64_t)r * P.H_kv + c) * P.max_sel;
-      if (P.sel_count != nullptr) {
-        cnt = P.sel_count[(int64_t)r * P.H_kv + c];
-        if (cnt < 0 || cnt > P.max_sel) flags |= SPATTN_STATUS_BAD_COUNT;
-        cnt = min(max(cnt, 0), P.max_sel);
-      } else {
-        cnt = P.max_sel;
-      }
-    }
-    v0 = s * P.chunk;
-    v1 = min(v0 + P.chunk, cnt);
-  }
-  const int n_keys = max(0, v1 - v0);
-
-  // ---- key -> cache-row indices (guarded) ----
-  for (int v = tid; v < n_keys; v += kThreads) {
-    int row = -1;
-    if (src == SRC_RANGE) {
-      row = key_row_range(P, ri.b, c, lo, v0 + v, flags);
-    } else {
-      const int j = sel[v0 + v];
-      if (src == SRC_SELECT) {
-        if (j != -1 && (j < 0 || j >= ri.kv_len)) flags |= SPATTN_STATUS_BAD_INDEX;
-        else if (j >= 0 && j <= ri.p) {
-          const int64_t off = cache_row(P.cd, ri.b, j, c, flags);
-          row = off < 0 ? -1 : (int)(off / P.D);
-        }
-      } else {
-        if (j != -1 && (j < 0 || j >= P.aux_len)) flags |= SPATTN_STATUS_BAD_INDEX;
-        else if (j >= 0) row = (int)(ri.b * P.aux_row_stride + (int64_t)j * P.H_kv + c);
-      }
-    }
-    rows[v] = row;
-  }
+  // ---- 2. the split's keys -> cache-row indices ----
+  const SplitRange sr = split_range<KIND>(P, ri, r, c, split, flags);
+  for (int v = tid; v < sr.n_keys; v += kThreads) rows[v] = split_key_row(P, sr, ri, c, v, flags);
   flush_flags(flags, P.status);
   __syncthreads();
 
-  // ---- per-wave key loop ----
+  // ---- 3. per-wave key loop ----
   float m_run = kNegInf, l_run = 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool use_scale = sizeof(KT) == 1 && src != SRC_AUX;
-  if (n_keys > 0) {
+  const bool use_scale = sizeof(KT) == 1 && sr.src != SRC_AUX;
+  if (sr.n_keys > 0) {
     const int head = h0 + lam;
     const bool hv = lam < nh;
-    if (src != SRC_AUX) {
+    const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + head) * D;
+    if (KIND != SPATTN_KIND_LOCAL_AUX || sr.src != SRC_AUX) {
       typename OpVec<OpM>::v8 qop[D / 32];
-      const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + head) * D;
 #pragma unroll
       for (int kc = 0; kc < D / 32; ++kc) {
         const int col = kc * 32 + grp * 8;
+        if constexpr (sizeof(KT) == 1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x = hv ? to_f32(qrow[col + e]) : 0.f;
-          if (use_scale) x *= P.key_scale[c * D + col + e];
-          qop[kc][e] = (OpM)x;
+          for (int e = 0; e < 8; ++e)
+            qop[kc][e] = (OpM)(hv ? to_f32(qrow[col + e]) * P.key_scale[c * D + col + e] : 0.f);
+        } else {
+          qop[kc] = hv ? __builtin_bit_cast(typename OpVec<OpM>::v8, load16(qrow + col))
+                       : typename OpVec<OpM>::v8{};
         }
       }
-      const KT* kb = reinterpret_cast<const KT*>(P.k_cache);
-      const KT* vb = reinterpret_cast<const KT*>(P.v_cache);
-      wave_keys<OpM, KT, D>(kb, vb, rows, n_keys, qop, P.scale_log2,
-                            reinterpret_cast<OpM*>(area + wave * SplitLds<D>::kVTileBytes),
+      wave_keys<OpM, KT, D>(reinterpret_cast<const KT*>(P.k_cache),
+                            reinterpret_cast<const KT*>(P.v_cache), rows, sr.n_keys, qop,
+                            P.scale_log2, reinterpret_cast<OpM*>(area + wave * SplitLds<D>::kVTileBytes),
                             m_run, l_run, acc);
-    } else {
+    } else if constexpr (sizeof(AT) == 2) {
       typename OpVec<OpA>::v8 qop[D / 32];
-      const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + head) * D;
 #pragma unroll
-      for (int kc = 0; kc < D / 32; ++kc) {
-        const int col = kc * 32 + grp * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qop[kc][e] = hv ? qrow[col + e] : (QT)0.f;
-      }
-      const AT* kb = reinterpret_cast<const AT*>(P.aux_k);
-      const AT* vb = reinterpret_cast<const AT*>(P.aux_v);
-      if constexpr (sizeof(AT) == 2)
-        wave_keys<OpA, AT, D>(kb, vb, rows, n_keys, qop, P.scale_log2,
-                              reinterpret_cast<OpA*>(area + wave * SplitLds<D>::kVTileBytes),
-                              m_run, l_run, acc);
+      for (int kc = 0; kc < D / 32; ++kc)
+        qop[kc] = hv ? __builtin_bit_cast(typename OpVec<OpA>::v8, load16(qrow + kc * 32 + grp * 8))
+                     : typename OpVec<OpA>::v8{};
+      wave_keys<OpA, AT, D>(reinterpret_cast<const AT*>(P.aux_k),
+                            reinterpret_cast<const AT*>(P.aux_v), rows, sr.n_keys, qop,
+                            P.scale_log2, reinterpret_cast<OpA*>(area + wave * SplitLds<D>::kVTileBytes),
+                            m_run, l_run, acc);
     }
   }
   __syncthreads();
 
-  // ---- merge the four wave states (head lam, dims 16m + 4grp + i) ----
+  // ---- 4. merge the four wave states (head lam, dims 16m + 4grp + i) ----
   float* cm = reinterpret_cast<float*>(area);              // [wave][16] m
   float* cl = cm + kWaves * 16;                           // [wave][16] l
   float* ca = cl + kWaves * 16;                           // [wave][16][D] acc
@@ -361,6 +420,8 @@ __global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
     for (int i = 0; i < 4; ++i) ca[(wave * 16 + lam) * D + 16 * m + 4 * grp + i] = acc[m][i];
   __syncthreads();
 
+  const bool single = P.n_splits == 1;
+  const int64_t so = (int64_t)split * P.T * P.H_q;
   for (int e = tid; e < 16 * D; e += kThreads) {
     const int h = e / D, d = e - h * D;
     if (h >= nh) continue;
@@ -379,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
     }
     const int head = h0 + h;
     const int64_t o = ((int64_t)r * P.H_q + head) * D + d;
-    if constexpr (DIRECT) {
+    if (single) {
       float res = 0.f;
       if (M != kNegInf) {
         const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
@@ -389,17 +450,75 @@ __global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
       }
       reinterpret_cast<QT*>(P.out)[o] = from_f32<QT>(res);
     } else {
-      const int64_t so = (int64_t)split * P.T * P.H_q;
       P.ws_acc[so * D + o] = A;
       if (d == 0) P.ws_ml[so + (int64_t)r * P.H_q + head] = make_float2(M, L);
     }
   }
+  if (single || !kFusedMerge) return;
+
+  // ---- 5. the last workgroup of the item merges every split ----
+  const int item = (r * P.H_kv + c) * P.head_tiles + ht;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_flag = atomicAdd(P.counters + item, 1) == P.n_splits - 1;
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  // per-split scale factors in LDS: fs[s][h] = exp2(m_s - M2), and 1 / L per head
+  float* fs = reinterpret_cast<float*>(area);                 // [n_splits][16]
+  float* inv = fs + P.n_splits * 16;                          // [16]
+  const int64_t stride = (int64_t)P.T * P.H_q;
+  if (tid < 16) {
+    const int h = tid;
+    float M = kNegInf;
+    if (h < nh) {
+      const int64_t pair = (int64_t)r * P.H_q + h0 + h;
+      for (int s = 0; s < P.n_splits; ++s) M = fmaxf(M, P.ws_ml[s * stride + pair].x);
+      float iv = 0.f;
+      if (M != kNegInf) {
+        const float sg = P.sinks != nullptr ? P.sinks[h0 + h] * kLog2e : kNegInf;
+        const float M2 = fmaxf(M, sg);
+        float L = exp2_safe(sg - M2);
+        for (int s = 0; s < P.n_splits; ++s) {
+          const float2 ml = P.ws_ml[s * stride + pair];
+          const float f = ml.x == kNegInf ? 0.f : exp2_safe(ml.x - M2);
+          fs[s * 16 + h] = f;
+          L += ml.y * f;
+        }
+        iv = 1.f / L;
+      } else {
+        for (int s = 0; s < P.n_splits; ++s) fs[s * 16 + h] = 0.f;
+      }
+      inv[h] = iv;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < nh * D; e += kThreads) {
+    const int h = e / D, d = e - h * D;
+    const int64_t o = ((int64_t)r * P.H_q + h0 + h) * D + d;
+    float A = 0.f;
+    const float iv = inv[h];
+    if (iv != 0.f) {
+      int s = 0;
+      for (; s + 4 <= P.n_splits; s += 4) {
+        const float a0 = P.ws_acc[(s + 0) * stride * D + o];
+        const float a1 = P.ws_acc[(s + 1) * stride * D + o];
+        const float a2 = P.ws_acc[(s + 2) * stride * D + o];
+        const float a3 = P.ws_acc[(s + 3) * stride * D + o];
+        A += a0 * fs[(s + 0) * 16 + h] + a1 * fs[(s + 1) * 16 + h] + a2 * fs[(s + 2) * 16 + h] +
+             a3 * fs[(s + 3) * 16 + h];
+      }
+      for (; s < P.n_splits; ++s) A += P.ws_acc[s * stride * D + o] * fs[s * 16 + h];
+    }
+    reinterpret_cast<QT*>(P.out)[o] = from_f32<QT>(A * iv);
+  }
+  if (tid == 0) P.counters[item] = 0;
 }
 
 // ---------------------------------------------------------------------------------------
-// Merge of split partial states plus the sink ("[WebGPU] Add SparsePagedAttention",
-// finalize stage; one wave per (row, query head), merge coefficients shared across the
-// head's output channels).
+// Merge of split partial states plus the sink for the float32 path ("[WebGPU] Add
+// SparsePagedAttention", finalize stage; one wave per (row, query head), merge
+// coefficients shared across the head's output channels).
 // ---------------------------------------------------------------------------------------
 template <typename QT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws_acc,
@@ -412,8 +531,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
   if (pair >= T * H_q) return;
   const int head = pair % H_q;
   const int64_t stride = (int64_t)T * H_q;
+  // lanes read the split states in parallel, then reduce across the wave
   float M = kNegInf;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ws_ml[s * stride + pair].x);
+  for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, ws_ml[s * stride + pair].x);
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   constexpr int PER = D / 64;
   float res[PER];
 #pragma unroll
@@ -421,15 +542,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
   if (M != kNegInf) {
     const float sg = sinks != nullptr ? sinks[head] * kLog2e : kNegInf;
     const float M2 = fmaxf(M, sg);
-    float L = exp2_safe(sg - M2);
+    float Lp = 0.f;
+    for (int s = lane; s < n_splits; s += 64) {
+      const float2 ml = ws_ml[s * stride + pair];
+      if (ml.x != kNegInf) Lp += ml.y * exp2_safe(ml.x - M2);
+    }
+    for (int o = 32; o >= 1; o >>= 1) Lp += __shfl_xor(Lp, o, 64);
+    const float L = Lp + exp2_safe(sg - M2);
     float A[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) A[k] = 0.f;
     for (int s = 0; s < n_splits; ++s) {
       const float2 ml = ws_ml[s * stride + pair];
-      if (ml.x == kNegInf) continue;
-      const float f = exp2_safe(ml.x - M2);
-      L += ml.y * f;
+      const float f = ml.x == kNegInf ? 0.f : exp2_safe(ml.x - M2);
       const float* a = ws_acc + (s * stride + pair) * D;
 #pragma unroll
       for (int k = 0; k < PER; ++k) A[k] += a[lane + 64 * k] * f;
@@ -443,8 +568,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 }
 
 // ---------------------------------------------------------------------------------------
-// float32 path (and any dtype with float32 queries): plain VALU arithmetic, one wave per
-// (split, row, query head); same key lists, same partial format and merge.
+// float32 path (float32 queries, float32 or INT8 caches): plain VALU arithmetic, one wave
+// per (split, row, query head); same key lists and partial format, merged by merge_kernel.
 // ---------------------------------------------------------------------------------------
 template <int KIND, typename KT, typename AT, int D, bool DIRECT>
 __global__ __launch_bounds__(64) void split_attn_f32_kernel(SplitParams P) {
@@ -458,32 +583,9 @@ __global__ __launch_bounds__(64) void split_attn_f32_kernel(SplitParams P) {
   const int head = rem - r * P.H_q;
   const int c = head / P.group;
   int flags = 0;
-  RowInfo ri = resolve_row(P.cu, P.seqlens_k, P.B, r, P.max_q, P.max_k, flags);
-  int src = SRC_RANGE, v0 = 0, v1 = 0, lo = 0, cnt = 0;
-  const int32_t* sel = nullptr;
-  if (ri.b >= 0) {
-    int s = split;
-    if (KIND == SPATTN_KIND_LOCAL_AUX && split >= P.n_main) { src = SRC_AUX; s = split - P.n_main; }
-    else if (KIND == SPATTN_KIND_SELECTED) src = SRC_SELECT;
-    if (src == SRC_RANGE) {
-      lo = P.window > 0 ? max(0, ri.p - P.window + 1) : 0;
-      cnt = ri.p - lo + 1;
-    } else {
-      sel = P.sel_idx + ((int64_t)r * P.H_kv + c) * P.max_sel;
-      if (P.sel_count != nullptr) {
-        cnt = P.sel_count[(int64_t)r * P.H_kv + c];
-        if (cnt < 0 || cnt > P.max_sel) flags |= SPATTN_STATUS_BAD_COUNT;
-        cnt = min(max(cnt, 0), P.max_sel);
-      } else {
-        cnt = P.max_sel;
-      }
-    }
-    v0 = s * P.chunk;
-    v1 = min(v0 + P.chunk, cnt);
-  }
-  const int n_keys = max(0, v1 - v0);
-  const bool is_i8 = sizeof(KT) == 1 && src != SRC_AUX;
-  // the query (key_scale folded in for INT8 caches)
+  const RowInfo ri = resolve_row(P.cu, P.seqlens_k, P.B, r, P.max_q, P.max_k, flags);
+  const SplitRange sr = split_range<KIND>(P, ri, r, c, split, flags);
+  const bool is_i8 = sizeof(KT) == 1 && sr.src != SRC_AUX;
   constexpr int PER = D / 64;
   float qv[D];
   const float* q32 = reinterpret_cast<const float*>(P.q) + ((int64_t)r * P.H_q + head) * D;
@@ -491,30 +593,13 @@ __global__ __launch_bounds__(64) void split_attn_f32_kernel(SplitParams P) {
   float m_run = kNegInf, l_run = 0.f, acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  for (int base = 0; base < n_keys; base += 64) {
+  for (int base = 0; base < sr.n_keys; base += 64) {
     const int v = base + lane;
-    int row = -1;
-    if (v < n_keys) {
-      if (src == SRC_RANGE) {
-        row = key_row_range(P, ri.b, c, lo, v0 + v, flags);
-      } else {
-        const int j = sel[v0 + v];
-        if (src == SRC_SELECT) {
-          if (j != -1 && (j < 0 || j >= ri.kv_len)) flags |= SPATTN_STATUS_BAD_INDEX;
-          else if (j >= 0 && j <= ri.p) {
-            const int64_t off = cache_row(P.cd, ri.b, j, c, flags);
-            row = off < 0 ? -1 : (int)(off / P.D);
-          }
-        } else {
-          if (j != -1 && (j < 0 || j >= P.aux_len)) flags |= SPATTN_STATUS_BAD_INDEX;
-          else if (j >= 0) row = (int)(ri.b * P.aux_row_stride + (int64_t)j * P.H_kv + c);
-        }
-      }
-    }
+    const int row = v < sr.n_keys ? split_key_row(P, sr, ri, c, v, flags) : -1;
     float s = kNegInf;
     if (row >= 0) {
       float dot = 0.f;
-      if (src == SRC_AUX) {
+      if (sr.src == SRC_AUX) {
         const AT* kr = reinterpret_cast<const AT*>(P.aux_k) + (int64_t)row * D;
         for (int d = 0; d < D; ++d) dot += qv[d] * to_f32(kr[d]);
       } else {
@@ -526,31 +611,29 @@ __global__ __launch_bounds__(64) void split_attn_f32_kernel(SplitParams P) {
     float mt = s;
     for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
     const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
     rows[lane] = row;
-    float p = 0.f;
-    if (m_new != kNegInf) p = exp2_safe(s - m_new);
+    const float p = exp2_safe(s - m_use);
     pw[lane] = p;
     __syncthreads();
-    if (m_new != kNegInf) {
-      float ps = p;
-      for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
-      const float alpha = exp2_safe(m_run - m_new);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
+    float ps = p;
+    for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
+    const float alpha = exp2_safe(m_run - m_use);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] *= alpha;
-      for (int kk = 0; kk < 64; ++kk) {
-        const int rw = rows[kk];
-        if (rw < 0) continue;
-        const float w = pw[kk];
+    for (int k = 0; k < PER; ++k) acc[k] *= alpha;
+    for (int kk = 0; kk < 64; ++kk) {
+      const int rw = rows[kk];
+      if (rw < 0) continue;
+      const float w = pw[kk];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const int d = lane + 64 * k;
-          float x;
-          if (src == SRC_AUX) x = to_f32(reinterpret_cast<const AT*>(P.aux_v)[(int64_t)rw * D + d]);
-          else x = to_f32(reinterpret_cast<const KT*>(P.v_cache)[(int64_t)rw * D + d]);
-          acc[k] += w * x;
-        }
+      for (int k = 0; k < PER; ++k) {
+        const int d = lane + 64 * k;
+        float x;
+        if (sr.src == SRC_AUX) x = to_f32(reinterpret_cast<const AT*>(P.aux_v)[(int64_t)rw * D + d]);
+        else x = to_f32(reinterpret_cast<const KT*>(P.v_cache)[(int64_t)rw * D + d]);
+        acc[k] += w * x;
       }
     }
     __syncthreads();
@@ -593,19 +676,22 @@ bool use_prefill_path(int kind, int dtype, int max_q) {
   return kind == SPATTN_KIND_PAGED && dtype != SPATTN_F32 && max_q > 8;
 }
 
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_k, int max_sel,
                           int window, int H_q, int H_kv, int D) {
   (void)B; (void)max_q;
   SplitPlan pl{};
   const int group = H_q / H_kv;
-  pl.head_tiles = dtype == SPATTN_F32 ? 1 : (group + 15) / 16;
+  const bool f32 = dtype == SPATTN_F32;
+  pl.head_tiles = f32 ? 1 : (group + 15) / 16;
   long n_main = 0, n_aux = 0;
   if (kind == SPATTN_KIND_PAGED) n_main = window > 0 ? std::min(window, max_k) : max_k;
   else if (kind == SPATTN_KIND_SELECTED) n_main = max_sel;
   else { n_main = window; n_aux = max_sel; }
   n_main = std::max(0L, n_main);
   n_aux = std::max(0L, n_aux);
-  const long items = (long)T * (dtype == SPATTN_F32 ? H_q : (long)H_kv * pl.head_tiles);
+  const long items = (long)T * (f32 ? H_q : (long)H_kv * pl.head_tiles);
   const long total = n_main + n_aux;
   int chunk = kWgStep;
   auto splits_for = [&](int ch) {
@@ -613,6 +699,11 @@ SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_
     return std::max(1L, s);
   };
   while (chunk < kMaxChunk && chunk < total && items * splits_for(chunk) > kTargetWorkgroups) chunk *= 2;
+  while (splits_for(chunk) > kMaxSplits && chunk < kChunkCap) chunk *= 2;
+  if (splits_for(chunk) > kMaxSplits) {  // key range too long for one call
+    pl.n_splits = -1;
+    return pl;
+  }
   pl.chunk = chunk;
   pl.n_main = (int)std::max(1L, (n_main + chunk - 1) / chunk);
   pl.n_aux = (int)((n_aux + chunk - 1) / chunk);
@@ -622,19 +713,17 @@ SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_
   if (pl.n_splits > 1) {
     const size_t acc = (size_t)pl.n_splits * T * H_q * D * sizeof(float);
     const size_t ml = (size_t)pl.n_splits * T * H_q * sizeof(float2);
-    pl.ws_bytes = ((acc + 255) / 256) * 256 + ((ml + 255) / 256) * 256;
+    const size_t cnt = (size_t)T * H_kv * pl.head_tiles * sizeof(int32_t);
+    pl.ws_bytes = align256(acc) + align256(ml) + align256(cnt);
   }
   return pl;
 }
 
 template <int KIND, typename QT, typename KT, typename AT, int D>
-static void launch_split_typed(const SplitParams& P, bool direct, hipStream_t stream) {
+static void launch_split_typed(const SplitParams& P, hipStream_t stream) {
   const int blocks = P.n_splits * P.T * P.H_kv * P.head_tiles;
-  const size_t lds = SplitLds<D>::kTotal;
-  if (direct)
-    hipLaunchKernelGGL((split_attn_kernel<KIND, QT, KT, AT, D, true>), dim3(blocks), dim3(kThreads), lds, stream, P);
-  else
-    hipLaunchKernelGGL((split_attn_kernel<KIND, QT, KT, AT, D, false>), dim3(blocks), dim3(kThreads), lds, stream, P);
+  const size_t lds = split_lds_bytes<D>(P.chunk, P.meta_lds ? 2 * (P.B + 1) : 0);
+  hipLaunchKernelGGL((split_attn_kernel<KIND, QT, KT, AT, D>), dim3(blocks), dim3(kThreads), lds, stream, P);
 }
 
 template <int KIND, typename KT, typename AT, int D>
@@ -647,28 +736,28 @@ static void launch_split_f32(const SplitParams& P, bool direct, hipStream_t stre
 }
 
 template <int KIND, typename QT, int D>
-static int dispatch_cache(const AttnArgs& a, const SplitParams& P, bool direct, hipStream_t stream) {
+static void dispatch_cache(const AttnArgs& a, const SplitParams& P, bool direct, hipStream_t stream) {
   const bool i8 = a.cache_dtype == SPATTN_I8;
   if constexpr (std::is_same<QT, float>::value) {
     if (i8) launch_split_f32<KIND, int8_t, float, D>(P, direct, stream);
     else launch_split_f32<KIND, float, float, D>(P, direct, stream);
   } else {
-    if (i8) launch_split_typed<KIND, QT, int8_t, QT, D>(P, direct, stream);
-    else launch_split_typed<KIND, QT, QT, QT, D>(P, direct, stream);
+    if (i8) launch_split_typed<KIND, QT, int8_t, QT, D>(P, stream);
+    else launch_split_typed<KIND, QT, QT, QT, D>(P, stream);
   }
-  return SPATTN_OK;
 }
 
 template <int KIND>
-static int dispatch_q(const AttnArgs& a, const SplitParams& P, bool direct, hipStream_t stream) {
+static void dispatch_q(const AttnArgs& a, const SplitParams& P, bool direct, hipStream_t stream) {
   if (a.D == 64) {
-    if (a.dtype == SPATTN_F32) return dispatch_cache<KIND, float, 64>(a, P, direct, stream);
-    if (a.dtype == SPATTN_F16) return dispatch_cache<KIND, f16, 64>(a, P, direct, stream);
-    return dispatch_cache<KIND, bf16, 64>(a, P, direct, stream);
+    if (a.dtype == SPATTN_F32) dispatch_cache<KIND, float, 64>(a, P, direct, stream);
+    else if (a.dtype == SPATTN_F16) dispatch_cache<KIND, f16, 64>(a, P, direct, stream);
+    else dispatch_cache<KIND, bf16, 64>(a, P, direct, stream);
+  } else {
+    if (a.dtype == SPATTN_F32) dispatch_cache<KIND, float, 128>(a, P, direct, stream);
+    else if (a.dtype == SPATTN_F16) dispatch_cache<KIND, f16, 128>(a, P, direct, stream);
+    else dispatch_cache<KIND, bf16, 128>(a, P, direct, stream);
   }
-  if (a.dtype == SPATTN_F32) return dispatch_cache<KIND, float, 128>(a, P, direct, stream);
-  if (a.dtype == SPATTN_F16) return dispatch_cache<KIND, f16, 128>(a, P, direct, stream);
-  return dispatch_cache<KIND, bf16, 128>(a, P, direct, stream);
 }
 
 int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t stream) {
@@ -692,27 +781,29 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   P.aux_len = a.aux_len;
   P.aux_row_stride = a.aux_stride / a.D;
   P.chunk = plan.chunk; P.n_main = plan.n_main; P.n_splits = plan.n_splits;
+  P.meta_lds = a.B + 1 <= kMetaLdsMax ? 1 : 0;
   P.scale_log2 = a.scale * kLog2e;
   const bool direct = plan.n_splits == 1;
-  P.ws_acc = nullptr; P.ws_ml = nullptr;
+  P.ws_acc = nullptr; P.ws_ml = nullptr; P.counters = nullptr;
   if (!direct) {
-    const size_t acc = (size_t)plan.n_splits * a.T * a.H_q * a.D * sizeof(float);
-    P.ws_acc = reinterpret_cast<float*>(a.workspace);
-    P.ws_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(a.workspace) + ((acc + 255) / 256) * 256);
+    const size_t acc = align256((size_t)plan.n_splits * a.T * a.H_q * a.D * sizeof(float));
+    const size_t ml = align256((size_t)plan.n_splits * a.T * a.H_q * sizeof(float2));
+    char* ws = reinterpret_cast<char*>(a.workspace);
+    P.ws_acc = reinterpret_cast<float*>(ws);
+    P.ws_ml = reinterpret_cast<float2*>(ws + acc);
+    P.counters = reinterpret_cast<int32_t*>(ws + acc + ml);
   }
-  int rc;
   switch (a.kind) {
-    case SPATTN_KIND_PAGED: rc = dispatch_q<SPATTN_KIND_PAGED>(a, P, direct, stream); break;
-    case SPATTN_KIND_SELECTED: rc = dispatch_q<SPATTN_KIND_SELECTED>(a, P, direct, stream); break;
-    default: rc = dispatch_q<SPATTN_KIND_LOCAL_AUX>(a, P, direct, stream); break;
+    case SPATTN_KIND_PAGED: dispatch_q<SPATTN_KIND_PAGED>(a, P, direct, stream); break;
+    case SPATTN_KIND_SELECTED: dispatch_q<SPATTN_KIND_SELECTED>(a, P, direct, stream); break;
+    default: dispatch_q<SPATTN_KIND_LOCAL_AUX>(a, P, direct, stream); break;
   }
-  if (rc != SPATTN_OK) return rc;
   if (hipGetLastError() != hipSuccess) return SPATTN_ERR_LAUNCH;
-  if (!direct) {
+  if (!direct && (a.dtype == SPATTN_F32 || !kFusedMerge)) {
     const int pairs = a.T * a.H_q;
     dim3 grid((pairs + 3) / 4);
-#define SPATTN_MERGE(QT, DD)                                                              \
-  hipLaunchKernelGGL((merge_kernel<QT, DD>), grid, dim3(256), 0, stream, P.ws_acc, P.ws_ml, \
+#define SPATTN_MERGE(QT, DD)                                                                 \
+  hipLaunchKernelGGL((merge_kernel<QT, DD>), grid, dim3(256), 0, stream, P.ws_acc, P.ws_ml,  \
                      a.sinks, a.out, a.T, a.H_q, plan.n_splits)
     if (a.D == 64) {
       if (a.dtype == SPATTN_F32) SPATTN_MERGE(float, 64);

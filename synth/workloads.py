@@ -11,8 +11,9 @@ Conventions (these are input conventions, not arithmetic of the method):
   minus one (the PagedAttention metadata page prints ``seqlen_k = -1`` for an empty
   request and ``seqlen_k = 1`` for a request holding two keys).
 * ``past_seqlens[b]`` is the key count already in the cache before this step.
-* The paged cache is ``[num_blocks, block_size, H_kv, D]``; a contiguous cache is
-  ``[B, capacity, H_kv, D]`` (``block_table`` is ``None``).
+* The paged cache is ``[num_blocks, H_kv, block_size, D]`` (each block holds its slots
+  head by head); a contiguous cache is ``[B, H_kv, capacity, D]`` (``block_table`` is
+  ``None``).  The auxiliary store is ``[B or 1, aux_len, H_kv, D]``.
 * bf16 tensors are carried as float32 arrays whose values are exactly representable in
   bf16 (``round_bf16``), because numpy has no bf16 type.
 """
@@ -85,7 +86,7 @@ class PagedCase:
     cu_seqlens_q: np.ndarray   # int32 [B+1]
     past_seqlens: np.ndarray   # int32 [B]
     seqlens_k: np.ndarray      # int32 [B]  (total keys - 1)
-    k_cache: np.ndarray        # [nb, bs, H_kv, D] or [B, cap, H_kv, D]
+    k_cache: np.ndarray        # [nb, H_kv, bs, D] or [B, H_kv, cap, D]
     v_cache: np.ndarray
     block_table: Optional[np.ndarray]   # int32 [B, max_blocks_per_seq] or None
     block_size: int            # block size, or capacity for a contiguous cache
@@ -202,7 +203,7 @@ def paged_case(seed: int, *, kv_lens, q_lens, H_q: int, H_kv: int, D: int,
         assert np.all(kv_lens <= cap)
         block_table = None
         bs = cap
-        shape = (B, cap, H_kv, D)
+        shape = (B, H_kv, cap, D)
         nblk = B
     else:
         bs = block_size
@@ -217,7 +218,7 @@ def paged_case(seed: int, *, kv_lens, q_lens, H_q: int, H_kv: int, D: int,
         for b in range(B):
             block_table[b, :need[b]] = perm[o:o + need[b]]
             o += need[b]
-        shape = (nblk, bs, H_kv, D)
+        shape = (nblk, H_kv, bs, D)
 
     q = _normal(rng, (T, H_q, D), dtype)
     if cache_dtype == I8:
@@ -247,12 +248,13 @@ def paged_case(seed: int, *, kv_lens, q_lens, H_q: int, H_kv: int, D: int,
         return int(block_table[b, j // bs]), j % bs
 
     if poison and cache_dtype != I8:
-        live = np.zeros(shape[:2], dtype=bool)
+        live = np.zeros((shape[0], shape[2]), dtype=bool)
         for b in range(B):
             for j in range(int(past[b])):
                 live[slot_of(b, j)] = True
-        k_cache[~live] = np.nan
-        v_cache[~live] = np.nan
+        dead = ~live
+        k_cache.transpose(0, 2, 1, 3)[dead] = np.nan
+        v_cache.transpose(0, 2, 1, 3)[dead] = np.nan
 
     if max_seqlen_q is None:
         max_seqlen_q = int(q_lens.max(initial=0))
@@ -326,10 +328,10 @@ def sparse_selected_case(seed: int, *, B: int, S_q: int, H_q: int, H_kv: int, D:
         for b in range(B):
             bt[b, :need[b]] = perm[o:o + need[b]]
             o += need[b]
-        shape = (nblk, block_size, H_kv, D)
+        shape = (nblk, H_kv, block_size, D)
         bsz = block_size
     else:
-        shape = (B, capacity, H_kv, D)
+        shape = (B, H_kv, capacity, D)
         bsz = capacity
     sel = _selected_indices(rng, T, H_kv, max_selected, counts, kv_lens[row_req], oor_frac)
     q = _normal(rng, (T, H_q, D), dtype)
@@ -353,9 +355,9 @@ def sparse_selected_case(seed: int, *, B: int, S_q: int, H_q: int, H_kv: int, D:
                 js = sel[r, c, :n]
                 js = js[(js >= 0) & (js < kv_lens[b])]
                 if bt is None:
-                    keep[b, js, c] = True
+                    keep[b, c, js] = True
                 else:
-                    keep[bt[b, js // bsz], js % bsz, c] = True
+                    keep[bt[b, js // bsz], c, js % bsz] = True
         k_cache[~keep] = np.nan
         v_cache[~keep] = np.nan
     return SparseCase(
@@ -388,7 +390,7 @@ def sparse_local_aux_case(seed: int, *, B: int, S_q: int, H_q: int, H_kv: int, D
     counts = np.asarray(counts, dtype=np.int64).reshape(T, H_kv)
     sel = _selected_indices(rng, T, H_kv, max_selected, counts, np.full(T, aux_len), oor_frac)
     q = _normal(rng, (T, H_q, D), dtype)
-    shape = (B, capacity, H_kv, D)
+    shape = (B, H_kv, capacity, D)
     if cache_dtype == I8:
         k_cache = _int8_uniform(rng, shape)
         v_cache = _int8_uniform(rng, shape)

@@ -203,3 +203,31 @@ def test_full_causal_prefill_sampled_rows():
     rng = np.random.default_rng(2)
     rows = sorted(set(rng.choice(case.T, size=12, replace=False).tolist()) | {3583, 5119})
     _sampled(case, rows, "paged_prefill_f16 no window (full)")
+
+
+def test_workspace_reuse_and_counter_reset():
+    # one zeroed workspace across many calls: the arrival counters must come back to zero
+    # and every call must give the same bits
+    case = synth.config_gqa_paged_decode(B=12, max_len=6000, seed=21)
+    t = case_tensors(case)
+    need = sta.attention_workspace_bytes(sta.KIND_PAGED, sta.F16, case.B, case.T, case.max_seqlen_q,
+                                         case.max_seqlen_k, 0, -1, case.H_q, case.H_kv, case.D)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], t["seqlens_k"], t["k_cache"], t["v_cache"],
+                        t["block_table"])
+    outs = []
+    for it in range(4):
+        out = torch.empty((case.T, case.H_q, case.D), dtype=torch.float16, device="cuda")
+        sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], t["seqlens_k"],
+                                case.max_seqlen_q, case.max_seqlen_k, out, block_table=t["block_table"],
+                                scale=case.scale, sinks=t["sinks"], workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    n_cnt = case.T * case.H_kv * 1 * 4
+    tail = ws[need - ((n_cnt + 255) // 256) * 256:]
+    assert int(tail.count_nonzero().item()) == 0
+    for o in outs[1:]:
+        assert torch.equal(o.cpu().view(torch.int16), outs[0].cpu().view(torch.int16))
+    ref, _, _ = oracle_paged_step(case)
+    assert_close(outs[0], ref, case.dtype, "workspace reuse")

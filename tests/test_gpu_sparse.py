@@ -84,7 +84,7 @@ def test_selected_single_key_is_the_value_row():
         for c in range(2):
             j = int(case.sel_idx[r, c, 0])
             p = 99 - 1 + (r % 2)
-            want = case.v_cache[b, j, c] if j <= p else np.zeros(64, np.float16)
+            want = case.v_cache[b, c, j] if j <= p else np.zeros(64, np.float16)
             for h in range(4 * c, 4 * c + 4):
                 assert np.array_equal(g[r, h].view(np.int16), want.view(np.int16))
 

@@ -35,9 +35,10 @@ def test_int8_error_bound():
 
 
 def _walk(cache, block_table, bs, b, j):
+    """All KV heads of position j of request b ([nb, H_kv, bs, D] blocks)."""
     if block_table is None:
-        return cache[b, j]
-    return cache[block_table[b][j // bs], j % bs]
+        return cache[b, :, j]
+    return cache[block_table[b][j // bs], :, j % bs]
 
 
 @pytest.mark.parametrize("contiguous", [False, True])
@@ -60,7 +61,7 @@ def test_append_places_rows_at_their_positions(contiguous):
                 want = case.k_new[cu[b] + j - (kv_len - q_len)]
             assert np.array_equal(got_k, want, equal_nan=True)
     # nothing else changed: compare everything not written
-    written = np.zeros(kc.shape[:2], dtype=bool)
+    written = np.zeros((kc.shape[0], kc.shape[2]), dtype=bool)
     for b in range(case.B):
         q_len = int(cu[b + 1] - cu[b])
         kv_len = int(case.seqlens_k[b]) + 1
@@ -69,8 +70,9 @@ def test_append_places_rows_at_their_positions(contiguous):
                 written[b, j] = True
             else:
                 written[case.block_table[b][j // case.block_size], j % case.block_size] = True
-    assert np.array_equal(kc[~written], case.k_cache[~written], equal_nan=True)
-    assert np.array_equal(vc[~written], case.v_cache[~written], equal_nan=True)
+    tr = (0, 2, 1, 3)
+    assert np.array_equal(kc.transpose(tr)[~written], case.k_cache.transpose(tr)[~written], equal_nan=True)
+    assert np.array_equal(vc.transpose(tr)[~written], case.v_cache.transpose(tr)[~written], equal_nan=True)
 
 
 def test_append_int8_quantises_with_channel_scales():

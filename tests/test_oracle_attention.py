@@ -42,13 +42,14 @@ def _dense_request(rng, kv_len, H_kv, D):
 
 
 def _page(rng, dense_k, dense_v, bs, extra_blocks=3):
-    """Lay dense per-request K/V into a shuffled paged pool (this test's own layout)."""
+    """Lay dense per-request K/V ([L, H_kv, D]) into a shuffled paged pool with the
+    library's block layout [nb, H_kv, bs, D] (this test's own layout code)."""
     B = len(dense_k)
     need = [(len(k) + bs - 1) // bs for k in dense_k]
     nb = sum(need) + extra_blocks
     H_kv, D = dense_k[0].shape[1:]
-    kc = np.full((nb, bs, H_kv, D), np.nan)
-    vc = np.full((nb, bs, H_kv, D), np.nan)
+    kc = np.full((nb, H_kv, bs, D), np.nan)
+    vc = np.full((nb, H_kv, bs, D), np.nan)
     perm = rng.permutation(nb)
     bt = np.full((B, max(need) + 1), -1, dtype=np.int32)
     o = 0
@@ -59,8 +60,8 @@ def _page(rng, dense_k, dense_v, bs, extra_blocks=3):
             bt[b, lb] = blk
             seg = slice(lb * bs, min((lb + 1) * bs, len(dense_k[b])))
             n = seg.stop - seg.start
-            kc[blk, :n] = dense_k[b][seg]
-            vc[blk, :n] = dense_v[b][seg]
+            kc[blk, :, :n] = dense_k[b][seg].transpose(1, 0, 2)
+            vc[blk, :, :n] = dense_v[b][seg].transpose(1, 0, 2)
     return kc, vc, bt
 
 
@@ -102,14 +103,14 @@ def test_paged_matches_library_sdpa(seed, W, with_sink, g):
 def test_single_visible_key_closed_form():
     rng = np.random.default_rng(7)
     D, L = 32, 9
-    k = rng.standard_normal((1, L, 1, D))
-    v = rng.standard_normal((1, L, 1, D))
+    k = rng.standard_normal((1, 1, L, D))     # contiguous cache [B, H_kv, cap, D]
+    v = rng.standard_normal((1, 1, L, D))
     q = rng.standard_normal((1, 2, D))
     sinks = np.array([0.7, -1.3])
     cu = np.array([0, 1], dtype=np.int32)
     out, _ = oracle.paged_attention(q, k, v, cu, np.array([L - 1]), H_kv=1, scale=0.25,
                                     local_window=1, sinks=sinks)
-    kk, vv = k[0, L - 1, 0], v[0, L - 1, 0]
+    kk, vv = k[0, 0, L - 1], v[0, 0, L - 1]
     for h in range(2):
         s = 0.25 * float(q[0, h] @ kk)
         np.testing.assert_allclose(out[0, h], vv / (1.0 + math.exp(sinks[h] - s)), rtol=1e-14)
@@ -119,8 +120,8 @@ def test_single_visible_key_closed_form():
 def test_visible_key_count_matches_window_formula(W):
     # K = 0 makes every score 0; V = 1 and sink 0 then give o = n / (n + 1)
     L, n_q = 40, 12
-    k = np.zeros((1, L, 1, 8))
-    v = np.ones((1, L, 1, 8))
+    k = np.zeros((1, 1, L, 8))
+    v = np.ones((1, 1, L, 8))
     q = np.ones((n_q, 1, 8))
     cu = np.array([0, n_q], dtype=np.int32)
     out, _ = oracle.paged_attention(q, k, v, cu, np.array([L - 1]), H_kv=1, scale=1.0,
@@ -181,8 +182,8 @@ def test_replicated_kv_heads_equal_gqa():
     case = _small_case()
     g = case.H_q // case.H_kv
     a, _ = _run_paged(case)
-    kc = np.repeat(case.k_cache, g, axis=2)
-    vc = np.repeat(case.v_cache, g, axis=2)
+    kc = np.repeat(case.k_cache, g, axis=1)
+    vc = np.repeat(case.v_cache, g, axis=1)
     b, _ = oracle.paged_attention(case.q, kc, vc, case.cu_seqlens_q, case.seqlens_k, H_kv=case.H_q,
                                   block_table=case.block_table, block_size=case.block_size,
                                   scale=case.scale, sinks=case.sinks)
@@ -211,8 +212,8 @@ def test_selecting_every_position_equals_paged_causal():
 def test_int8_equals_dequantised_float_cache():
     case = _small_case(seed=23, dtype=synth.F16, cache_dtype=synth.I8)
     a, _ = _run_paged(case)
-    kf = case.k_cache.astype(np.float64) * case.key_scale.astype(np.float64)[None, None]
-    vf = case.v_cache.astype(np.float64) * case.value_scale.astype(np.float64)[None, None]
+    kf = case.k_cache.astype(np.float64) * case.key_scale.astype(np.float64)[None, :, None, :]
+    vf = case.v_cache.astype(np.float64) * case.value_scale.astype(np.float64)[None, :, None, :]
     b, _ = oracle.paged_attention(case.q, kf, vf, case.cu_seqlens_q, case.seqlens_k, H_kv=case.H_kv,
                                   block_table=case.block_table, block_size=case.block_size,
                                   scale=case.scale, sinks=case.sinks)
@@ -308,8 +309,8 @@ def test_local_plus_aux_matches_library_sdpa():
         p = L - 3 + i
         for c in range(2):
             local = list(range(max(0, p - 5), p + 1))
-            Km = case.k_cache[b, local, c].astype(np.float64) * case.key_scale[c]
-            Vm = case.v_cache[b, local, c].astype(np.float64) * case.value_scale[c]
+            Km = case.k_cache[b, c, local].astype(np.float64) * case.key_scale[c]
+            Vm = case.v_cache[b, c, local].astype(np.float64) * case.value_scale[c]
             idx = case.sel_idx[r, c, :case.sel_count[r, c]]
             Ka = case.aux_k[b, idx, c].astype(np.float64)
             Va = case.aux_v[b, idx, c].astype(np.float64)
