@@ -15,11 +15,11 @@
 //  1. cu_seqlens_q / seqlens_k are staged in LDS in one parallel round and the row's
 //     request and key position are found by binary search there;
 //  2. the split's keys are turned into cache-row indices in LDS (one pass, guarded);
-//  3. each wave takes 32-key tiles, double-buffered (the next tile's loads are in flight
-//     while the current one is computed): S^T = K Q^T with v_mfma_f32_16x16x32 (K rows
-//     loaded straight into the A operand with 16-byte loads), an online softmax in the
-//     log2 domain (the accumulator is rescaled only when a running maximum moved), then
-//     O^T += V^T P^T where V^T comes from LDS through ds_read_b64_tr_b16;
+//  3. each wave takes 32-key tiles: K rows are loaded straight into the A operand of
+//     S^T = K Q^T (v_mfma_f32_16x16x32, 16-byte loads) while V rows go into the wave's LDS
+//     buffer by DMA (global_load_lds_dwordx4, no registers held while in flight); an online
+//     softmax in the log2 domain (the accumulator is rescaled only when a running maximum
+//     moved), then O^T += V^T P^T with V^T read through ds_read_b64_tr_b16;
 //  4. the four wave states are merged in LDS.  With one split the workgroup writes the
 //     normalised output; otherwise it writes its partial (m, l, acc) and bumps the item's
 //     arrival counter, and the last workgroup to arrive merges every split of the item,
@@ -43,7 +43,6 @@ constexpr int kChunkCap = 4096;    // keys per split, hard limit (LDS row-index 
 constexpr int kMaxSplits = 256;    // splits per item (LDS merge coefficients)
 constexpr int kTargetWorkgroups = 4096;
 constexpr bool kFusedMerge = false;  // last-arriving workgroup merges (else a merge kernel)
-constexpr bool kPipelined = false;  // next tile's loads in flight during the current tile
 constexpr int kMetaLdsMax = 512;   // cu entries staged in LDS (more: binary search in memory)
 
 enum Src { SRC_RANGE = 0, SRC_SELECT = 1, SRC_AUX = 2 };
@@ -121,8 +120,8 @@ __device__ __forceinline__ void flush_flags(int flags, int32_t* status) {
 // loop), then the split's cache-row indices, then the staged metadata.
 template <int D>
 struct SplitLds {
-  static constexpr int kVld = D + 16;                       // padded V tile row (elements)
-  static constexpr int kVTileBytes = kTile * kVld * 2;
+  static constexpr bool kDeep = D == 64;                     // two tiles in flight per wave
+  static constexpr int kVTileBytes = (kDeep ? 2 : 1) * kTile * D * 2;  // a wave's V tiles
   static constexpr int kCombineBytes = kWaves * 16 * (D + 2) * 4;
   static constexpr int kAreaBytes = (kWaves * kVTileBytes > kCombineBytes) ? kWaves * kVTileBytes : kCombineBytes;
 };
@@ -132,46 +131,76 @@ static size_t split_lds_bytes(int chunk, int meta_ints) {
   return SplitLds<D>::kAreaBytes + (size_t)chunk * 4 + (size_t)meta_ints * 4;
 }
 
-// K and V of one 32-key tile for one lane: rows 16*st + (lane & 15), dims 32*kc + 8*(lane >> 4).
-template <typename OpT, int D>
-struct KvTile {
+// LDS-DMA of 16 bytes per lane: lane l's bytes land at lds + 16 * l (the LDS address is
+// wave-uniform; lanes that skip the call leave their 16 bytes untouched).
+__device__ __forceinline__ void dma16(const void* gptr, void* lds) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+// The compiler does not track LDS-DMA completion: wait for every vector memory operation
+// of this wave, and for every LDS operation before an LDS buffer is overwritten by DMA.
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// vmcnt wait with a compile-time count (gfx9 encoding: low 4 bits at [3:0], high 2 at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Issue the loads of one 32-key tile.  K rows 16*st + lam, dims 32*kc + 8*grp .. +7 come
+// straight into the A operand of S^T = K Q^T; 16-bit V rows go into the wave's LDS buffer
+// by DMA in the same lane layout (block (st, kc) of 1 KB, lane l at 16*l); INT8 V is loaded
+// into registers and converted.  Every lane issues every load (a masked key reads the
+// in-bounds rows `dk` / `dv`: its score is replaced by -inf and its V row, which must be
+// finite, gets weight 0), so each tile costs exactly 4*D/32 vector memory instructions and
+// can be waited for with a fixed vmcnt.
+template <typename OpT, typename KT, int D>
+struct TileRegs {
   typename OpVec<OpT>::v8 k[2][D / 32];
-  typename OpVec<OpT>::v8 v[2][D / 32];
-  uint32_t valid;  // bit i: key i of the tile exists
+  typename OpVec<OpT>::v8 v[2][D / 32];   // INT8 caches only
 };
 
 template <typename OpT, typename KT, int D>
-__device__ __forceinline__ void load_tile(KvTile<OpT, D>& t, const KT* __restrict__ kbase,
-                                          const KT* __restrict__ vbase, const int32_t* rows,
-                                          int n_keys, int base, int lam, int grp) {
-  typedef typename OpVec<OpT>::v8 V8;
-  const int row0 = (base + lam < n_keys) ? rows[base + lam] : -1;
-  const int row1 = (base + 16 + lam < n_keys) ? rows[base + 16 + lam] : -1;
+__device__ __forceinline__ void issue_tile(TileRegs<OpT, KT, D>& t, const KT* __restrict__ kbase,
+                                           const KT* __restrict__ vbase, const KT* dk,
+                                           const KT* dv, int row0, int row1, unsigned char* vbuf,
+                                           int grp) {
+  constexpr int KC = D / 32;
+  const int rows[2] = {row0, row1};
 #pragma unroll
-  for (int kc = 0; kc < D / 32; ++kc) {
-    const int col = kc * 32 + grp * 8;
-    V8 z = {};
-    t.k[0][kc] = row0 >= 0 ? load_op8<OpT>(kbase + (int64_t)row0 * D + col) : z;
-    t.k[1][kc] = row1 >= 0 ? load_op8<OpT>(kbase + (int64_t)row1 * D + col) : z;
-    t.v[0][kc] = row0 >= 0 ? load_op8<OpT>(vbase + (int64_t)row0 * D + col) : z;
-    t.v[1][kc] = row1 >= 0 ? load_op8<OpT>(vbase + (int64_t)row1 * D + col) : z;
-  }
-  const uint64_t b0 = __ballot(row0 >= 0);
-  const uint64_t b1 = __ballot(row1 >= 0);
-  t.valid = (uint32_t)(b0 & 0xFFFFu) | ((uint32_t)(b1 & 0xFFFFu) << 16);
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int col = kc * 32 + grp * 8;
+      const KT* kp = rows[st] >= 0 ? kbase + (int64_t)rows[st] * D + col : dk + col;
+      const KT* vp = rows[st] >= 0 ? vbase + (int64_t)rows[st] * D + col : dv + col;
+      if constexpr (sizeof(KT) == 2) dma16(vp, vbuf + (st * KC + kc) * 1024);
+      else t.v[st][kc] = load_op8<OpT>(vp);
+      t.k[st][kc] = load_op8<OpT>(kp);
+    }
 }
 
-// One tile of the online softmax and the two products (every lane runs it: the MFMAs
-// read operands of all 64 lanes).
-template <typename OpT, int D>
-__device__ __forceinline__ void compute_tile(const KvTile<OpT, D>& t,
+// Softmax update and both products for a tile whose loads have completed.
+template <typename OpT, typename KT, int D>
+__device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t valid,
                                              const typename OpVec<OpT>::v8 (&qop)[D / 32],
-                                             float scale_log2, OpT* vtile, float& m_run,
+                                             float scale_log2, unsigned char* vbuf, float& m_run,
                                              float& l_run, f32x4 (&acc)[D / 16], int lam, int grp) {
   typedef typename OpVec<OpT>::v8 V8;
   constexpr int KC = D / 32;
   constexpr int MT = D / 16;
-  constexpr int VLD = SplitLds<D>::kVld;
+  if constexpr (sizeof(KT) == 1) {
+    // INT8 V: into the LDS buffer in the DMA lane layout (masked keys as zeros)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bool ok = (valid >> (16 * st + lam)) & 1u;
+        *reinterpret_cast<V8*>(vbuf + (st * KC + kc) * 1024 + 16 * (threadIdx.x & 63)) =
+            ok ? t.v[st][kc] : V8{};
+      }
+  }
   // S^T[key][head] for keys 16*st + 4*grp + i, head lam
   f32x4 s[2];
 #pragma unroll
@@ -181,20 +210,13 @@ __device__ __forceinline__ void compute_tile(const KvTile<OpT, D>& t,
     for (int kc = 0; kc < KC; ++kc) c = mfma16(t.k[st][kc], qop[kc], c);
     s[st] = c;
   }
-  // V tile -> LDS (row-major, padded), read back transposed below
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      *reinterpret_cast<V8*>(vtile + (16 * st + lam) * VLD + kc * 32 + grp * 8) = t.v[st][kc];
-
   float mt = kNegInf;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = 16 * st + 4 * grp + i;
-      const float v = ((t.valid >> key) & 1u) ? s[st][i] * scale_log2 : kNegInf;
+      const float v = ((valid >> key) & 1u) ? s[st][i] * scale_log2 : kNegInf;
       s[st][i] = v;
       mt = fmaxf(mt, v);
     }
@@ -223,11 +245,15 @@ __device__ __forceinline__ void compute_tile(const KvTile<OpT, D>& t,
   psum = xor_sum(psum, 16);
   psum = xor_sum(psum, 32);
   l_run += psum;
+  if constexpr (sizeof(KT) == 1) wait_lgkm0();
+  const int s4 = lam >> 2, u = lam & 3;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    // lane (grp, lam) provides rows 4*grp + lam/4 (+16), columns 16*m + 4*(lam%4)
-    const OpT* a0 = vtile + (4 * grp + (lam >> 2)) * VLD + 16 * m + 4 * (lam & 3);
-    const OpT* a1 = a0 + 16 * VLD;
+    // V[key][dim] sits in block (key / 16, dim / 32) at lane slot (key % 16) + 16 * ((dim % 32) / 8)
+    // and byte 2 * (dim % 8); lane (grp, 4*s4 + u) fetches key 4*grp + s4 (+16), dims 16m + 4u ..
+    const int slot = 4 * grp + s4 + 16 * (2 * (m & 1) + (u >> 1));
+    const unsigned char* a0 = vbuf + (m >> 1) * 1024 + slot * 16 + (u & 1) * 8;
+    const unsigned char* a1 = a0 + KC * 1024;
     s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a0));
     s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a1));
     typename OpVec<OpT>::v4 h0 = __builtin_bit_cast(typename OpVec<OpT>::v4, r0);
@@ -237,38 +263,72 @@ __device__ __forceinline__ void compute_tile(const KvTile<OpT, D>& t,
   }
 }
 
-// The key loop of one wave over one source, with the next tile's loads in flight while the
-// current tile is computed.  `rows` holds the cache-row index (row of D elements counted
-// from kbase / vbase) of each key of the split, or -1.
+__device__ __forceinline__ uint32_t tile_valid(int row0, int row1) {
+  const uint64_t b0 = __ballot(row0 >= 0);
+  const uint64_t b1 = __ballot(row1 >= 0);
+  return (uint32_t)(b0 & 0xFFFFu) | ((uint32_t)(b1 & 0xFFFFu) << 16);
+}
+
+// The key loop of one wave over one source, two tiles deep: the next tile's loads are in
+// flight while the current tile is computed (V tiles alternate between two LDS buffers).
+// `rows` holds the cache-row index (row of D elements counted from kbase / vbase) of each
+// key of the split, or -1; `dk` is any in-bounds row and `dv` an in-bounds row of finite
+// values, read for masked keys.
 template <typename OpT, typename KT, int D>
 __device__ __forceinline__ void wave_keys(const KT* __restrict__ kbase, const KT* __restrict__ vbase,
-                                          const int32_t* rows, int n_keys,
+                                          const KT* dk, const KT* dv, const int32_t* rows, int n_keys,
                                           const typename OpVec<OpT>::v8 (&qop)[D / 32],
-                                          float scale_log2, OpT* vtile, float& m_run,
+                                          float scale_log2, unsigned char* vbuf2, float& m_run,
                                           float& l_run, f32x4 (&acc)[D / 16]) {
+  constexpr int kTileBytes = (D / 32) * 2 * 1024;
+  constexpr int kOps = 4 * (D / 32);   // vector memory instructions per tile
+  constexpr bool kDeep = SplitLds<D>::kDeep;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lam = lane & 15;
   const int grp = lane >> 4;
   const int n_tiles = (n_keys + kTile - 1) / kTile;
-  KvTile<OpT, D> ta, tb;
+  auto row_of = [&](int tile, int k) {
+    const int key = tile * kTile + k;
+    return key < n_keys ? rows[key] : -1;
+  };
+  TileRegs<OpT, KT, D> ta, tb;
   int tile = wave;
-  if constexpr (!kPipelined) {
+  if (tile >= n_tiles) return;
+  if constexpr (!kDeep) {
+    // one tile at a time (wider heads need the registers for more waves instead)
     for (; tile < n_tiles; tile += kWaves) {
-      load_tile<OpT, KT, D>(ta, kbase, vbase, rows, n_keys, tile * kTile, lam, grp);
-      compute_tile<OpT, D>(ta, qop, scale_log2, vtile, m_run, l_run, acc, lam, grp);
+      const int r0 = row_of(tile, lam), r1 = row_of(tile, 16 + lam);
+      const uint32_t v = tile_valid(r0, r1);
+      wait_lgkm0();
+      issue_tile<OpT, KT, D>(ta, kbase, vbase, dk, dv, r0, r1, vbuf2, grp);
+      wait_vm<0>();
+      consume_tile<OpT, KT, D>(ta, v, qop, scale_log2, vbuf2, m_run, l_run, acc, lam, grp);
     }
     return;
   }
-  if (tile < n_tiles) load_tile<OpT, KT, D>(ta, kbase, vbase, rows, n_keys, tile * kTile, lam, grp);
-  for (; tile < n_tiles; tile += 2 * kWaves) {
-    const int t1 = tile + kWaves;
-    if (t1 < n_tiles) load_tile<OpT, KT, D>(tb, kbase, vbase, rows, n_keys, t1 * kTile, lam, grp);
-    compute_tile<OpT, D>(ta, qop, scale_log2, vtile, m_run, l_run, acc, lam, grp);
-    if (t1 >= n_tiles) break;
-    const int t2 = t1 + kWaves;
-    if (t2 < n_tiles) load_tile<OpT, KT, D>(ta, kbase, vbase, rows, n_keys, t2 * kTile, lam, grp);
-    compute_tile<OpT, D>(tb, qop, scale_log2, vtile, m_run, l_run, acc, lam, grp);
+  int a0 = row_of(tile, lam), a1 = row_of(tile, 16 + lam);
+  uint32_t va = tile_valid(a0, a1);
+  issue_tile<OpT, KT, D>(ta, kbase, vbase, dk, dv, a0, a1, vbuf2, grp);
+  int buf = 0;
+  for (;;) {
+    const int next = tile + kWaves;
+    if (next < n_tiles) {
+      const int b0 = row_of(next, lam), b1 = row_of(next, 16 + lam);
+      const uint32_t vb = tile_valid(b0, b1);
+      wait_lgkm0();  // the LDS buffer about to be refilled has been read
+      issue_tile<OpT, KT, D>(tb, kbase, vbase, dk, dv, b0, b1, vbuf2 + (buf ^ 1) * kTileBytes, grp);
+      wait_vm<kOps>();  // everything but the next tile has landed
+      consume_tile<OpT, KT, D>(ta, va, qop, scale_log2, vbuf2 + buf * kTileBytes, m_run, l_run, acc, lam, grp);
+      ta = tb;
+      va = vb;
+      buf ^= 1;
+      tile = next;
+    } else {
+      wait_vm<0>();
+      consume_tile<OpT, KT, D>(ta, va, qop, scale_log2, vbuf2 + buf * kTileBytes, m_run, l_run, acc, lam, grp);
+      break;
+    }
   }
 }
 
@@ -319,8 +379,11 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
   return -1;
 }
 
+// Occupancy hint for D = 64 (two tiles in flight per wave): 5 waves per SIMD fit without
+// spilling; more tiles in flight per CU is what the memory-bound key loop needs.
 template <int KIND, typename QT, typename KT, typename AT, int D>
-__global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 1, 8)))
+void split_attn_kernel(SplitParams P) {
   typedef typename std::conditional<sizeof(KT) == 1, f16, KT>::type OpM;  // main operand
   typedef QT OpA;                                                          // aux operand
   extern __shared__ __align__(16) unsigned char smem[];
@@ -377,6 +440,7 @@ __global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
     const int head = h0 + lam;
     const bool hv = lam < nh;
     const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + head) * D;
+    const QT* q0row = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0) * D;
     if (KIND != SPATTN_KIND_LOCAL_AUX || sr.src != SRC_AUX) {
       typename OpVec<OpM>::v8 qop[D / 32];
 #pragma unroll
@@ -391,10 +455,15 @@ __global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
                        : typename OpVec<OpM>::v8{};
         }
       }
+      // masked keys read row 0 of the cache for K and, with 16-bit caches, the query row of
+      // the tile's first head for V (in bounds for every lane, and finite); INT8 V of masked
+      // keys is replaced by zeros
+      const KT* dv = sizeof(KT) == 2 ? reinterpret_cast<const KT*>(q0row)
+                                     : reinterpret_cast<const KT*>(P.k_cache);
       wave_keys<OpM, KT, D>(reinterpret_cast<const KT*>(P.k_cache),
-                            reinterpret_cast<const KT*>(P.v_cache), rows, sr.n_keys, qop,
-                            P.scale_log2, reinterpret_cast<OpM*>(area + wave * SplitLds<D>::kVTileBytes),
-                            m_run, l_run, acc);
+                            reinterpret_cast<const KT*>(P.v_cache),
+                            reinterpret_cast<const KT*>(P.k_cache), dv, rows, sr.n_keys, qop,
+                            P.scale_log2, area + wave * SplitLds<D>::kVTileBytes, m_run, l_run, acc);
     } else if constexpr (sizeof(AT) == 2) {
       typename OpVec<OpA>::v8 qop[D / 32];
 #pragma unroll
@@ -402,9 +471,10 @@ __global__ __launch_bounds__(kThreads) void split_attn_kernel(SplitParams P) {
         qop[kc] = hv ? __builtin_bit_cast(typename OpVec<OpA>::v8, load16(qrow + kc * 32 + grp * 8))
                      : typename OpVec<OpA>::v8{};
       wave_keys<OpA, AT, D>(reinterpret_cast<const AT*>(P.aux_k),
-                            reinterpret_cast<const AT*>(P.aux_v), rows, sr.n_keys, qop,
-                            P.scale_log2, reinterpret_cast<OpA*>(area + wave * SplitLds<D>::kVTileBytes),
-                            m_run, l_run, acc);
+                            reinterpret_cast<const AT*>(P.aux_v),
+                            reinterpret_cast<const AT*>(q0row), reinterpret_cast<const AT*>(q0row),
+                            rows, sr.n_keys, qop,
+                            P.scale_log2, area + wave * SplitLds<D>::kVTileBytes, m_run, l_run, acc);
     }
   }
   __syncthreads();
