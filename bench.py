@@ -86,7 +86,7 @@ def bench_decode(steps, warmup, copies=3):
     need = sta.attention_workspace_bytes(sta.KIND_PAGED, sta.F16, B, T, case.max_seqlen_q,
                                          case.max_seqlen_k, 0, case.local_window, case.H_q,
                                          case.H_kv, case.D)
-    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")  # counters start at zero
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step(i, ev=None):
         t = sets[i % copies]

@@ -142,10 +142,9 @@ SPATTN_API int kv_cache_append(const void* k_new, const void* v_new, int new_dty
  * attention_workspace_bytes - device workspace (bytes) an attention call with these
  * arguments needs for its split-K partial softmax states ([SPA] file summaries and
  * follow-up description: FP32 partial states merged by a finalize stage).  Pure host
- * function; 0 means the call may pass workspace = NULL.  The workspace also holds
- * per-(row, KV head) arrival counters that must be ZERO before the first call that uses
- * it (allocate it zeroed once); every call leaves them zero again.  Calls that may run
- * at the same time need separate workspaces.  `kind` is SPATTN_KIND_*;
+ * function; 0 means the call may pass workspace = NULL.  Its contents need no
+ * initialisation; calls that may run at the same time need separate workspaces.  `kind`
+ * is SPATTN_KIND_*;
  * max_seqlen_k is used by SPATTN_KIND_PAGED, max_selected by the sparse kinds,
  * local_window by SPATTN_KIND_PAGED and SPATTN_KIND_LOCAL_AUX, dtype is the Q dtype.
  * Returns (size_t)-1 for arguments the attention calls would reject (including key

@@ -133,8 +133,7 @@ def _workspace(ws: Optional[torch.Tensor], nbytes: int, like: torch.Tensor):
     if nbytes == 0:
         return None, 0
     if ws is None:
-        # zeroed: the workspace's arrival counters must start at zero (calls leave them zero)
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=like.device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
     return ws, int(ws.numel() * ws.element_size())
 
 

@@ -21,9 +21,10 @@
 //     softmax in the log2 domain (the accumulator is rescaled only when a running maximum
 //     moved), then O^T += V^T P^T with V^T read through ds_read_b64_tr_b16;
 //  4. the four wave states are merged in LDS.  With one split the workgroup writes the
-//     normalised output; otherwise it writes its partial (m, l, acc) and bumps the item's
-//     arrival counter, and the last workgroup to arrive merges every split of the item,
-//     applies the sink, writes the output and resets the counter to zero.
+//     normalised output; otherwise it writes its partial (m, l, acc) and a merge kernel
+//     combines the splits of every (row, query head) and applies the sink.  (Merging in the
+//     last-arriving workgroup instead needs an agent-scope release per workgroup, which on
+//     this chip writes back the L2 and measured several times slower.)
 //
 // INT8 caches: key_scale is folded into the query operand (f16), value_scale is applied
 // to the accumulator before it leaves the workgroup.
@@ -42,7 +43,6 @@ constexpr int kMaxChunk = 2048;    // keys per split while there are enough work
 constexpr int kChunkCap = 4096;    // keys per split, hard limit (LDS row-index buffer)
 constexpr int kMaxSplits = 256;    // splits per item (LDS merge coefficients)
 constexpr int kTargetWorkgroups = 4096;
-constexpr bool kFusedMerge = false;  // last-arriving workgroup merges (else a merge kernel)
 constexpr int kMetaLdsMax = 512;   // cu entries staged in LDS (more: binary search in memory)
 
 enum Src { SRC_RANGE = 0, SRC_SELECT = 1, SRC_AUX = 2 };
@@ -92,7 +92,6 @@ struct SplitParams {
   void* out;
   float* ws_acc;    // [n_splits][T][H_q][D]
   float2* ws_ml;    // [n_splits][T][H_q]
-  int32_t* counters;  // [T][H_kv][head_tiles], zero between calls
   int32_t* status;
   CacheDesc cd;
   int B, T, H_q, H_kv, D, group, head_tiles;
@@ -120,7 +119,7 @@ __device__ __forceinline__ void flush_flags(int flags, int32_t* status) {
 // loop), then the split's cache-row indices, then the staged metadata.
 template <int D>
 struct SplitLds {
-  static constexpr bool kDeep = D == 64;                     // two tiles in flight per wave
+  static constexpr bool kDeep = false;  // two tiles in flight per wave: measured no faster
   static constexpr int kVTileBytes = (kDeep ? 2 : 1) * kTile * D * 2;  // a wave's V tiles
   static constexpr int kCombineBytes = kWaves * 16 * (D + 2) * 4;
   static constexpr int kAreaBytes = (kWaves * kVTileBytes > kCombineBytes) ? kWaves * kVTileBytes : kCombineBytes;
@@ -379,10 +378,10 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
   return -1;
 }
 
-// Occupancy hint for D = 64 (two tiles in flight per wave): 5 waves per SIMD fit without
-// spilling; more tiles in flight per CU is what the memory-bound key loop needs.
+// Occupancy hint for D = 64: 7 waves per SIMD fit in 72 registers without spilling (more
+// waves, more tiles in flight per CU for the memory-bound key loop).
 template <int KIND, typename QT, typename KT, typename AT, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 1, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 7 : 1, 8)))
 void split_attn_kernel(SplitParams P) {
   typedef typename std::conditional<sizeof(KT) == 1, f16, KT>::type OpM;  // main operand
   typedef QT OpA;                                                          // aux operand
@@ -390,7 +389,6 @@ void split_attn_kernel(SplitParams P) {
   unsigned char* area = smem;
   int32_t* rows = reinterpret_cast<int32_t*>(smem + SplitLds<D>::kAreaBytes);
   int32_t* meta = rows + P.chunk;
-  __shared__ int last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -524,65 +522,6 @@ void split_attn_kernel(SplitParams P) {
       if (d == 0) P.ws_ml[so + (int64_t)r * P.H_q + head] = make_float2(M, L);
     }
   }
-  if (single || !kFusedMerge) return;
-
-  // ---- 5. the last workgroup of the item merges every split ----
-  const int item = (r * P.H_kv + c) * P.head_tiles + ht;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last_flag = atomicAdd(P.counters + item, 1) == P.n_splits - 1;
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  // per-split scale factors in LDS: fs[s][h] = exp2(m_s - M2), and 1 / L per head
-  float* fs = reinterpret_cast<float*>(area);                 // [n_splits][16]
-  float* inv = fs + P.n_splits * 16;                          // [16]
-  const int64_t stride = (int64_t)P.T * P.H_q;
-  if (tid < 16) {
-    const int h = tid;
-    float M = kNegInf;
-    if (h < nh) {
-      const int64_t pair = (int64_t)r * P.H_q + h0 + h;
-      for (int s = 0; s < P.n_splits; ++s) M = fmaxf(M, P.ws_ml[s * stride + pair].x);
-      float iv = 0.f;
-      if (M != kNegInf) {
-        const float sg = P.sinks != nullptr ? P.sinks[h0 + h] * kLog2e : kNegInf;
-        const float M2 = fmaxf(M, sg);
-        float L = exp2_safe(sg - M2);
-        for (int s = 0; s < P.n_splits; ++s) {
-          const float2 ml = P.ws_ml[s * stride + pair];
-          const float f = ml.x == kNegInf ? 0.f : exp2_safe(ml.x - M2);
-          fs[s * 16 + h] = f;
-          L += ml.y * f;
-        }
-        iv = 1.f / L;
-      } else {
-        for (int s = 0; s < P.n_splits; ++s) fs[s * 16 + h] = 0.f;
-      }
-      inv[h] = iv;
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < nh * D; e += kThreads) {
-    const int h = e / D, d = e - h * D;
-    const int64_t o = ((int64_t)r * P.H_q + h0 + h) * D + d;
-    float A = 0.f;
-    const float iv = inv[h];
-    if (iv != 0.f) {
-      int s = 0;
-      for (; s + 4 <= P.n_splits; s += 4) {
-        const float a0 = P.ws_acc[(s + 0) * stride * D + o];
-        const float a1 = P.ws_acc[(s + 1) * stride * D + o];
-        const float a2 = P.ws_acc[(s + 2) * stride * D + o];
-        const float a3 = P.ws_acc[(s + 3) * stride * D + o];
-        A += a0 * fs[(s + 0) * 16 + h] + a1 * fs[(s + 1) * 16 + h] + a2 * fs[(s + 2) * 16 + h] +
-             a3 * fs[(s + 3) * 16 + h];
-      }
-      for (; s < P.n_splits; ++s) A += P.ws_acc[s * stride * D + o] * fs[s * 16 + h];
-    }
-    reinterpret_cast<QT*>(P.out)[o] = from_f32<QT>(A * iv);
-  }
-  if (tid == 0) P.counters[item] = 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -624,7 +563,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
     for (int k = 0; k < PER; ++k) A[k] = 0.f;
     for (int s = 0; s < n_splits; ++s) {
       const float2 ml = ws_ml[s * stride + pair];
-      const float f = ml.x == kNegInf ? 0.f : exp2_safe(ml.x - M2);
+      if (ml.x == kNegInf) continue;   // empty split
+      const float f = exp2_safe(ml.x - M2);
       const float* a = ws_acc + (s * stride + pair) * D;
 #pragma unroll
       for (int k = 0; k < PER; ++k) A[k] += a[lane + 64 * k] * f;
@@ -783,8 +723,7 @@ SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_
   if (pl.n_splits > 1) {
     const size_t acc = (size_t)pl.n_splits * T * H_q * D * sizeof(float);
     const size_t ml = (size_t)pl.n_splits * T * H_q * sizeof(float2);
-    const size_t cnt = (size_t)T * H_kv * pl.head_tiles * sizeof(int32_t);
-    pl.ws_bytes = align256(acc) + align256(ml) + align256(cnt);
+    pl.ws_bytes = align256(acc) + align256(ml);
   }
   return pl;
 }
@@ -854,14 +793,13 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   P.meta_lds = a.B + 1 <= kMetaLdsMax ? 1 : 0;
   P.scale_log2 = a.scale * kLog2e;
   const bool direct = plan.n_splits == 1;
-  P.ws_acc = nullptr; P.ws_ml = nullptr; P.counters = nullptr;
+  P.ws_acc = nullptr; P.ws_ml = nullptr;
   if (!direct) {
     const size_t acc = align256((size_t)plan.n_splits * a.T * a.H_q * a.D * sizeof(float));
     const size_t ml = align256((size_t)plan.n_splits * a.T * a.H_q * sizeof(float2));
     char* ws = reinterpret_cast<char*>(a.workspace);
     P.ws_acc = reinterpret_cast<float*>(ws);
     P.ws_ml = reinterpret_cast<float2*>(ws + acc);
-    P.counters = reinterpret_cast<int32_t*>(ws + acc + ml);
   }
   switch (a.kind) {
     case SPATTN_KIND_PAGED: dispatch_q<SPATTN_KIND_PAGED>(a, P, direct, stream); break;
@@ -869,7 +807,7 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
     default: dispatch_q<SPATTN_KIND_LOCAL_AUX>(a, P, direct, stream); break;
   }
   if (hipGetLastError() != hipSuccess) return SPATTN_ERR_LAUNCH;
-  if (!direct && (a.dtype == SPATTN_F32 || !kFusedMerge)) {
+  if (!direct) {
     const int pairs = a.T * a.H_q;
     dim3 grid((pairs + 3) / 4);
 #define SPATTN_MERGE(QT, DD)                                                                 \

@@ -205,15 +205,14 @@ def test_full_causal_prefill_sampled_rows():
     _sampled(case, rows, "paged_prefill_f16 no window (full)")
 
 
-def test_workspace_reuse_and_counter_reset():
-    # one zeroed workspace across many calls: the arrival counters must come back to zero
-    # and every call must give the same bits
+def test_workspace_reuse():
+    # one uninitialised workspace across many calls: every call gives the same bits
     case = synth.config_gqa_paged_decode(B=12, max_len=6000, seed=21)
     t = case_tensors(case)
     need = sta.attention_workspace_bytes(sta.KIND_PAGED, sta.F16, case.B, case.T, case.max_seqlen_q,
                                          case.max_seqlen_k, 0, -1, case.H_q, case.H_kv, case.D)
     assert need > 0
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN-pattern garbage
     sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], t["seqlens_k"], t["k_cache"], t["v_cache"],
                         t["block_table"])
     outs = []
@@ -224,9 +223,6 @@ def test_workspace_reuse_and_counter_reset():
                                 scale=case.scale, sinks=t["sinks"], workspace=ws)
         outs.append(out)
     torch.cuda.synchronize()
-    n_cnt = case.T * case.H_kv * 1 * 4
-    tail = ws[need - ((n_cnt + 255) // 256) * 256:]
-    assert int(tail.count_nonzero().item()) == 0
     for o in outs[1:]:
         assert torch.equal(o.cpu().view(torch.int16), outs[0].cpu().view(torch.int16))
     ref, _, _ = oracle_paged_step(case)
