@@ -59,7 +59,8 @@ struct PfLds {
   static constexpr int kVld = D + 16;    // V tile row (elements)
   static constexpr int kKBytes = kPfTile * kKld * 2;
   static constexpr int kVBytes = kPfTile * kVld * 2;
-  static constexpr int kStage = kKBytes + kVBytes + kPfTile * 4;  // + key validity words
+  static constexpr int kStage = kKBytes + kVBytes + kPfTile * 4 + 16;  // + key validity words
+                                                                       // + 4 per-wave flags
   static constexpr int kTotal = 2 * kStage;
 };
 
@@ -145,7 +146,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
   const int w_lo = P.window > 0 ? max(0, w_p_first - P.window + 1) : 0;
   const bool wave_active = head_ok && wave_rows > 0;
 
-  // query operand (B of S^T = K Q^T): row my_row, dims 16*kc + 8*h .. +7
+  // query operand (B of S^T = K Q^T): row my_row, dims 16*kc + 8*h .. +7.  The running max
+  // is kept on raw scores q.k and the positive factor c = |scale| * log2(e) is applied inside
+  // the exponent, so a negative scale is folded into the query's sign.
+  const float c_scale = fabsf(P.scale_log2);
+  const bool q_neg = P.scale_log2 < 0.f;
   V8 qop[KC];
   {
     const QT* qr = reinterpret_cast<const QT*>(P.q) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
@@ -163,6 +168,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
       } else {
         qop[kc] = V8{};
       }
+      if (q_neg) qop[kc] = -qop[kc];
     }
   }
 
@@ -222,6 +228,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
       *reinterpret_cast<V8*>(vl + key * PfLds<D>::kVld + col) = vv;
       if (col == 0) vb[key] = kok[n] ? 1 : 0;
     }
+    // one flag per loading wave: every key it loaded exists
+    bool all_ok = true;
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) all_ok = all_ok && kok[n];
+    const bool wave_ok = __ballot(!all_ok) == 0;
+    if (lane == 0) vb[kPfTile + wave] = wave_ok ? 1 : 0;
   };
 
   if (n_tiles > 0) {
@@ -247,41 +259,49 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
         V8 a = *reinterpret_cast<const V8*>(kl + l32 * PfLds<D>::kKld + kc * 16 + h * 8);
         s = mfma32(a, qop[kc], s);
       }
-      // masks; lane holds keys 8*(i/4) + 4*h + i%4 of row l32
-      float mt = kNegInf;
+      // lane holds keys 8*(i/4) + 4*h + i%4 of row l32.  Masks only on tiles some row of the
+      // wave does not fully see (the diagonal, the window edge, missing keys).
+      const i32x4 wflags = *reinterpret_cast<const i32x4*>(vb + kPfTile);
+      const bool tile_ok = (wflags[0] & wflags[1] & wflags[2] & wflags[3]) != 0;
+      const bool full = tile_ok && kt + kPfTile - 1 <= w_p_first &&
+                        (P.window <= 0 || kt >= w_p_last - P.window + 1);
+      if (!full) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int k0 = 8 * g4 + 4 * h;
-        const i32x4 ok = *reinterpret_cast<const i32x4*>(vb + k0);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int k0 = 8 * g4 + 4 * h;
+          const i32x4 ok = *reinterpret_cast<const i32x4*>(vb + k0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = kt + k0 + e;
-          const bool vis = row_ok && ok[e] && j <= my_p && j >= my_lo;
-          const float v = vis ? s[4 * g4 + e] * P.scale_log2 : kNegInf;
-          s[4 * g4 + e] = v;
-          mt = fmaxf(mt, v);
+          for (int e = 0; e < 4; ++e) {
+            const int j = kt + k0 + e;
+            if (!(ok[e] && j <= my_p && j >= my_lo)) s[4 * g4 + e] = kNegInf;
+          }
         }
       }
-      mt = xor_max(mt, 32);
-      const float m_new = fmaxf(m_run, mt);
-      // Every lane runs the update and the MFMAs (they read operands of all 64 lanes);
-      // a row with no visible key so far keeps m = -inf, l = 0, acc = 0.
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      {
-        const float alpha = exp2_safe(m_run - m_use);
-        float psum = 0.f;
-        V8 pop[2];
+      float mt = s[0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2_safe(s[i] - m_use);
-          psum += p;
-          pop[i >> 3][i & 7] = (OpT)p;
-        }
-        psum = xor_sum(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
+      mt = xor_max(mt, 32);
+      const float m_new = fmaxf(m_run, mt);      // raw-score maximum of the row
+      if (__ballot(m_new > m_run)) {
+        // rows whose max did not move keep alpha = 1 (including rows that have seen no key
+        // yet: -inf - -inf must not reach the exponent); a row seeing its first key gets
+        // alpha = 0 on acc = 0, l = 0
+        const float alpha = m_new == m_run ? 1.f : exp2_safe((m_run - m_new) * c_scale);
+        l_run *= alpha;
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m] *= alpha;
+      }
+      m_run = m_new;
+      // p = exp2(c * (s - m)); a row with no visible key yet keeps p = 0
+      const float nm = m_new == kNegInf ? 0.f : -m_new * c_scale;
+      V8 pop[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_safe(__builtin_fmaf(s[i], c_scale, nm));
+        l_run += p;                                 // this lane's part of the row sum
+        pop[i >> 3][i & 7] = (OpT)p;
+      }
+      {
         const int grp = lane >> 4, lam = lane & 15;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -306,13 +326,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
   }
 
   // ---- finalise: sink, normalise, store (lane: row l32, dims 32m + 8(i/4) + 4h + i%4) ----
+  l_run = xor_sum(l_run, 32);                        // both lane halves of the row
   if (row_ok) {
     QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
     float f = 0.f, inv = 0.f;
     if (m_run != kNegInf) {
+      const float ms = m_run * c_scale;                // log2-domain maximum
       const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
-      const float M2 = fmaxf(m_run, sg);
-      f = exp2_safe(m_run - M2);
+      const float M2 = fmaxf(ms, sg);
+      f = exp2_safe(ms - M2);
       inv = f / (l_run * f + exp2_safe(sg - M2));
     }
 #pragma unroll
