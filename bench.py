@@ -17,6 +17,7 @@ and of the same without a window are reported alongside, as the metric names bot
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -29,6 +30,23 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2516.6    # MI355X dense fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged attn"
+
+# HBM bytes per paged_attention_fwd call on the decode workload, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE counter passes scaled by the same counters' reading on a plain device copy of
+# known size (profiles/decode_gqa_paged_f16_traffic.md).  Valid only for the kernel sources
+# whose digest is recorded with it; any other source reports traffic = null.
+MEASURED_TRAFFIC = {"sources_sha1": "9de2f4b7d4f709476f4f363881028b6c92bcd7f3",
+                    "bytes_per_call": 290362594}
+KERNEL_SOURCES = ("selected_token_sparse_amd/csrc/decode.hip", "selected_token_sparse_amd/csrc/common.h",
+                  "selected_token_sparse_amd/csrc/launch.h")
+
+
+def kernel_sources_sha1():
+    h = hashlib.sha1()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _kv_bytes(case):
@@ -59,6 +77,13 @@ def _prefill_flops(case):
             lo = max(0, p - case.local_window + 1) if case.local_window > 0 else 0
             pairs += max(0, p - lo + 1)
     return pairs * case.H_q * 4 * case.D
+
+
+def _queue_ahead():
+    """A short device spin before a timed loop, so that the host has queued the loop's
+    launches before the GPU reaches them and the events time the GPU, not the launches."""
+    import torch
+    torch.cuda._sleep(4_000_000)
 
 
 def _events():
@@ -107,6 +132,7 @@ def bench_decode(steps, warmup, copies=3):
     evs = [_events() for _ in range(steps)]
     t0, t1 = _events()
     torch.cuda.synchronize()
+    _queue_ahead()
     t0.record()
     for i in range(steps):
         step(i, evs[i])
@@ -142,6 +168,7 @@ def bench_prefill(window, steps, warmup):
         call()
     torch.cuda.synchronize()
     evs = [_events() for _ in range(steps)]
+    _queue_ahead()
     for a, b in evs:
         a.record()
         call()
@@ -158,6 +185,93 @@ def bench_prefill(window, steps, warmup):
         "algorithmic_gflop": round(flops / 1e9, 3),
         "qo_gbs": round(qo_bytes / (med * 1e-3) / 1e9, 1),
     }
+
+
+def _sparse_bytes(case):
+    """Algorithmic bytes of a sparse call: K+V of every key a row sees, once per (row, KV
+    head) (visible selected main positions j <= p, window positions, in-range auxiliary
+    rows), plus Q and out."""
+    import numpy as np
+    cu = case.cu_seqlens_q
+    T, H_kv, D = case.T, case.H_kv, case.D
+    main_es = 1 if case.cache_dtype == 3 else 2
+    req = np.searchsorted(cu, np.arange(T), side="right") - 1
+    kv = case.seqlens_k[req].astype(np.int64) + 1
+    p = kv - (cu[req + 1] - cu[req]) + (np.arange(T) - cu[req])           # [T]
+    sel = case.sel_idx.astype(np.int64)                                   # [T, H_kv, S]
+    t = np.arange(sel.shape[2])[None, None, :]
+    cnt = np.clip(case.sel_count.astype(np.int64), 0, case.max_selected)[:, :, None]
+    inside = t < cnt
+    if case.mode == 0:
+        vis = inside & (sel >= 0) & (sel <= p[:, None, None]) & (sel < kv[:, None, None])
+        main_keys = int(vis.sum())
+        aux_keys = 0
+    else:
+        W = case.local_window
+        main_keys = int(np.minimum(p + 1, W).sum()) * H_kv
+        aux_keys = int((inside & (sel >= 0) & (sel < case.aux_len)).sum())
+    qo = 2 * T * case.H_q * D * 2
+    return main_keys * 2 * D * main_es + aux_keys * 2 * D * 2 + qo, main_keys, aux_keys
+
+
+def bench_sparse(which, steps, warmup):
+    """Selected-token grouped decode (mode 0) or local-plus-aux INT8 (mode 1)."""
+    import torch
+
+    import selected_token_sparse_amd as sta
+    import synth
+    from synth.device import case_tensors
+
+    case = synth.config_selected_decode() if which == "selected" else synth.config_local_plus_aux_int8()
+    t = case_tensors(case)
+    out = torch.empty((case.T, case.H_q, case.D), dtype=torch.float16, device="cuda")
+    kind = sta.KIND_SELECTED if case.mode == 0 else sta.KIND_LOCAL_AUX
+    need = sta.attention_workspace_bytes(kind, sta.F16, case.B, case.T, case.max_seqlen_q, 0,
+                                         case.max_selected, case.local_window, case.H_q,
+                                         case.H_kv, case.D)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call():
+        sta.sparse_attention_fwd(t["q"], case.mode, t["k_cache"], t["v_cache"], t["cu"],
+                                 t["seqlens_k"], case.max_seqlen_q, t["sel_idx"], out,
+                                 sel_count=t["sel_count"], key_scale=t["key_scale"],
+                                 value_scale=t["value_scale"], local_window=case.local_window,
+                                 aux_k=t["aux_k"], aux_v=t["aux_v"],
+                                 aux_batch_stride=case.aux_batch_stride if case.mode == 1 else None,
+                                 scale=case.scale, sinks=t["sinks"], workspace=ws, status=status)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [_events() for _ in range(steps)]
+    for a, b in evs:
+        flush.zero_()          # outside the events: the Infinity Cache holds none of the rows
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ms[len(ms) // 2]
+    alg, main_keys, aux_keys = _sparse_bytes(case)
+    gbs = alg / (med * 1e-3) / 1e9
+    return {"workload": case.name, "median_us": round(med * 1e3, 2),
+            "avg_us": round(sum(ms) / len(ms) * 1e3, 2), "algorithmic_bytes": alg,
+            "main_keys": main_keys, "aux_keys": aux_keys, "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "status": int(status.item())}
+
+
+def copy_calibration(mib, reps=4):
+    """A plain device-to-device copy of `mib` MiB, for scaling the HBM byte counters: the
+    copy reads and writes exactly mib * 2^20 bytes each."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy calibration: {reps} copies of {mib << 20} bytes", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(target_s=12.0):
@@ -202,6 +316,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-sparse", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
@@ -211,6 +328,8 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
     case, ms_step, attn_ms, st = bench_decode(args.steps, args.warmup)
     kv = _kv_bytes(case)
     gbs = kv / (ms_step * 1e-3) / 1e9
@@ -221,6 +340,9 @@ def main():
     bt_bytes = sum((int(s) + 1 + 15) // 16 for s in case.seqlens_k if s >= 0) * 4
     alg = kv + 2 * q_bytes + bt_bytes
     achieved = alg / (attn_avg * 1e-3) / 1e9
+    digest = kernel_sources_sha1()
+    traffic = (MEASURED_TRAFFIC["bytes_per_call"]
+               if MEASURED_TRAFFIC["sources_sha1"] == digest else None)
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -231,14 +353,18 @@ def main():
                    "kv_bytes_per_step": kv, "global_batch": case.B, "rows": case.T,
                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "status": st},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attention_fwd (split-K decode + merge)",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "paged_attention_fwd decode call: split-K kernel + merge kernel",
+                     "kernel_sources_sha1": digest,
                      "avg_us": round(attn_avg * 1e3, 2), "median_us": round(attn_med * 1e3, 2),
                      "algorithmic_bytes": alg},
     }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(128, 50, 5)
         line["prefill_no_window"] = bench_prefill(-1, 30, 3)
+    if not args.no_sparse:
+        line["selected_decode"] = bench_sparse("selected", 50, 5)
+        line["local_plus_aux"] = bench_sparse("local_aux", 50, 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -1,0 +1,103 @@
+"""The calls need no host synchronisation: the metadata pass, the cache append and both
+attention entry points are recorded into one HIP graph and replayed.  ("[WebGPU] Add
+PagedAttention metadata and GPT-OSS support", Description: sequence lengths are produced
+on the device so the step needs no readback and can be replayed.)
+
+Each replay runs after unrelated eager work and a synchronisation, with the outputs
+overwritten by NaN first; every replay must reproduce the eager outputs bit for bit (the
+kernels are deterministic: no atomics decide any value), and the eager outputs are
+checked against the oracle too."""
+import numpy as np
+import pytest
+import torch
+
+import selected_token_sparse_amd as sta
+import synth
+from synth.device import TORCH_DTYPE, case_tensors
+
+from harness import assert_close, oracle_paged_step, oracle_sparse, status_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _ws(kind, case, max_sel=0):
+    n = sta.attention_workspace_bytes(kind, case.dtype, case.B, case.T, case.max_seqlen_q,
+                                      getattr(case, "max_seqlen_k", 0), max_sel,
+                                      case.local_window, case.H_q, case.H_kv, case.D)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+
+def test_decode_prefill_sparse_step_in_one_graph():
+    dec = synth.config_gqa_paged_decode(poison=True, B=8, max_len=3000, seed=91)
+    pre = synth.paged_case(92, kv_lens=[130, 40], q_lens=[130, 40], H_q=16, H_kv=2, D=64,
+                           dtype=synth.F16, sinks=True, local_window=64, poison=True)
+    sel = synth.sparse_selected_case(93, B=3, S_q=2, H_q=24, H_kv=2, D=128, capacity=900,
+                                     max_selected=256, dtype=synth.F16, sinks=True, oor_frac=0.02,
+                                     poison=True)
+    td, tp, ts = case_tensors(dec), case_tensors(pre), case_tensors(sel)
+    sq = torch.empty(dec.B, dtype=torch.int32, device="cuda")
+    sk = torch.empty(dec.B, dtype=torch.int32, device="cuda")
+    st = status_tensor()
+    ws_d = _ws(sta.KIND_PAGED, dec)
+    ws_s = _ws(sta.KIND_SELECTED, sel, sel.max_selected)
+    out_d = torch.empty((dec.T, dec.H_q, dec.D), dtype=TORCH_DTYPE[dec.dtype], device="cuda")
+    out_p = torch.empty((pre.T, pre.H_q, pre.D), dtype=TORCH_DTYPE[pre.dtype], device="cuda")
+    out_s = torch.empty((sel.T, sel.H_q, sel.D), dtype=TORCH_DTYPE[sel.dtype], device="cuda")
+
+    # the prefill's prompt rows enter the cache once, before capture
+    sta.kv_cache_append(tp["k_new"], tp["v_new"], tp["cu"], tp["seqlens_k"], tp["k_cache"],
+                        tp["v_cache"], tp["block_table"])
+
+    def step():
+        sta.prepare_seqlens(td["cu"], td["past"], dec.T, sq, sk, status=st)
+        sta.kv_cache_append(td["k_new"], td["v_new"], td["cu"], sk, td["k_cache"], td["v_cache"],
+                            td["block_table"], status=st)
+        sta.paged_attention_fwd(td["q"], td["k_cache"], td["v_cache"], td["cu"], sk,
+                                dec.max_seqlen_q, dec.max_seqlen_k, out_d,
+                                block_table=td["block_table"], scale=dec.scale,
+                                sinks=td["sinks"], workspace=ws_d, status=st)
+        sta.paged_attention_fwd(tp["q"], tp["k_cache"], tp["v_cache"], tp["cu"], tp["seqlens_k"],
+                                pre.max_seqlen_q, pre.max_seqlen_k, out_p,
+                                block_table=tp["block_table"], scale=pre.scale,
+                                local_window=pre.local_window, sinks=tp["sinks"], status=st)
+        sta.sparse_attention_fwd(ts["q"], sel.mode, ts["k_cache"], ts["v_cache"], ts["cu"],
+                                 ts["seqlens_k"], sel.max_seqlen_q, ts["sel_idx"], out_s,
+                                 sel_count=ts["sel_count"], scale=sel.scale, sinks=ts["sinks"],
+                                 workspace=ws_s, status=st)
+
+    print("graph: eager step", flush=True)
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in (out_d, out_p, out_s)]
+    st_eager = int(st.item())
+    ref_d, dst, _ = oracle_paged_step(dec)
+    assert_close(eager[0], ref_d, dec.dtype, "graph eager decode")
+    ref_p, pst, _ = oracle_paged_step(pre)       # the oracle appends the prompt rows itself
+    assert_close(eager[1], ref_p, pre.dtype, "graph eager prefill")
+    ref_s, sst, _ = oracle_sparse(sel)
+    assert_close(eager[2], ref_s, sel.dtype, "graph eager selected")
+    assert st_eager == dst | pst | sst, (st_eager, dst, pst, sst)
+
+    print("graph: capture", flush=True)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    noise = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        print(f"graph: replay {rep}", flush=True)
+        for o in (out_d, out_p, out_s):
+            o.fill_(float("nan"))
+        (noise * 3.0).sum().item()  # unrelated eager work and a synchronisation
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((out_d, out_p, out_s), eager, ("decode", "prefill", "selected")):
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (rep, name)
+    assert int(st.item()) == st_eager
