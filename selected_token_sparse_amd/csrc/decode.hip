@@ -42,7 +42,11 @@ constexpr int kWgStep = kWaves * kTile;
 constexpr int kMaxChunk = 2048;    // keys per split while there are enough workgroups
 constexpr int kChunkCap = 4096;    // keys per split, hard limit (LDS row-index buffer)
 constexpr int kMaxSplits = 256;    // splits per item (LDS merge coefficients)
-constexpr int kTargetWorkgroups = 4096;
+// Workgroups the split plan aims for: paged ranges stream 2 KB runs and gain from more,
+// shorter splits; selected rows are random 256-byte gathers where fewer, longer splits
+// (fewer partial states) measured faster.
+constexpr int kTargetWorkgroupsPaged = 4096;
+constexpr int kTargetWorkgroupsSparse = 2048;
 constexpr int kMetaLdsMax = 512;   // cu entries staged in LDS (more: binary search in memory)
 
 enum Src { SRC_RANGE = 0, SRC_SELECT = 1, SRC_AUX = 2 };
@@ -102,24 +106,22 @@ struct SplitParams {
   float scale_log2;         // scale * log2(e)
 };
 
-__device__ __forceinline__ void flush_flags(int flags, int32_t* status) {
-  // OR the per-lane flags across the wave, then one atomic per wave and only when the
-  // bits are not set yet.
+// OR of the per-lane status flags across the wave (uniform result).
+__device__ __forceinline__ int wave_or_flags(int flags) {
   int wave_flags = 0;
 #pragma unroll
   for (int bit = 0; bit < 8; ++bit)
     if (__ballot(flags & (1 << bit))) wave_flags |= 1 << bit;
-  if (wave_flags && (threadIdx.x & 63) == 0 && status != nullptr) {
-    int cur = __atomic_load_n(status, __ATOMIC_RELAXED);
-    if ((cur & wave_flags) != wave_flags) atomicOr(status, wave_flags);
-  }
+  return wave_flags;
 }
+// Flags reach the status word through raise_status: one atomic OR whose result is unused,
+// so nothing waits for it (a read-then-OR would put a contended load on the critical path).
 
 // LDS layout (bytes): per-wave V tiles (reused as the combine / merge area after the key
 // loop), then the split's cache-row indices, then the staged metadata.
 template <int D>
 struct SplitLds {
-  static constexpr bool kDeep = false;  // two tiles in flight per wave: measured no faster
+  static constexpr bool kDeep = D == 64;  // two tiles in flight per wave at D = 64
   static constexpr int kVTileBytes = (kDeep ? 2 : 1) * kTile * D * 2;  // a wave's V tiles
   static constexpr int kCombineBytes = kWaves * 16 * (D + 2) * 4;
   static constexpr int kAreaBytes = (kWaves * kVTileBytes > kCombineBytes) ? kWaves * kVTileBytes : kCombineBytes;
@@ -378,10 +380,10 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
   return -1;
 }
 
-// Occupancy hint for D = 64: 7 waves per SIMD fit in 72 registers without spilling (more
-// waves, more tiles in flight per CU for the memory-bound key loop).
+// Occupancy hint for D = 64: with two tiles in flight per wave, 5 waves per SIMD (the
+// register budget of that occupancy holds both tiles' K operands without spilling).
 template <int KIND, typename QT, typename KT, typename AT, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 7 : 1, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 1, 8)))
 void split_attn_kernel(SplitParams P) {
   typedef typename std::conditional<sizeof(KT) == 1, f16, KT>::type OpM;  // main operand
   typedef QT OpA;                                                          // aux operand
@@ -407,6 +409,15 @@ void split_attn_kernel(SplitParams P) {
   const int h0 = c * P.group + ht * 16;                 // first query head of the tile
   const int nh = min(16, P.group - ht * 16);            // heads in the tile
 
+  // the query rows depend on the grid position only: their loads overlap the prologue
+  const bool hv = lam < nh;
+  const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0 + (hv ? lam : 0)) * D;
+  const QT* q0row = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0) * D;
+  i32x4 qraw[D / 32];
+#pragma unroll
+  for (int kc = 0; kc < D / 32; ++kc)
+    qraw[kc] = hv ? load16(qrow + kc * 32 + grp * 8) : i32x4{0, 0, 0, 0};
+
   // ---- 1. the row's request and position ----
   const int32_t* cu = P.cu;
   const int32_t* skl = P.seqlens_k;
@@ -424,9 +435,22 @@ void split_attn_kernel(SplitParams P) {
 
   // ---- 2. the split's keys -> cache-row indices ----
   const SplitRange sr = split_range<KIND>(P, ri, r, c, split, flags);
+  if (sr.n_keys == 0 && P.n_splits > 1) {
+    // nothing in this split: (m, l) = (-inf, 0) tells the merge to skip it; no accumulator
+    // (the flags raised so far are the same in every wave)
+    if (tid == 0) raise_status(P.status, flags);
+    if (tid < nh)
+      P.ws_ml[(int64_t)split * P.T * P.H_q + (int64_t)r * P.H_q + h0 + tid] = make_float2(kNegInf, 0.f);
+    return;
+  }
   for (int v = tid; v < sr.n_keys; v += kThreads) rows[v] = split_key_row(P, sr, ri, c, v, flags);
-  flush_flags(flags, P.status);
+  __shared__ int wave_flags[kWaves];
+  {
+    const int wf = wave_or_flags(flags);
+    if (lane == 0) wave_flags[wave] = wf;
+  }
   __syncthreads();
+  if (tid == 0) raise_status(P.status, wave_flags[0] | wave_flags[1] | wave_flags[2] | wave_flags[3]);
 
   // ---- 3. per-wave key loop ----
   float m_run = kNegInf, l_run = 0.f;
@@ -435,22 +459,18 @@ void split_attn_kernel(SplitParams P) {
   for (int m = 0; m < D / 16; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool use_scale = sizeof(KT) == 1 && sr.src != SRC_AUX;
   if (sr.n_keys > 0) {
-    const int head = h0 + lam;
-    const bool hv = lam < nh;
-    const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + head) * D;
-    const QT* q0row = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0) * D;
     if (KIND != SPATTN_KIND_LOCAL_AUX || sr.src != SRC_AUX) {
       typename OpVec<OpM>::v8 qop[D / 32];
 #pragma unroll
       for (int kc = 0; kc < D / 32; ++kc) {
         const int col = kc * 32 + grp * 8;
         if constexpr (sizeof(KT) == 1) {
+          const typename OpVec<QT>::v8 qv = __builtin_bit_cast(typename OpVec<QT>::v8, qraw[kc]);
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            qop[kc][e] = (OpM)(hv ? to_f32(qrow[col + e]) * P.key_scale[c * D + col + e] : 0.f);
+            qop[kc][e] = (OpM)(hv ? to_f32((QT)qv[e]) * P.key_scale[c * D + col + e] : 0.f);
         } else {
-          qop[kc] = hv ? __builtin_bit_cast(typename OpVec<OpM>::v8, load16(qrow + col))
-                       : typename OpVec<OpM>::v8{};
+          qop[kc] = __builtin_bit_cast(typename OpVec<OpM>::v8, qraw[kc]);
         }
       }
       // masked keys read row 0 of the cache for K and, with 16-bit caches, the query row of
@@ -465,9 +485,7 @@ void split_attn_kernel(SplitParams P) {
     } else if constexpr (sizeof(AT) == 2) {
       typename OpVec<OpA>::v8 qop[D / 32];
 #pragma unroll
-      for (int kc = 0; kc < D / 32; ++kc)
-        qop[kc] = hv ? __builtin_bit_cast(typename OpVec<OpA>::v8, load16(qrow + kc * 32 + grp * 8))
-                     : typename OpVec<OpA>::v8{};
+      for (int kc = 0; kc < D / 32; ++kc) qop[kc] = __builtin_bit_cast(typename OpVec<OpA>::v8, qraw[kc]);
       wave_keys<OpA, AT, D>(reinterpret_cast<const AT*>(P.aux_k),
                             reinterpret_cast<const AT*>(P.aux_v),
                             reinterpret_cast<const AT*>(q0row), reinterpret_cast<const AT*>(q0row),
@@ -535,15 +553,27 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
                                                     const float* __restrict__ sinks,
                                                     void* __restrict__ out, int T, int H_q,
                                                     int n_splits) {
+  // Splits without a visible key wrote m = -inf and no accumulator: only live splits are
+  // read.  Their (m, l) pairs come in one parallel round (lane s holds split s + 64 g); the
+  // accumulators of live splits are then loaded eight at a time with every load in flight
+  // before the first is used.
+  constexpr int kGroups = kMaxSplits / 64;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (pair >= T * H_q) return;
   const int head = pair % H_q;
   const int64_t stride = (int64_t)T * H_q;
-  // lanes read the split states in parallel, then reduce across the wave
+  float2 ml[kGroups];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int sp = lane + 64 * g;
+    ml[g] = sp < n_splits ? ws_ml[sp * stride + pair] : make_float2(kNegInf, 0.f);
+  }
   float M = kNegInf;
-  for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, ws_ml[s * stride + pair].x);
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) M = fmaxf(M, ml[g].x);
+  M = xor_max(M, 32); M = xor_max(M, 16); M = xor_max(M, 8);
+  M = xor_max(M, 4); M = xor_max(M, 2); M = xor_max(M, 1);
   constexpr int PER = D / 64;
   float res[PER];
 #pragma unroll
@@ -551,23 +581,45 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
   if (M != kNegInf) {
     const float sg = sinks != nullptr ? sinks[head] * kLog2e : kNegInf;
     const float M2 = fmaxf(M, sg);
+    float f[kGroups];
     float Lp = 0.f;
-    for (int s = lane; s < n_splits; s += 64) {
-      const float2 ml = ws_ml[s * stride + pair];
-      if (ml.x != kNegInf) Lp += ml.y * exp2_safe(ml.x - M2);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      f[g] = ml[g].x != kNegInf ? exp2_safe(ml[g].x - M2) : 0.f;
+      Lp += ml[g].y * f[g];
     }
-    for (int o = 32; o >= 1; o >>= 1) Lp += __shfl_xor(Lp, o, 64);
+    Lp = xor_sum(Lp, 32); Lp = xor_sum(Lp, 16); Lp = xor_sum(Lp, 8);
+    Lp = xor_sum(Lp, 4); Lp = xor_sum(Lp, 2); Lp = xor_sum(Lp, 1);
     const float L = Lp + exp2_safe(sg - M2);
     float A[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) A[k] = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float2 ml = ws_ml[s * stride + pair];
-      if (ml.x == kNegInf) continue;   // empty split
-      const float f = exp2_safe(ml.x - M2);
-      const float* a = ws_acc + (s * stride + pair) * D;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) A[k] += a[lane + 64 * k] * f;
+    for (int g = 0; g < kGroups; ++g) {
+      if (64 * g >= n_splits) break;
+      uint64_t live = __ballot(ml[g].x != kNegInf);
+      while (live) {
+        // the next (up to) eight live splits; missing ones repeat the first with weight 0
+        int idx[8];
+        float cf[8];
+        const int first = __builtin_ctzll(live);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int bit = live ? __builtin_ctzll(live) : first;
+          cf[k] = live ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f[g]), bit)) : 0.f;
+          idx[k] = 64 * g + bit;
+          live &= live - 1;
+        }
+        float a[8][PER];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int e = 0; e < PER; ++e) a[k][e] = ws_acc[(idx[k] * stride + pair) * D + lane + 64 * e];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int e = 0; e < PER; ++e) A[e] += a[k][e] * cf[k];
+      }
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) res[k] = A[k] / L;
@@ -648,7 +700,10 @@ __global__ __launch_bounds__(64) void split_attn_f32_kernel(SplitParams P) {
     }
     __syncthreads();
   }
-  flush_flags(flags, P.status);
+  {
+    const int wf = wave_or_flags(flags);
+    if (lane == 0) raise_status(P.status, wf);
+  }
   const int64_t o = ((int64_t)r * P.H_q + head) * D;
   if constexpr (DIRECT) {
     float* out = reinterpret_cast<float*>(P.out) + o;
@@ -708,7 +763,8 @@ SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_
     long s = (n_main + ch - 1) / ch + (n_aux + ch - 1) / ch;
     return std::max(1L, s);
   };
-  while (chunk < kMaxChunk && chunk < total && items * splits_for(chunk) > kTargetWorkgroups) chunk *= 2;
+  const long target = kind == SPATTN_KIND_PAGED ? kTargetWorkgroupsPaged : kTargetWorkgroupsSparse;
+  while (chunk < kMaxChunk && chunk < total && items * splits_for(chunk) > target) chunk *= 2;
   while (splits_for(chunk) > kMaxSplits && chunk < kChunkCap) chunk *= 2;
   if (splits_for(chunk) > kMaxSplits) {  // key range too long for one call
     pl.n_splits = -1;
