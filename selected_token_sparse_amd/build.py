@@ -24,6 +24,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax rescales and reads them every tile,
+    # and AGPR placement would add a move per element each time (and cost occupancy)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
 ]
 

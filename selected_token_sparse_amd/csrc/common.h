@@ -24,6 +24,11 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// Lazy rescaling of the online softmax: a row's reference maximum (log2 domain) moves only
+// when a new score exceeds it by more than this, so exp2 arguments stay <= 8 and the
+// unnormalised weights <= 256 (exact relative precision in f16 / bf16, no overflow in the
+// float32 sums).  Any reference <= the true maximum gives the same softmax once normalised.
+constexpr float kLazyRescaleLog2 = 8.0f;
 
 // ---------------------------------------------------------------------------------------
 // element conversions

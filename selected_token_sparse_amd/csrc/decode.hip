@@ -224,15 +224,18 @@ __device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t v
   mt = xor_max(mt, 16);
   mt = xor_max(mt, 32);
   const float m_new = fmaxf(m_run, mt);
-  // a head with no visible key so far keeps m = -inf, l = 0, acc = 0
-  const float m_use = m_new == kNegInf ? 0.f : m_new;
-  if (__ballot(m_new > m_run)) {
-    const float alpha = exp2_safe(m_run - m_use);
+  // the reference maximum m_run moves only when some head's maximum outgrows it by more
+  // than kLazyRescaleLog2 (a head's first visible key always moves it: x - -inf = inf);
+  // -inf - -inf is NaN and compares false, so a head with no visible key keeps m = -inf
+  if (__ballot(m_new - m_run > kLazyRescaleLog2)) {
+    const float alpha = m_new == m_run ? 1.f : exp2_safe(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] *= alpha;
+    m_run = m_new;
   }
-  m_run = m_new;
+  // a head with no visible key so far keeps l = 0, acc = 0 (its scores are all -inf)
+  const float m_use = m_run == kNegInf ? 0.f : m_run;
   float psum = 0.f;
   V8 pop;
 #pragma unroll

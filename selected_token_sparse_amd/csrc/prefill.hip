@@ -282,7 +282,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
       mt = xor_max(mt, 32);
       const float m_new = fmaxf(m_run, mt);      // raw-score maximum of the row
-      if (__ballot(m_new > m_run)) {
+      // the reference maximum moves only when some row's maximum outgrows it by more than
+      // kLazyRescaleLog2 (in the exponent); a row's first visible key always moves it
+      if (__ballot((m_new - m_run) * c_scale > kLazyRescaleLog2)) {
         // rows whose max did not move keep alpha = 1 (including rows that have seen no key
         // yet: -inf - -inf must not reach the exponent); a row seeing its first key gets
         // alpha = 0 on acc = 0, l = 0
@@ -290,10 +292,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
         l_run *= alpha;
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m] *= alpha;
+        m_run = m_new;
       }
-      m_run = m_new;
-      // p = exp2(c * (s - m)); a row with no visible key yet keeps p = 0
-      const float nm = m_new == kNegInf ? 0.f : -m_new * c_scale;
+      // p = exp2(c * (s - m)) <= 2^8; a row with no visible key yet keeps p = 0
+      const float nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
       V8 pop[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
