@@ -60,6 +60,17 @@ __device__ __forceinline__ float xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }
 
+// Combine lane l with lane l ^ 32 through v_permlane32_swap (a VALU swap of the two
+// 32-lane halves, no LDS round trip): the two results hold v[l] and v[l ^ 32] in some order.
+__device__ __forceinline__ float half_swap_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // exp2 that maps -inf to 0 and never produces NaN from (-inf) - (-inf): callers pass
 // differences whose minuend is finite or -inf.
 __device__ __forceinline__ float exp2_safe(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -50,6 +50,7 @@ struct PrefillParams {
   int n_rt;        // row tiles per request (host bound)
   int n_hg;        // head groups per KV head
   int total;       // workgroups
+  int xcd_pairs;   // 1: (request, KV head) pairs split evenly over the 8 XCDs
   float scale_log2;
 };
 
@@ -61,11 +62,16 @@ struct PfLds {
   static constexpr int kVBytes = kPfTile * kVld * 2;
   static constexpr int kStage = kKBytes + kVBytes + kPfTile * 4 + 16;  // + key validity words
                                                                        // + 4 per-wave flags
-  static constexpr int kTotal = 2 * kStage;
+  static constexpr int kBtCap = 512;     // window of block ids staged in LDS
+  static constexpr int kBtOffset = 2 * kStage;
+  static constexpr int kTotal = kBtOffset + kBtCap * 4;
 };
 
+// 4 waves per SIMD at D = 64 (128 registers: both tile buffers, the accumulators and the
+// query operand fit), 2 at D = 128.
 template <typename QT, typename KT, int D, int RW>
-__global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, 8)))
+void prefill_kernel(PrefillParams P) {
   constexpr int HW = 4 / RW;
   constexpr int KC = D / 16;          // QK k-steps
   constexpr int MT = D / 32;          // PV m-tiles
@@ -85,21 +91,32 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
   const int h = lane >> 5;            // lane half
   const int l32 = lane & 31;
 
-  // XCD-aware order: consecutive logical workgroups land on the same XCD
-  int logical;
+  // Work order: heaviest row tiles (the last ones of a request, which see the most keys)
+  // first.  Workgroup i runs on XCD i % 8; when the (request, KV head) pairs split evenly
+  // over the 8 XCDs, pair p is kept on XCD p % 8, so every XCD gets the same mix of row
+  // tiles and the K/V of a pair is read through one L2.
+  int rt, b, c, hg;
   {
     const int i = blockIdx.x;
-    const int n = P.total;
-    const int x = i & 7, k = i >> 3;
-    const int q = n >> 3, rem = n & 7;
-    logical = x * q + min(x, rem) + k;
+    const int pairs = P.B * P.H_kv;
+    int pair, rt_idx;
+    if (P.xcd_pairs) {
+      const int x = i & 7, k = i >> 3;
+      const int per_rt = (pairs >> 3) * P.n_hg;       // items of one row-tile index per XCD
+      rt_idx = k / per_rt;
+      const int rem = k - rt_idx * per_rt;
+      hg = rem % P.n_hg;
+      pair = (rem / P.n_hg) * 8 + x;
+    } else {
+      hg = i % P.n_hg;
+      const int t = i / P.n_hg;
+      pair = t % pairs;
+      rt_idx = t / pairs;
+    }
+    c = pair % P.H_kv;
+    b = pair / P.H_kv;
+    rt = P.n_rt - 1 - rt_idx;
   }
-  const int hg = logical % P.n_hg;
-  int t = logical / P.n_hg;
-  const int c = t % P.H_kv;
-  t /= P.H_kv;
-  const int b = t % P.B;
-  const int rt = P.n_rt - 1 - t / P.B;   // heaviest (last) row tiles first
 
   int flags = 0;
   const int c0 = P.cu[b];
@@ -183,29 +200,89 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
   const KT* kcache = reinterpret_cast<const KT*>(P.k_cache);
   const KT* vcache = reinterpret_cast<const KT*>(P.v_cache);
 
-  // ---- tile loader: global -> registers -> LDS stage ----
+  // ---- block ids of the key range, staged in LDS (paged caches) ----
+  // The window holds the ids of logical blocks win_lb .. win_lb + kBtCap - 1; a workgroup
+  // whose key range needs more refills it between barriers (block size 16: every 8192 keys).
+  int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + PfLds<D>::kBtOffset);
+  const bool paged = P.cd.block_table != nullptr;
+  const int bs = P.cd.block_size;
+  const bool pow2 = P.cd.bs_shift >= 0;
+  auto lblock = [&](int j) { return pow2 ? j >> P.cd.bs_shift : j / bs; };
+  const int lb_last = n_tiles > 0 ? lblock(j_hi) : 0;
+  int win_lb = n_tiles > 0 ? lblock(j_lo) : 0;
+  auto fill_window = [&]() {
+    const int32_t* row = P.cd.block_table + (int64_t)b * P.cd.max_blocks;
+    for (int i = tid; i < PfLds<D>::kBtCap; i += kPfThreads) {
+      const int lb = win_lb + i;
+      // never read past the table width or the blocks of the key range
+      bt_lds[i] = lb < P.cd.max_blocks && lb <= lb_last ? row[lb] : 0;
+    }
+  };
+  if (paged && n_tiles > 0) {
+    fill_window();
+    __syncthreads();
+  }
+  // before loading tile `it`: move the window when the tile's last key lies beyond it
+  auto ensure_window = [&](int it) {
+    if (!paged) return;
+    const int kt = kt_begin + it * kPfTile;
+    if (lblock(min(kt + kPfTile - 1, j_hi)) < win_lb + PfLds<D>::kBtCap) return;
+    __syncthreads();                       // every thread is done with the old window
+    win_lb = lblock(max(kt, j_lo));
+    fill_window();
+    __syncthreads();
+  };
+
+  // ---- tile loader: global -> registers -> LDS stage; two tiles in registers at a time ----
+  // A thread always loads the same 16-byte piece (key lkey, columns lcol..+7) of each tile,
+  // so the address is   block * blk_stride + slot * D + head_col   (paged) or
+  //                     req_base + j * D                         (contiguous).
   typedef typename std::conditional<kI8, int2, i32x4>::type Raw;
-  Raw kraw[NCH], vraw[NCH];
-  bool kok[NCH];
-  auto load_tile = [&](int kt) {
+  struct TileRegs { Raw k[NCH], v[NCH]; bool ok[NCH]; };
+  // a finite row of D elements for the loads of missing keys: the workgroup's first query
+  // row for 16-bit caches (same element size), the cache's first row for INT8 caches
+  const KT* safe_k = kI8 ? kcache : reinterpret_cast<const KT*>(
+      reinterpret_cast<const QT*>(P.q) + ((int64_t)(c0 + row_base) * P.H_q + c * P.group) * D);
+  const KT* safe_v = kI8 ? vcache : safe_k;
+  const int64_t blk_stride = (int64_t)P.cd.H_kv * bs * D;
+  const int64_t head_off = (int64_t)c * bs * D;
+  const int64_t req_base = ((int64_t)b * P.cd.H_kv + c) * bs * D;   // contiguous caches
+  auto load_tile = [&](TileRegs& tr, int kt) {
 #pragma unroll
     for (int n = 0; n < NCH; ++n) {
       const int qi = tid + n * kPfThreads;
       const int key = qi / CH, col = (qi % CH) * 8;
       const int j = kt + key;
-      int64_t off = -1;
-      if (j >= j_lo && j <= j_hi) off = cache_row(P.cd, b, j, c, flags);
-      kok[n] = off >= 0;
-      if (off >= 0) {
-        kraw[n] = *reinterpret_cast<const Raw*>(kcache + off + col);
-        vraw[n] = *reinterpret_cast<const Raw*>(vcache + off + col);
+      bool ok = j >= j_lo && j <= j_hi;
+      int64_t off;
+      if (paged) {
+        const int lb = lblock(j);
+        const int o = j - lb * bs;
+        const bool in_tab = lb < P.cd.max_blocks;
+        // in-range keys index the window; others read any entry and are dropped
+        const int blk = bt_lds[min(max(lb - win_lb, 0), PfLds<D>::kBtCap - 1)];
+        const bool blk_ok = blk >= 0 && blk < P.cd.num_blocks;
+        if (ok && !(in_tab && blk_ok))
+          flags |= in_tab ? SPATTN_STATUS_BAD_BLOCK : SPATTN_STATUS_CAPACITY;
+        ok = ok && in_tab && blk_ok;
+        off = (int64_t)blk * blk_stride + head_off + o * D + col;
       } else {
-        kraw[n] = Raw{};
-        vraw[n] = Raw{};
+        const bool in_cap = j < bs && b < P.cd.num_blocks;
+        if (ok && !in_cap) flags |= SPATTN_STATUS_CAPACITY;
+        ok = ok && in_cap;
+        off = req_base + (int64_t)j * D + col;
       }
+      tr.ok[n] = ok;
+      // every lane loads (no register is cleared, so nothing waits for loads in flight): a
+      // missing key reads a safe finite row instead; its score is masked to -inf and its
+      // weight is exactly 0
+      const KT* kp = ok ? kcache + off : safe_k + col;
+      const KT* vp = ok ? vcache + off : safe_v + col;
+      tr.k[n] = *reinterpret_cast<const Raw*>(kp);
+      tr.v[n] = *reinterpret_cast<const Raw*>(vp);
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](const TileRegs& tr, int stage) {
     unsigned char* base = smem + stage * PfLds<D>::kStage;
     OpT* kl = reinterpret_cast<OpT*>(base);
     OpT* vl = reinterpret_cast<OpT*>(base + PfLds<D>::kKBytes);
@@ -216,36 +293,29 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
       const int key = qi / CH, col = (qi % CH) * 8;
       V8 kv, vv;
       if constexpr (kI8) {
-        const int8_t* kc8 = reinterpret_cast<const int8_t*>(&kraw[n]);
-        const int8_t* vc8 = reinterpret_cast<const int8_t*>(&vraw[n]);
+        const int8_t* kc8 = reinterpret_cast<const int8_t*>(&tr.k[n]);
+        const int8_t* vc8 = reinterpret_cast<const int8_t*>(&tr.v[n]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { kv[e] = (OpT)(float)kc8[e]; vv[e] = (OpT)(float)vc8[e]; }
       } else {
-        kv = __builtin_bit_cast(V8, kraw[n]);
-        vv = __builtin_bit_cast(V8, vraw[n]);
+        kv = __builtin_bit_cast(V8, tr.k[n]);
+        vv = __builtin_bit_cast(V8, tr.v[n]);
       }
       *reinterpret_cast<V8*>(kl + key * PfLds<D>::kKld + col) = kv;
       *reinterpret_cast<V8*>(vl + key * PfLds<D>::kVld + col) = vv;
-      if (col == 0) vb[key] = kok[n] ? 1 : 0;
+      if (col == 0) vb[key] = tr.ok[n] ? 1 : 0;
     }
     // one flag per loading wave: every key it loaded exists
     bool all_ok = true;
 #pragma unroll
-    for (int n = 0; n < NCH; ++n) all_ok = all_ok && kok[n];
+    for (int n = 0; n < NCH; ++n) all_ok = all_ok && tr.ok[n];
     const bool wave_ok = __ballot(!all_ok) == 0;
     if (lane == 0) vb[kPfTile + wave] = wave_ok ? 1 : 0;
   };
 
-  if (n_tiles > 0) {
-    load_tile(kt_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
+  auto compute_tile = [&](int it) {
     const int kt = kt_begin + it * kPfTile;
     const int stage = it & 1;
-    const bool has_next = it + 1 < n_tiles;
-    if (has_next) load_tile(kt + kPfTile);
     // skip tiles outside this wave's key range (fully masked for every row it owns)
     if (wave_active && kt + kPfTile - 1 >= w_lo && kt <= w_p_last) {
       const unsigned char* base = smem + stage * PfLds<D>::kStage;
@@ -280,7 +350,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
       float mt = s[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
-      mt = xor_max(mt, 32);
+      mt = half_swap_max(mt);                    // the row's other lane half
       const float m_new = fmaxf(m_run, mt);      // raw-score maximum of the row
       // the reference maximum moves only when some row's maximum outgrows it by more than
       // kLazyRescaleLog2 (in the exponent); a row's first visible key always moves it
@@ -323,12 +393,39 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams P) {
           }
       }
     }
-    if (has_next) store_tile(stage ^ 1);
+  };
+
+  // Iteration it computes tile it from LDS stage it & 1 while tile it + 2 loads into the
+  // register buffer tile it freed; tile it + 1 (loaded one iteration earlier) then goes to
+  // the other stage.  One barrier per tile.
+  auto step = [&](int it, TileRegs& next, TileRegs& later) {
+    if (it + 2 < n_tiles) {
+      ensure_window(it + 2);
+      load_tile(later, kt_begin + (it + 2) * kPfTile);
+    }
+    compute_tile(it);
+    if (it + 1 < n_tiles) store_tile(next, (it + 1) & 1);
     __syncthreads();
+  };
+  TileRegs ra, rb;
+  if (n_tiles > 0) load_tile(ra, kt_begin);
+  if (n_tiles > 1) {
+    ensure_window(1);
+    load_tile(rb, kt_begin + kPfTile);
   }
+  if (n_tiles > 0) store_tile(ra, 0);
+  __syncthreads();
+  // two steps per trip with fixed buffer roles, so no register copies (which would wait for
+  // the loads in flight) are needed; an odd last tile runs after the loop
+  int it = 0;
+  for (; it + 1 < n_tiles; it += 2) {
+    step(it, rb, ra);
+    step(it + 1, ra, rb);
+  }
+  if (it < n_tiles) step(it, rb, ra);
 
   // ---- finalise: sink, normalise, store (lane: row l32, dims 32m + 8(i/4) + 4h + i%4) ----
-  l_run = xor_sum(l_run, 32);                        // both lane halves of the row
+  l_run = half_swap_sum(l_run);                      // both lane halves of the row
   if (row_ok) {
     QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
     float f = 0.f, inv = 0.f;
@@ -396,6 +493,7 @@ int launch_prefill_attention(const AttnArgs& a, hipStream_t stream) {
   if (total <= 0) return SPATTN_OK;
   if (total > 0x7fffffffL) return SPATTN_ERR_SHAPE;
   P.total = (int)total;
+  P.xcd_pairs = (a.B * a.H_kv) % 8 == 0 ? 1 : 0;
   const bool i8 = a.cache_dtype == SPATTN_I8;
   if (a.D == 64) {
     if (a.dtype == SPATTN_F16) { if (i8) launch_prefill_typed<f16, int8_t, 64>(P, RW, stream); else launch_prefill_typed<f16, f16, 64>(P, RW, stream); }

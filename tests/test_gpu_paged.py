@@ -72,6 +72,10 @@ PREFILL = [
     ("f16_w1", dict(kv_lens=[40], q_lens=[40], H_q=8, H_kv=2, D=64, dtype=synth.F16, local_window=1)),
     ("f16_bs5", dict(kv_lens=[61, 20], q_lens=[61, 12], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=5, sinks=True)),
     ("f16_empty_mixed", dict(kv_lens=[0, 50, 0, 9], q_lens=[0, 50, 0, 9], H_q=8, H_kv=2, D=64, dtype=synth.F16, sinks=True)),
+    # a key range of more than 512 blocks (block size 4): block ids read from the table in
+    # global memory instead of the staged copy
+    ("f16_bs4_long_table", dict(kv_lens=[2100, 70], q_lens=[40, 70], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=4, sinks=True)),
+    ("bf16_bs4_long_table_d128", dict(kv_lens=[2300], q_lens=[33], H_q=4, H_kv=1, D=128, dtype=synth.BF16, block_size=4)),
 ]
 
 
