@@ -485,7 +485,9 @@ int launch_prefill_attention(const AttnArgs& a, hipStream_t stream) {
   P.group = a.H_q / a.H_kv;
   P.max_q = a.max_q; P.max_k = a.max_k; P.window = a.window;
   P.scale_log2 = a.scale * kLog2e;
-  const int RW = P.group >= 4 ? 1 : (P.group == 1 ? 4 : 2);
+  // workgroup = RW row blocks x (4 / RW) heads: two row blocks of two heads measured fastest
+  // for groups of 4 or more (more rows per K/V tile than four heads of one row block)
+  const int RW = P.group == 1 ? 4 : 2;
   const int HW = 4 / RW;
   P.n_hg = (P.group + HW - 1) / HW;
   P.n_rt = (a.max_q + 32 * RW - 1) / (32 * RW);
