@@ -54,18 +54,36 @@ struct PrefillParams {
   float scale_log2;
 };
 
-template <int D>
+// LDS stage of a 32-key K/V tile.  16-bit caches arrive by LDS DMA, which writes each
+// lane's 16 bytes at a fixed place, so their rows are unpadded and the 16-byte chunks of key
+// k are XOR-swizzled by k (chunk c sits in slot c ^ (k mod D/8)) to spread the operand reads
+// over the banks; INT8 caches are converted in registers and stored with padded rows.
+template <int D, bool kDma>
 struct PfLds {
-  static constexpr int kKld = D + 8;     // K tile row (elements)
-  static constexpr int kVld = D + 16;    // V tile row (elements)
+  static constexpr int kKld = kDma ? D : D + 8;    // K tile row (elements)
+  static constexpr int kVld = kDma ? D : D + 16;   // V tile row (elements)
   static constexpr int kKBytes = kPfTile * kKld * 2;
   static constexpr int kVBytes = kPfTile * kVld * 2;
   static constexpr int kStage = kKBytes + kVBytes + kPfTile * 4 + 16;  // + key validity words
                                                                        // + 4 per-wave flags
+  static constexpr int kStages = kDma ? 3 : 2;     // DMA: compute, landed, in flight
   static constexpr int kBtCap = 512;     // window of block ids staged in LDS
-  static constexpr int kBtOffset = 2 * kStage;
+  static constexpr int kBtOffset = kStages * kStage;
   static constexpr int kTotal = kBtOffset + kBtCap * 4;
+  static_assert(kStage % 16 == 0, "DMA destinations are 16-byte aligned");
 };
+
+// LDS-DMA of 16 bytes per lane (lane l's bytes land at lds + 16 * l) and the waits the
+// compiler does not insert for it.
+__device__ __forceinline__ void pf_dma16(const void* gptr, void* lds) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void pf_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void pf_wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // 4 waves per SIMD at D = 64 (128 registers: both tile buffers, the accumulators and the
 // query operand fit), 2 at D = 128.
@@ -78,6 +96,9 @@ void prefill_kernel(PrefillParams P) {
   constexpr int CH = D / 8;           // 8-element chunks per row
   constexpr int NCH = kPfTile * CH / kPfThreads;
   constexpr bool kI8 = sizeof(KT) == 1;
+  constexpr bool kDma = !kI8;
+  typedef PfLds<D, kDma> L;
+  constexpr int CHK = D / 8;          // 16-byte chunks per K/V row
   typedef typename std::conditional<kI8, f16, QT>::type OpT;
   typedef typename Op32<OpT>::v8 V8;
   typedef typename Op32<OpT>::v4 V4;
@@ -203,7 +224,7 @@ void prefill_kernel(PrefillParams P) {
   // ---- block ids of the key range, staged in LDS (paged caches) ----
   // The window holds the ids of logical blocks win_lb .. win_lb + kBtCap - 1; a workgroup
   // whose key range needs more refills it between barriers (block size 16: every 8192 keys).
-  int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + PfLds<D>::kBtOffset);
+  int32_t* bt_lds = reinterpret_cast<int32_t*>(smem + L::kBtOffset);
   const bool paged = P.cd.block_table != nullptr;
   const int bs = P.cd.block_size;
   const bool pow2 = P.cd.bs_shift >= 0;
@@ -212,7 +233,7 @@ void prefill_kernel(PrefillParams P) {
   int win_lb = n_tiles > 0 ? lblock(j_lo) : 0;
   auto fill_window = [&]() {
     const int32_t* row = P.cd.block_table + (int64_t)b * P.cd.max_blocks;
-    for (int i = tid; i < PfLds<D>::kBtCap; i += kPfThreads) {
+    for (int i = tid; i < L::kBtCap; i += kPfThreads) {
       const int lb = win_lb + i;
       // never read past the table width or the blocks of the key range
       bt_lds[i] = lb < P.cd.max_blocks && lb <= lb_last ? row[lb] : 0;
@@ -226,7 +247,7 @@ void prefill_kernel(PrefillParams P) {
   auto ensure_window = [&](int it) {
     if (!paged) return;
     const int kt = kt_begin + it * kPfTile;
-    if (lblock(min(kt + kPfTile - 1, j_hi)) < win_lb + PfLds<D>::kBtCap) return;
+    if (lblock(min(kt + kPfTile - 1, j_hi)) < win_lb + L::kBtCap) return;
     __syncthreads();                       // every thread is done with the old window
     win_lb = lblock(max(kt, j_lo));
     fill_window();
@@ -247,31 +268,34 @@ void prefill_kernel(PrefillParams P) {
   const int64_t blk_stride = (int64_t)P.cd.H_kv * bs * D;
   const int64_t head_off = (int64_t)c * bs * D;
   const int64_t req_base = ((int64_t)b * P.cd.H_kv + c) * bs * D;   // contiguous caches
+  // element offset of key j's cache row (KV head c), or ok = false (missing key: flagged,
+  // never read)
+  auto key_row = [&](int j, bool& ok) -> int64_t {
+    ok = j >= j_lo && j <= j_hi;
+    if (paged) {
+      const int lb = lblock(j);
+      const int o = j - lb * bs;
+      const bool in_tab = lb < P.cd.max_blocks;
+      // in-range keys index the window; others read any entry and are dropped
+      const int blk = bt_lds[min(max(lb - win_lb, 0), L::kBtCap - 1)];
+      const bool blk_ok = blk >= 0 && blk < P.cd.num_blocks;
+      if (ok && !(in_tab && blk_ok))
+        flags |= in_tab ? SPATTN_STATUS_BAD_BLOCK : SPATTN_STATUS_CAPACITY;
+      ok = ok && in_tab && blk_ok;
+      return (int64_t)blk * blk_stride + head_off + o * D;
+    }
+    const bool in_cap = j < bs && b < P.cd.num_blocks;
+    if (ok && !in_cap) flags |= SPATTN_STATUS_CAPACITY;
+    ok = ok && in_cap;
+    return req_base + (int64_t)j * D;
+  };
   auto load_tile = [&](TileRegs& tr, int kt) {
 #pragma unroll
     for (int n = 0; n < NCH; ++n) {
       const int qi = tid + n * kPfThreads;
       const int key = qi / CH, col = (qi % CH) * 8;
-      const int j = kt + key;
-      bool ok = j >= j_lo && j <= j_hi;
-      int64_t off;
-      if (paged) {
-        const int lb = lblock(j);
-        const int o = j - lb * bs;
-        const bool in_tab = lb < P.cd.max_blocks;
-        // in-range keys index the window; others read any entry and are dropped
-        const int blk = bt_lds[min(max(lb - win_lb, 0), PfLds<D>::kBtCap - 1)];
-        const bool blk_ok = blk >= 0 && blk < P.cd.num_blocks;
-        if (ok && !(in_tab && blk_ok))
-          flags |= in_tab ? SPATTN_STATUS_BAD_BLOCK : SPATTN_STATUS_CAPACITY;
-        ok = ok && in_tab && blk_ok;
-        off = (int64_t)blk * blk_stride + head_off + o * D + col;
-      } else {
-        const bool in_cap = j < bs && b < P.cd.num_blocks;
-        if (ok && !in_cap) flags |= SPATTN_STATUS_CAPACITY;
-        ok = ok && in_cap;
-        off = req_base + (int64_t)j * D + col;
-      }
+      bool ok;
+      const int64_t off = key_row(kt + key, ok) + col;
       tr.ok[n] = ok;
       // every lane loads (no register is cleared, so nothing waits for loads in flight): a
       // missing key reads a safe finite row instead; its score is masked to -inf and its
@@ -282,11 +306,37 @@ void prefill_kernel(PrefillParams P) {
       tr.v[n] = *reinterpret_cast<const Raw*>(vp);
     }
   };
+  // 16-bit caches: DMA of a tile straight into an LDS stage.  Instruction q of the tile
+  // (wave w issues q = w * kDmaPerWave + n) fills 16-byte positions 64q .. 64q + 63, i.e.
+  // key p / CHK, slot p % CHK, which holds the key's chunk slot ^ (key mod CHK).
+  constexpr int kDmaPerWave = kPfTile * CHK / (64 * (kPfThreads / 64));
+  auto issue_dma = [&](int kt, int stage) {
+    unsigned char* base = smem + stage * L::kStage;
+    int32_t* vb = reinterpret_cast<int32_t*>(base + L::kKBytes + L::kVBytes);
+    bool all_ok = true;
+#pragma unroll
+    for (int n = 0; n < kDmaPerWave; ++n) {
+      const int q = wave * kDmaPerWave + n;
+      const int p = q * 64 + lane;
+      const int key = p / CHK, slot = p % CHK;
+      const int col = (slot ^ (key & (CHK - 1))) * 8;
+      bool ok;
+      const int64_t off = key_row(kt + key, ok) + col;
+      const KT* kp = ok ? kcache + off : safe_k + col;
+      const KT* vp = ok ? vcache + off : safe_v + col;
+      pf_dma16(kp, base + q * 1024);
+      pf_dma16(vp, base + L::kKBytes + q * 1024);
+      if (slot == 0) vb[key] = ok ? 1 : 0;
+      all_ok = all_ok && ok;
+    }
+    const bool wave_ok = __ballot(!all_ok) == 0;
+    if (lane == 0) vb[kPfTile + wave] = wave_ok ? 1 : 0;
+  };
   auto store_tile = [&](const TileRegs& tr, int stage) {
-    unsigned char* base = smem + stage * PfLds<D>::kStage;
+    unsigned char* base = smem + stage * L::kStage;
     OpT* kl = reinterpret_cast<OpT*>(base);
-    OpT* vl = reinterpret_cast<OpT*>(base + PfLds<D>::kKBytes);
-    int32_t* vb = reinterpret_cast<int32_t*>(base + PfLds<D>::kKBytes + PfLds<D>::kVBytes);
+    OpT* vl = reinterpret_cast<OpT*>(base + L::kKBytes);
+    int32_t* vb = reinterpret_cast<int32_t*>(base + L::kKBytes + L::kVBytes);
 #pragma unroll
     for (int n = 0; n < NCH; ++n) {
       const int qi = tid + n * kPfThreads;
@@ -301,8 +351,8 @@ void prefill_kernel(PrefillParams P) {
         kv = __builtin_bit_cast(V8, tr.k[n]);
         vv = __builtin_bit_cast(V8, tr.v[n]);
       }
-      *reinterpret_cast<V8*>(kl + key * PfLds<D>::kKld + col) = kv;
-      *reinterpret_cast<V8*>(vl + key * PfLds<D>::kVld + col) = vv;
+      *reinterpret_cast<V8*>(kl + key * L::kKld + col) = kv;
+      *reinterpret_cast<V8*>(vl + key * L::kVld + col) = vv;
       if (col == 0) vb[key] = tr.ok[n] ? 1 : 0;
     }
     // one flag per loading wave: every key it loaded exists
@@ -313,20 +363,29 @@ void prefill_kernel(PrefillParams P) {
     if (lane == 0) vb[kPfTile + wave] = wave_ok ? 1 : 0;
   };
 
-  auto compute_tile = [&](int it) {
+  // byte offset of logical 16-byte chunk c of key kk within a K / V tile
+  auto k_chunk = [&](int kk, int c) -> int {
+    if constexpr (kDma) return kk * D * 2 + ((c ^ (kk & (CHK - 1))) << 4);
+    else return (kk * L::kKld + c * 8) * 2;
+  };
+  auto v_chunk = [&](int kk, int c) -> int {
+    if constexpr (kDma) return kk * D * 2 + ((c ^ (kk & (CHK - 1))) << 4);
+    else return (kk * L::kVld + c * 8) * 2;
+  };
+  auto compute_tile = [&](int it, int stage) {
     const int kt = kt_begin + it * kPfTile;
-    const int stage = it & 1;
     // skip tiles outside this wave's key range (fully masked for every row it owns)
     if (wave_active && kt + kPfTile - 1 >= w_lo && kt <= w_p_last) {
-      const unsigned char* base = smem + stage * PfLds<D>::kStage;
+      const unsigned char* base = smem + stage * L::kStage;
       const OpT* kl = reinterpret_cast<const OpT*>(base);
-      const OpT* vl = reinterpret_cast<const OpT*>(base + PfLds<D>::kKBytes);
-      const int32_t* vb = reinterpret_cast<const int32_t*>(base + PfLds<D>::kKBytes + PfLds<D>::kVBytes);
+      const OpT* vl = reinterpret_cast<const OpT*>(base + L::kKBytes);
+      const int32_t* vb = reinterpret_cast<const int32_t*>(base + L::kKBytes + L::kVBytes);
       // S^T: A = K[key l32][16kc + 8h ..], B = qop
       f32x16 s = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        V8 a = *reinterpret_cast<const V8*>(kl + l32 * PfLds<D>::kKld + kc * 16 + h * 8);
+        V8 a = *reinterpret_cast<const V8*>(reinterpret_cast<const unsigned char*>(kl) +
+                                            k_chunk(l32, 2 * kc + h));
         s = mfma32(a, qop[kc], s);
       }
       // lane holds keys 8*(i/4) + 4*h + i%4 of row l32.  Masks only on tiles some row of the
@@ -379,9 +438,12 @@ void prefill_kernel(PrefillParams P) {
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            const OpT* a0 = vl + (16 * ks + 4 * h + (lam >> 2)) * PfLds<D>::kVld + 32 * m +
-                            16 * (grp & 1) + 4 * (lam & 3);
-            const OpT* a1 = a0 + 8 * PfLds<D>::kVld;
+            // key vk, dims d .. d + 3 (8 bytes inside chunk d / 8), and key vk + 8
+            const int vk = 16 * ks + 4 * h + (lam >> 2);
+            const int d = 32 * m + 16 * (grp & 1) + 4 * (lam & 3);
+            const unsigned char* vlb = reinterpret_cast<const unsigned char*>(vl);
+            const OpT* a0 = reinterpret_cast<const OpT*>(vlb + v_chunk(vk, d >> 3) + (d & 7) * 2);
+            const OpT* a1 = reinterpret_cast<const OpT*>(vlb + v_chunk(vk + 8, d >> 3) + (d & 7) * 2);
             s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4*)(a0));
             s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -395,34 +457,61 @@ void prefill_kernel(PrefillParams P) {
     }
   };
 
-  // Iteration it computes tile it from LDS stage it & 1 while tile it + 2 loads into the
-  // register buffer tile it freed; tile it + 1 (loaded one iteration earlier) then goes to
-  // the other stage.  One barrier per tile.
-  auto step = [&](int it, TileRegs& next, TileRegs& later) {
-    if (it + 2 < n_tiles) {
-      ensure_window(it + 2);
-      load_tile(later, kt_begin + (it + 2) * kPfTile);
+  if constexpr (kDma) {
+    // Iteration it computes tile it from stage it % 3 while tile it + 2 streams into stage
+    // (it + 2) % 3 (last read in iteration it - 1, before its barrier); before the barrier
+    // each wave waits for its DMAs of tile it + 1.  One barrier per tile.
+    if (n_tiles > 0) issue_dma(kt_begin, 0);
+    if (n_tiles > 1) {
+      ensure_window(1);
+      issue_dma(kt_begin + kPfTile, 1);
     }
-    compute_tile(it);
-    if (it + 1 < n_tiles) store_tile(next, (it + 1) & 1);
+    if (n_tiles > 1) pf_wait_vm<2 * kDmaPerWave>(); else pf_wait_vm<0>();
+    pf_wait_lgkm0();
     __syncthreads();
-  };
-  TileRegs ra, rb;
-  if (n_tiles > 0) load_tile(ra, kt_begin);
-  if (n_tiles > 1) {
-    ensure_window(1);
-    load_tile(rb, kt_begin + kPfTile);
+    int stage = 0;
+    for (int it = 0; it < n_tiles; ++it) {
+      const bool more = it + 2 < n_tiles;
+      if (more) {
+        ensure_window(it + 2);
+        issue_dma(kt_begin + (it + 2) * kPfTile, stage == 0 ? 2 : stage - 1);
+      }
+      compute_tile(it, stage);
+      if (more) pf_wait_vm<2 * kDmaPerWave>(); else pf_wait_vm<0>();   // tile it + 1 landed
+      pf_wait_lgkm0();
+      __syncthreads();
+      stage = stage == 2 ? 0 : stage + 1;
+    }
+  } else {
+    // Iteration it computes tile it from LDS stage it & 1 while tile it + 2 loads into the
+    // register buffer tile it freed; tile it + 1 (loaded one iteration earlier) then goes to
+    // the other stage.  One barrier per tile.
+    auto step = [&](int it, TileRegs& next, TileRegs& later) {
+      if (it + 2 < n_tiles) {
+        ensure_window(it + 2);
+        load_tile(later, kt_begin + (it + 2) * kPfTile);
+      }
+      compute_tile(it, it & 1);
+      if (it + 1 < n_tiles) store_tile(next, (it + 1) & 1);
+      __syncthreads();
+    };
+    TileRegs ra, rb;
+    if (n_tiles > 0) load_tile(ra, kt_begin);
+    if (n_tiles > 1) {
+      ensure_window(1);
+      load_tile(rb, kt_begin + kPfTile);
+    }
+    if (n_tiles > 0) store_tile(ra, 0);
+    __syncthreads();
+    // two steps per trip with fixed buffer roles, so no register copies (which would wait
+    // for the loads in flight) are needed; an odd last tile runs after the loop
+    int it = 0;
+    for (; it + 1 < n_tiles; it += 2) {
+      step(it, rb, ra);
+      step(it + 1, ra, rb);
+    }
+    if (it < n_tiles) step(it, rb, ra);
   }
-  if (n_tiles > 0) store_tile(ra, 0);
-  __syncthreads();
-  // two steps per trip with fixed buffer roles, so no register copies (which would wait for
-  // the loads in flight) are needed; an odd last tile runs after the loop
-  int it = 0;
-  for (; it + 1 < n_tiles; it += 2) {
-    step(it, rb, ra);
-    step(it + 1, ra, rb);
-  }
-  if (it < n_tiles) step(it, rb, ra);
 
   // ---- finalise: sink, normalise, store (lane: row l32, dims 32m + 8(i/4) + 4h + i%4) ----
   l_run = half_swap_sum(l_run);                      // both lane halves of the row
@@ -461,7 +550,7 @@ void prefill_kernel(PrefillParams P) {
 
 template <typename QT, typename KT, int D>
 static void launch_prefill_typed(const PrefillParams& P, int RW, hipStream_t stream) {
-  const size_t lds = PfLds<D>::kTotal;
+  const size_t lds = PfLds<D, sizeof(KT) == 2>::kTotal;
   dim3 grid(P.total), block(kPfThreads);
   if (RW == 1) hipLaunchKernelGGL((prefill_kernel<QT, KT, D, 1>), grid, block, lds, stream, P);
   else if (RW == 2) hipLaunchKernelGGL((prefill_kernel<QT, KT, D, 2>), grid, block, lds, stream, P);
