@@ -92,6 +92,7 @@ extern "C" {
 #define SPATTN_STATUS_BAD_INDEX (1 << 5)  /* a selected index (inside the count) is neither -1 nor in range */
 #define SPATTN_STATUS_BAD_COUNT (1 << 6)  /* a selected count outside [0, max_selected]; clamped */
 #define SPATTN_STATUS_SHORT_KV (1 << 7)   /* fewer keys than query rows: rows before key 0 see nothing */
+#define SPATTN_STATUS_CURSOR (1 << 8)     /* committed_length disagrees with the append position */
 
 /* attention kinds for attention_workspace_bytes */
 #define SPATTN_KIND_PAGED 0
@@ -130,13 +131,20 @@ SPATTN_API int prepare_seqlens(const int32_t* cu_seqlens_q, const int32_t* past_
  *   key_scale / value_scale [H_kv, D] float32 are then required.
  *   Rows without a slot are skipped: p < 0 (SHORT_KV), past the capacity (CAPACITY), a
  *   block id outside [0, num_blocks) (BAD_BLOCK).
+ *   committed_length [B] (optional, may be NULL): the key count the caller's cursor says
+ *   request b held before this step ([I8] Key Changes: optional committed_length input;
+ *   review finding "Strict mode ignores cursor validation errors").  A request with rows
+ *   whose committed_length[b] differs from seqlens_k[b] + 1 - q_len_b raises
+ *   SPATTN_STATUS_CURSOR and none of its rows is written; other requests append normally.
+ *   The check is on the device: a caller that must not run attention after a failed check
+ *   reads `status` (or skips the call) itself.
  */
 SPATTN_API int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
                     const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int B, int T,
                     void* k_cache, void* v_cache, int cache_dtype, const int32_t* block_table,
                     int max_blocks_per_seq, int block_size, int num_blocks,
                     const float* key_scale, const float* value_scale, int H_kv, int D,
-                    int32_t* status, void* stream);
+                    const int32_t* committed_length, int32_t* status, void* stream);
 
 /*
  * attention_workspace_bytes - device workspace (bytes) an attention call with these

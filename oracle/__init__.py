@@ -27,7 +27,7 @@ page fixes (the sanitisation of malformed inputs and the status bits) are marked
 """
 from .status import (  # noqa: F401
     STATUS_BAD_CU, STATUS_Q_BOUND, STATUS_K_BOUND, STATUS_CAPACITY, STATUS_BAD_BLOCK,
-    STATUS_BAD_INDEX, STATUS_BAD_COUNT, STATUS_SHORT_KV,
+    STATUS_BAD_INDEX, STATUS_BAD_COUNT, STATUS_SHORT_KV, STATUS_CURSOR,
 )
 from .metadata import prepare_seqlens  # noqa: F401
 from .append import quantize_int8, kv_cache_append  # noqa: F401

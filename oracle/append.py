@@ -5,13 +5,17 @@ into the paged cache through a token-to-slot mapping derived from the block tabl
 "[WebGPU] Add DynamicSparseAttention", Description: contiguous per-request caches are
 updated in place (alias-safe).  DynamicSparseAttention INT8 KV cache (onnxruntime PR
 33472), Key Changes table: INT8 caches carry per-channel fp32 key_scale / value_scale and
-the append quantises with them.
+the append quantises with them.  The same page adds an optional committed_length input,
+and its review finding "Strict mode ignores cursor validation errors" shows a cursor that
+disagrees with the sequence lengths (batch 1, one new row, capacity 2, seqlens_k = {0},
+committed_length = {1}) still appending; here such a request is flagged before any of its
+rows is written, and none is.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .status import STATUS_CAPACITY, STATUS_BAD_BLOCK, STATUS_SHORT_KV
+from .status import STATUS_CAPACITY, STATUS_BAD_BLOCK, STATUS_CURSOR, STATUS_SHORT_KV
 
 
 def quantize_int8(x, s):
@@ -38,7 +42,8 @@ def _check_cu(cu, B, T):
 
 
 def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
-                    block_table=None, block_size=None, key_scale=None, value_scale=None):
+                    block_table=None, block_size=None, key_scale=None, value_scale=None,
+                    committed_length=None):
     """Write row ``cu[b] + i`` of ``k_new`` / ``v_new`` (``[T, H_kv, D]``) at key position
     ``p = (seqlens_k[b] + 1) - q_len_b + i`` of request ``b``.
 
@@ -47,6 +52,11 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
     cache ``[B, H_kv, cap, D]`` (``block_table is None``) -> block ``b``, slot ``p``.  The
     row of KV head ``c`` goes to ``cache[block, c, slot]``.  Float caches store the row as
     is (same dtype); INT8 caches store ``quantize_int8(row, scale[c][d])``.
+
+    ``committed_length[b]`` (optional) is the key count the caller believes request ``b``
+    already holds.  It must equal ``kv_len - q_len_b`` (the position of the first row this
+    step writes); otherwise STATUS_CURSOR is raised and none of the request's rows is
+    written (checked before any write of the request).
 
     Rows whose slot does not exist are skipped and flagged (parity unpinned): ``p < 0``
     (STATUS_SHORT_KV), ``p // bs >= max_blocks_per_seq`` or ``p >= cap``
@@ -64,9 +74,13 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
     int8 = kc.dtype == np.int8
     nb = kc.shape[0]
     status = 0
+    committed = None if committed_length is None else [int(x) for x in np.asarray(committed_length).reshape(-1)]
     for b in range(B):
         q_len = cu[b + 1] - cu[b]
         kv_len = sk[b] + 1
+        if committed is not None and q_len > 0 and committed[b] != kv_len - q_len:
+            status |= STATUS_CURSOR
+            continue
         for i in range(q_len):
             r = cu[b] + i
             p = kv_len - q_len + i

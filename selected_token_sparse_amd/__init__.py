@@ -25,6 +25,7 @@ STATUS_BAD_BLOCK = 1 << 4
 STATUS_BAD_INDEX = 1 << 5
 STATUS_BAD_COUNT = 1 << 6
 STATUS_SHORT_KV = 1 << 7
+STATUS_CURSOR = 1 << 8
 
 _ERRORS = {-1: "null pointer", -2: "shape", -3: "dtype", -4: "unsupported", -5: "workspace too small",
            -6: "launch failed"}
@@ -98,8 +99,11 @@ def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, cu_seqlens_q: torc
                     block_table: Optional[torch.Tensor] = None,
                     key_scale: Optional[torch.Tensor] = None,
                     value_scale: Optional[torch.Tensor] = None,
-                    status: Optional[torch.Tensor] = None) -> None:
-    """Write this step's K/V rows ([T, H_kv, D]) into the cache in place."""
+                    status: Optional[torch.Tensor] = None,
+                    committed_length: Optional[torch.Tensor] = None) -> None:
+    """Write this step's K/V rows ([T, H_kv, D]) into the cache in place.  With
+    `committed_length` ([B] int32), a request whose cursor disagrees with its append
+    position is flagged (STATUS_CURSOR) and left unwritten."""
     T, H_kv, D = (int(x) for x in k_new.shape)
     B = int(seqlens_k.shape[0])
     nb, bs, mbps = _cache_dims(k_cache, block_table)
@@ -109,7 +113,7 @@ def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, cu_seqlens_q: torc
         _i32(seqlens_k, "seqlens_k"), B, T, _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
         _dt(k_cache), _i32(block_table, "block_table"), mbps, bs, nb,
         _ptr(key_scale, "key_scale"), _ptr(value_scale, "value_scale"), H_kv, D,
-        _i32(status, "status"), _stream(k_new)))
+        _i32(committed_length, "committed_length"), _i32(status, "status"), _stream(k_new)))
 
 
 def attention_workspace_bytes(kind: int, dtype: int, B: int, T: int, max_seqlen_q: int,

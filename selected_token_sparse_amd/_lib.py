@@ -18,7 +18,7 @@ _SIGNATURES = {
                                 c_void_p, c_void_p, c_void_p]),
     "kv_cache_append": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_int,
                                 c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int,
-                                c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p]),
+                                c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "attention_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                              c_int, c_int, c_int, c_int]),
     "paged_attention_fwd": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_int,

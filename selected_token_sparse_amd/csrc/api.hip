@@ -62,7 +62,7 @@ int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
                     void* k_cache, void* v_cache, int cache_dtype, const int32_t* block_table,
                     int max_blocks_per_seq, int block_size, int num_blocks,
                     const float* key_scale, const float* value_scale, int H_kv, int D,
-                    int32_t* status, void* stream) {
+                    const int32_t* committed_length, int32_t* status, void* stream) {
   if (B < 0 || T < 0 || H_kv < 1 || D < 8 || D % 8 != 0) return SPATTN_ERR_SHAPE;
   if (!float_dtype(new_dtype)) return SPATTN_ERR_DTYPE;
   if (cache_dtype != SPATTN_I8 && !float_dtype(cache_dtype)) return SPATTN_ERR_DTYPE;
@@ -75,8 +75,8 @@ int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
   if (rc != SPATTN_OK) return rc;
   return launch_kv_cache_append(k_new, v_new, new_dtype, cu_seqlens_q, seqlens_k, B, T, k_cache,
                                 v_cache, cache_dtype, block_table, max_blocks_per_seq, block_size,
-                                num_blocks, key_scale, value_scale, H_kv, D, status,
-                                (hipStream_t)stream);
+                                num_blocks, key_scale, value_scale, H_kv, D, committed_length,
+                                status, (hipStream_t)stream);
 }
 
 size_t attention_workspace_bytes(int kind, int dtype, int B, int T, int max_seqlen_q,

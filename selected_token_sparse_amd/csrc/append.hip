@@ -37,7 +37,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const NewT* __restrict__ k_new, const NewT* __restrict__ v_new, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seqlens_k, int B, void* __restrict__ k_cache,
     void* __restrict__ v_cache, CacheDesc cd, const float* __restrict__ key_scale,
-    const float* __restrict__ value_scale, int32_t* status) {
+    const float* __restrict__ value_scale, const int32_t* __restrict__ committed,
+    int32_t* status) {
   const int r = blockIdx.x;
   int flags = 0;
   const int b = find_request(cu, B, r);
@@ -48,7 +49,10 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const int q_len = cu[b + 1] - cu[b];
     const int kv_len = seqlens_k[b] + 1;
     const int p = kv_len - q_len + (r - cu[b]);
-    if (p < 0) flags |= SPATTN_STATUS_SHORT_KV;
+    // the caller's cursor must agree with the first position this step writes; every row
+    // of the request makes the same check, so a disagreeing request writes nothing
+    if (committed != nullptr && committed[b] != kv_len - q_len) flags |= SPATTN_STATUS_CURSOR;
+    else if (p < 0) flags |= SPATTN_STATUS_SHORT_KV;
     else dst = cache_row(cd, b, p, 0, flags);
   }
   if (threadIdx.x == 0) raise_status(status, flags);
@@ -81,7 +85,8 @@ int launch_kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
                            void* k_cache, void* v_cache, int cache_dtype,
                            const int32_t* block_table, int max_blocks, int block_size,
                            int num_blocks, const float* key_scale, const float* value_scale,
-                           int H_kv, int D, int32_t* status, hipStream_t stream) {
+                           int H_kv, int D, const int32_t* committed, int32_t* status,
+                           hipStream_t stream) {
   if (T == 0) return SPATTN_OK;
   CacheDesc cd;
   cd.block_table = block_table;
@@ -96,7 +101,8 @@ int launch_kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
 #define SPATTN_APPEND(NT, I8)                                                              \
   hipLaunchKernelGGL((kv_append_kernel<NT, I8>), grid, block, 0, stream,                   \
                      reinterpret_cast<const NT*>(k_new), reinterpret_cast<const NT*>(v_new), \
-                     cu, seqlens_k, B, k_cache, v_cache, cd, key_scale, value_scale, status)
+                     cu, seqlens_k, B, k_cache, v_cache, cd, key_scale, value_scale, committed, \
+                     status)
   switch (new_dtype) {
     case SPATTN_F32: if (i8) SPATTN_APPEND(float, true); else SPATTN_APPEND(float, false); break;
     case SPATTN_F16: if (i8) SPATTN_APPEND(f16, true); else SPATTN_APPEND(f16, false); break;

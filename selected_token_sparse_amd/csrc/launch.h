@@ -16,7 +16,8 @@ int launch_kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
                            void* k_cache, void* v_cache, int cache_dtype,
                            const int32_t* block_table, int max_blocks, int block_size,
                            int num_blocks, const float* key_scale, const float* value_scale,
-                           int H_kv, int D, int32_t* status, hipStream_t stream);
+                           int H_kv, int D, const int32_t* committed_length, int32_t* status,
+                           hipStream_t stream);
 
 // Everything an attention launch needs; filled and validated by api.hip.
 struct AttnArgs {

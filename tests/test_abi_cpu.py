@@ -106,7 +106,7 @@ def test_sparse_argument_errors(lib, kw, rc):
 
 def test_append_argument_errors(lib):
     f = lib.kv_cache_append
-    base = [FAKE, FAKE, 1, FAKE, FAKE, 2, 4, FAKE, FAKE, 1, FAKE, 4, 16, 8, None, None, 2, 64, None, None]
+    base = [FAKE, FAKE, 1, FAKE, FAKE, 2, 4, FAKE, FAKE, 1, FAKE, 4, 16, 8, None, None, 2, 64, None, None, None]
     def call(i, v):
         a = list(base)
         a[i] = v

@@ -101,3 +101,67 @@ def test_decode_prefill_sparse_step_in_one_graph():
         for got, want, name in zip((out_d, out_p, out_s), eager, ("decode", "prefill", "selected")):
             assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (rep, name)
     assert int(st.item()) == st_eager
+
+
+def test_multi_layer_decode_step_in_one_graph():
+    """One decode step of a 4-layer model as one HIP graph: the metadata pass once, then
+    per layer the append into that layer's cache and the attention over it.  Every replay
+    reproduces the eager outputs bit for bit, and each layer matches the oracle."""
+    layers = 4
+    base = synth.config_gqa_paged_decode(poison=True, B=6, max_len=2500, seed=95)
+    cases = [synth.paged_case(500 + i, kv_lens=base.seqlens_k + 1, q_lens=np.diff(base.cu_seqlens_q),
+                              H_q=base.H_q, H_kv=base.H_kv, D=base.D, dtype=base.dtype,
+                              num_blocks=int(((base.seqlens_k + 16) // 16).sum()) + 64,
+                              max_blocks_per_seq=base.max_blocks_per_seq,
+                              sinks=True, scale=base.scale, poison=True,
+                              max_seqlen_k=base.max_seqlen_k)
+             for i in range(layers)]
+    ts = [case_tensors(c) for c in cases]
+    cu = ts[0]["cu"]
+    past = ts[0]["past"]
+    T, B = base.T, base.B
+    sq = torch.empty(B, dtype=torch.int32, device="cuda")
+    sk = torch.empty(B, dtype=torch.int32, device="cuda")
+    st = status_tensor()
+    ws = _ws(sta.KIND_PAGED, cases[0])
+    outs = [torch.empty((T, base.H_q, base.D), dtype=TORCH_DTYPE[base.dtype], device="cuda")
+            for _ in range(layers)]
+
+    def step():
+        sta.prepare_seqlens(cu, past, T, sq, sk, status=st)
+        for t, o, c in zip(ts, outs, cases):
+            sta.kv_cache_append(t["k_new"], t["v_new"], cu, sk, t["k_cache"], t["v_cache"],
+                                t["block_table"], status=st)
+            sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], cu, sk, c.max_seqlen_q,
+                                    c.max_seqlen_k, o, block_table=t["block_table"], scale=c.scale,
+                                    sinks=t["sinks"], workspace=ws, status=st)
+
+    print("multi-layer graph: eager", flush=True)
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    assert int(st.item()) == 0
+    for c, e in zip(cases, eager):
+        ref, ost, _ = oracle_paged_step(c)
+        assert ost == 0
+        assert_close(e, ref, c.dtype, "multi-layer eager")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print(f"multi-layer graph: replay {rep}", flush=True)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o.view(torch.int16), e.view(torch.int16)), (rep, i)
+    assert int(st.item()) == 0

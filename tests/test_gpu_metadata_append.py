@@ -11,6 +11,8 @@ import selected_token_sparse_amd as sta
 import synth
 from synth.device import TORCH_DTYPE, case_tensors, tensor
 
+from harness import status_tensor
+
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -155,3 +157,44 @@ def test_append_quantisation_hand_worked_codes():
     sta.kv_cache_append(xt, xt, cu, sk, kc, vc, None, st_, st_)
     torch.cuda.synchronize()
     assert kc.cpu().numpy().reshape(-1)[:n].tolist() == want[:n].tolist()
+
+
+def test_append_cursor_page_example():
+    """The DynamicSparseAttention INT8 page's strict-mode cursor case (batch 1, one new row,
+    capacity 2, seqlens_k = {0}, committed_length = {1}): flagged, nothing written."""
+    print("append cursor page example", flush=True)
+    rng = np.random.default_rng(21)
+    kc0 = rng.standard_normal((1, 1, 2, 64)).astype(np.float32)
+    k_new = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    kc, vc = tensor(kc0, None), tensor(kc0.copy(), None)
+    kn = tensor(k_new, None)
+    cu = tensor(np.array([0, 1], np.int32), None)
+    sk = tensor(np.array([0], np.int32), None)
+    st = status_tensor()
+    sta.kv_cache_append(kn, kn, cu, sk, kc, vc, status=st,
+                        committed_length=tensor(np.array([1], np.int32), None))
+    torch.cuda.synchronize()
+    assert int(st.item()) == oracle.STATUS_CURSOR
+    assert np.array_equal(kc.cpu().numpy(), kc0) and np.array_equal(vc.cpu().numpy(), kc0)
+
+
+@pytest.mark.parametrize("contiguous", [False, True])
+def test_append_cursor_check_bit_exact(contiguous):
+    print("append cursor mixed batch", contiguous, flush=True)
+    case = synth.paged_case(31, kv_lens=[20, 33, 7, 64], q_lens=[3, 1, 7, 2], H_q=4, H_kv=2, D=64,
+                            block_size=16, dtype=synth.F16, contiguous=contiguous, capacity=64,
+                            poison=True)
+    committed = case.past_seqlens.copy()
+    committed[1] += 1
+    committed[3] -= 2
+    t = case_tensors(case)
+    st = status_tensor()
+    sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], t["seqlens_k"], t["k_cache"], t["v_cache"],
+                        t["block_table"], status=st, committed_length=tensor(committed, None))
+    torch.cuda.synchronize()
+    kc, vc, ost = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, case.seqlens_k,
+                                         case.k_cache, case.v_cache, case.block_table,
+                                         case.block_size, committed_length=committed)
+    assert int(st.item()) == ost == oracle.STATUS_CURSOR
+    assert np.array_equal(t["k_cache"].cpu().numpy().view(np.uint16), kc.view(np.uint16))
+    assert np.array_equal(t["v_cache"].cpu().numpy().view(np.uint16), vc.view(np.uint16))

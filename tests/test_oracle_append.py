@@ -104,3 +104,50 @@ def test_append_skips_missing_slots():
     kc, vc, st = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, sk,
                                         case.k_cache, case.v_cache, case.block_table, case.block_size)
     assert st & oracle.STATUS_CAPACITY
+
+
+def test_cursor_mismatch_page_example_appends_nothing():
+    """The DynamicSparseAttention INT8 page's review finding on strict-mode cursor
+    validation: batch 1, one new row, cache capacity 2, seqlens_k = {0} (the row goes to
+    position 0), committed_length = {1}.  The cursor disagrees with the append position,
+    so the request is flagged and the cache is left untouched."""
+    rng = np.random.default_rng(21)
+    kc = rng.standard_normal((1, 1, 2, 64)).astype(np.float32)   # contiguous [B, H_kv, cap, D]
+    vc = rng.standard_normal((1, 1, 2, 64)).astype(np.float32)
+    k_new = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    v_new = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    cu = np.array([0, 1], np.int32)
+    sk = np.array([0], np.int32)
+    out_k, out_v, st = oracle.kv_cache_append(k_new, v_new, cu, sk, kc, vc,
+                                              committed_length=np.array([1], np.int32))
+    assert st == oracle.STATUS_CURSOR
+    assert np.array_equal(out_k, kc) and np.array_equal(out_v, vc)
+    # the consistent cursor (0 keys before this step) appends the row at position 0
+    out_k, out_v, st = oracle.kv_cache_append(k_new, v_new, cu, sk, kc, vc,
+                                              committed_length=np.array([0], np.int32))
+    assert st == 0
+    assert np.array_equal(out_k[0, 0, 0], k_new[0, 0]) and np.array_equal(out_k[0, 0, 1], kc[0, 0, 1])
+
+
+def test_cursor_check_skips_only_the_inconsistent_request():
+    case = synth.paged_case(14, kv_lens=[20, 33, 7], q_lens=[3, 1, 7], H_q=2, H_kv=1, D=64,
+                            block_size=16, dtype=synth.F16)
+    committed = case.past_seqlens.copy()
+    committed[1] += 1                    # request 1 believes it holds one key more
+    kc, vc, st = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, case.seqlens_k,
+                                        case.k_cache, case.v_cache, case.block_table,
+                                        case.block_size, committed_length=committed)
+    assert st == oracle.STATUS_CURSOR
+    ref_k, _, st0 = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, case.seqlens_k,
+                                           case.k_cache, case.v_cache, case.block_table,
+                                           case.block_size)
+    assert st0 == 0
+    cu = case.cu_seqlens_q
+    for b in range(case.B):
+        q_len = int(cu[b + 1] - cu[b])
+        kv_len = int(case.seqlens_k[b]) + 1
+        for j in range(kv_len - q_len, kv_len):
+            got = _walk(kc, case.block_table, case.block_size, b, j)
+            want = (_walk(case.k_cache, case.block_table, case.block_size, b, j) if b == 1
+                    else _walk(ref_k, case.block_table, case.block_size, b, j))
+            assert np.array_equal(got, want, equal_nan=True), (b, j)
