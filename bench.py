@@ -144,6 +144,72 @@ def bench_decode(steps, warmup, copies=3):
     return case, total_ms / steps, attn_ms, st
 
 
+def bench_decode_graph(layers=24, steps=20, warmup=3, copies=3):
+    """A decode step of a `layers`-layer model (one metadata pass, then per layer the cache
+    append and the attention) on the GQA paged decode workload, eager and replayed from one
+    HIP graph.  Layer i uses the i % 3 copy of the KV pool, so consecutive layers read
+    different 655 MB pools as a real model's layers would."""
+    import torch
+
+    import selected_token_sparse_amd as sta
+    import synth
+    from synth.device import case_tensors
+
+    case = synth.config_gqa_paged_decode()
+    base = case_tensors(case)
+    sets = [base] + [dict(base, k_cache=base["k_cache"].clone(), v_cache=base["v_cache"].clone())
+                     for _ in range(copies - 1)]
+    B, T = case.B, case.T
+    sq = torch.empty(B, dtype=torch.int32, device="cuda")
+    sk = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, case.H_q, case.D), dtype=torch.float16, device="cuda")
+    need = sta.attention_workspace_bytes(sta.KIND_PAGED, sta.F16, B, T, case.max_seqlen_q,
+                                         case.max_seqlen_k, 0, case.local_window, case.H_q,
+                                         case.H_kv, case.D)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sta.prepare_seqlens(base["cu"], base["past"], T, sq, sk)
+        for layer in range(layers):
+            t = sets[layer % copies]
+            sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], sk, t["k_cache"], t["v_cache"],
+                                t["block_table"])
+            sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], sk,
+                                    case.max_seqlen_q, case.max_seqlen_k, out,
+                                    block_table=t["block_table"], scale=case.scale,
+                                    sinks=t["sinks"], workspace=ws)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = _events()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    eager_us = timed(step)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    graph_us = timed(g.replay)
+    kv = _kv_bytes(case) * layers
+    return {"workload": f"{case.name} x {layers} layers", "layers": layers,
+            "eager_us_per_step": round(eager_us, 1), "graph_us_per_step": round(graph_us, 1),
+            "graph_us_per_layer": round(graph_us / layers, 2),
+            "graph_kv_gbs": round(kv / (graph_us * 1e-6) / 1e9, 1)}
+
+
 def bench_prefill(window, steps, warmup):
     import torch
 
@@ -317,6 +383,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sparse", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -362,6 +429,8 @@ def main():
     if not args.no_prefill:
         line["prefill"] = bench_prefill(128, 50, 5)
         line["prefill_no_window"] = bench_prefill(-1, 30, 3)
+    if not args.no_graph:
+        line["decode_graph"] = bench_decode_graph()
     if not args.no_sparse:
         line["selected_decode"] = bench_sparse("selected", 50, 5)
         line["local_plus_aux"] = bench_sparse("local_aux", 50, 5)
