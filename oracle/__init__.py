@@ -30,5 +30,5 @@ from .status import (  # noqa: F401
     STATUS_BAD_INDEX, STATUS_BAD_COUNT, STATUS_SHORT_KV, STATUS_CURSOR,
 )
 from .metadata import prepare_seqlens  # noqa: F401
-from .append import quantize_int8, kv_cache_append  # noqa: F401
+from .append import quantize_int8, quantize_fp8_e4m3, decode_fp8_e4m3, kv_cache_append  # noqa: F401
 from .attention import attend, paged_attention, sparse_attention  # noqa: F401

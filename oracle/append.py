@@ -36,6 +36,58 @@ def quantize_int8(x, s):
     return r.astype(np.int8)
 
 
+def decode_fp8_e4m3(codes):
+    """Exact float64 values of FP8 E4M3 codes.
+
+    Reading taken: the pages name an FP8 KV cache (DynamicSparseAttention INT8 page, build
+    notes: FP8/INT4 KV cache enabled) without a format; it is taken as the OCP "E4M3FN"
+    encoding (ONNX float8e4m3fn): sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
+    subnormals ``m * 2**-9`` for exponent 0, no infinities, and the two codes 0x7F / 0xFF
+    (exponent 15, mantissa 7) are NaN.  Largest finite magnitude 448.  Scaled per channel
+    like INT8: ``value = decode(code) * scale[c][d]``.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def quantize_fp8_e4m3(x, s):
+    """FP8 E4M3 code of ``x`` with scale ``s``: the float32 quotient ``x / s`` (one IEEE
+    float32 division) rounded to the nearest E4M3 value, ties to the even mantissa;
+    magnitudes above 448 saturate to 448 (as INT8 clamps to 127); a NaN quotient gives
+    code 0 (as INT8).  Reading taken; pinned by hand-worked codes and against the library
+    float8_e4m3fn conversion in its finite range."""
+    x = np.asarray(x, dtype=np.float32)
+    s = np.asarray(s, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        q = np.divide(x, s, dtype=np.float32).astype(np.float64)
+    sign = np.where(np.signbit(q), 0x80, 0x00)
+    a = np.abs(q)
+    nan = np.isnan(a)
+    big = a > 448.0
+    a = np.where(nan | big, 0.0, a)          # the codes of these are fixed below
+    # subnormal range (below 2**-6): multiples of 2**-9, code = the multiple (8 = 2**-6)
+    sub = np.rint(a * 2.0 ** 9)
+    # normal range: a = f * 2**e with f in [1, 2); 3 mantissa bits after rounding
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    # log2 of an exact power of two is exact; guard the rounding of log2 anyway
+    e = np.where(np.exp2(e) > a, e - 1, e)
+    e = np.where(np.exp2(e + 1) <= a, e + 1, e)
+    r = np.rint(a / np.exp2(e) * 8.0)               # in [8, 16]
+    e = np.where(r == 16, e + 1, e)
+    r = np.where(r == 16, 8, r)
+    normal = ((e + 7).astype(np.int64) << 3) | (r.astype(np.int64) - 8)
+    mag = np.where(a < 2.0 ** -6, sub.astype(np.int64), normal)
+    mag = np.where(big, 0x7E, mag)
+    code = np.where(nan, 0, sign | mag)
+    return code.astype(np.uint8)
+
+
 def _check_cu(cu, B, T):
     if not (cu[0] == 0 and cu[B] == T and all(cu[b] <= cu[b + 1] for b in range(B))):
         raise ValueError("oracle: kv_cache_append / attention need a well-formed cu_seqlens_q")
@@ -72,6 +124,7 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
     int8 = kc.dtype == np.int8
+    fp8 = kc.dtype == np.uint8      # FP8 E4M3 codes
     nb = kc.shape[0]
     status = 0
     committed = None if committed_length is None else [int(x) for x in np.asarray(committed_length).reshape(-1)]
@@ -106,6 +159,9 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
             if int8:
                 kc[blk, :, off] = quantize_int8(np.asarray(k_new[r], np.float32), key_scale)
                 vc[blk, :, off] = quantize_int8(np.asarray(v_new[r], np.float32), value_scale)
+            elif fp8:
+                kc[blk, :, off] = quantize_fp8_e4m3(np.asarray(k_new[r], np.float32), key_scale)
+                vc[blk, :, off] = quantize_fp8_e4m3(np.asarray(v_new[r], np.float32), value_scale)
             else:
                 kc[blk, :, off] = k_new[r]
                 vc[blk, :, off] = v_new[r]

@@ -11,7 +11,8 @@ selection only decide which cached rows form that set.  For packed row ``r`` of 
 2. The KV head is ``c = h // (H_q / H_kv)`` (GQA head mapping, DynamicSparseAttention
    Description; H_q a multiple of H_kv as on the LinearAttention page).
 3. The key set depends on the operator (``paged_attention`` / ``sparse_attention``).
-4. INT8 cache rows are dequantised per channel: ``k[d] = code[d] * key_scale[c][d]`` and
+4. INT8 / FP8 cache rows are dequantised per channel: ``k[d] = code[d] * key_scale[c][d]``
+   (FP8 codes by their E4M3 value, ``decode_fp8_e4m3``) and
    ``v[d] = code[d] * value_scale[c][d]`` (PR 33472, Key Changes table).
 5. ``s_j = scale * <q, k_j>`` with ``scale = 1/sqrt(D)`` when 0 is passed (the
    LinearAttention page's convention for a zero scale).
@@ -28,7 +29,7 @@ import math
 
 import numpy as np
 
-from .append import _check_cu
+from .append import _check_cu, decode_fp8_e4m3
 from .status import (STATUS_BAD_BLOCK, STATUS_BAD_COUNT, STATUS_BAD_INDEX, STATUS_CAPACITY,
                      STATUS_K_BOUND, STATUS_Q_BOUND, STATUS_SHORT_KV)
 
@@ -65,6 +66,7 @@ class _Cache:
         self.bs = int(block_size) if block_table is not None else int(k.shape[2])
         self.nb = int(k.shape[0])
         self.int8 = k.dtype == np.int8
+        self.fp8 = k.dtype == np.uint8      # FP8 E4M3 codes (same per-channel scales)
         self.ks, self.vs = key_scale, value_scale
 
     def rows(self, b, c, js):
@@ -92,9 +94,13 @@ class _Cache:
             ok = in_table & good_blk
             off = js % self.bs
         blk, off = blk[ok], off[ok]
-        K = self.k[blk, c, off].astype(np.float64)
-        V = self.v[blk, c, off].astype(np.float64)
-        if self.int8:
+        if self.fp8:
+            K = decode_fp8_e4m3(self.k[blk, c, off])
+            V = decode_fp8_e4m3(self.v[blk, c, off])
+        else:
+            K = self.k[blk, c, off].astype(np.float64)
+            V = self.v[blk, c, off].astype(np.float64)
+        if self.int8 or self.fp8:
             K = K * self.ks[c].astype(np.float64)
             V = V * self.vs[c].astype(np.float64)
         return K, V, status

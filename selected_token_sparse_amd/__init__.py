@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 
-F32, F16, BF16, I8 = 0, 1, 2, 3
+F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4  # FP8: E4M3 (caches only)
 KIND_PAGED, KIND_SELECTED, KIND_LOCAL_AUX = 0, 1, 2
 
 STATUS_BAD_CU = 1 << 0
@@ -30,7 +30,8 @@ STATUS_CURSOR = 1 << 8
 _ERRORS = {-1: "null pointer", -2: "shape", -3: "dtype", -4: "unsupported", -5: "workspace too small",
            -6: "launch failed"}
 
-_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8}
+_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+           torch.float8_e4m3fn: FP8}
 
 
 class SpattnError(RuntimeError):

@@ -8,7 +8,7 @@ operators (the total key count minus one, the convention the PagedAttention meta
 uses for its worked examples), chosen together with the other lengths it draws.
 """
 from .workloads import (  # noqa: F401
-    BF16, F16, F32, I8, DTYPE_NAMES,
+    BF16, F16, F32, I8, FP8, QUANTISED, DTYPE_NAMES,
     PagedCase, SparseCase,
     paged_case, sparse_selected_case, sparse_local_aux_case,
     config_tiny_paged_decode, config_gqa_paged_decode, config_paged_prefill_window,

@@ -4,18 +4,22 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .workloads import BF16, F16, F32, I8
+from .workloads import BF16, F16, F32, FP8, I8
 
-TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, I8: torch.int8}
+TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, I8: torch.int8,
+               FP8: torch.float8_e4m3fn}
 
 
 def tensor(x, dtype: int = None, device="cuda"):
-    """numpy -> device tensor; bf16 data (carried as float32) is converted exactly."""
+    """numpy -> device tensor; bf16 data (carried as float32) is converted exactly, FP8
+    E4M3 codes (carried as uint8) are reinterpreted as float8_e4m3fn."""
     if x is None:
         return None
     t = torch.from_numpy(np.ascontiguousarray(x))
     if dtype == BF16:
         t = t.to(torch.bfloat16)
+    elif dtype == FP8:
+        t = t.view(torch.float8_e4m3fn)
     return t.to(device)
 
 

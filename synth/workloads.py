@@ -24,8 +24,10 @@ from typing import Optional
 
 import numpy as np
 
-F32, F16, BF16, I8 = 0, 1, 2, 3
-DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", I8: "i8"}
+F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", I8: "i8", FP8: "fp8"}
+QUANTISED = (I8, FP8)           # cache dtypes with per-channel key / value scales
+_FP8_FINITE = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -62,6 +64,20 @@ def _normal(rng: np.random.Generator, shape, dtype: int, chunk: int = 1 << 26) -
     return out.reshape(shape)
 
 
+def _fp8_uniform(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
+    """FP8 E4M3 codes drawn uniformly from the 254 finite ones (uint8 arrays)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = _FP8_FINITE[rng.integers(0, len(_FP8_FINITE), size=e - s)]
+    return out.reshape(shape)
+
+
+def _quantised_uniform(rng, shape, cache_dtype):
+    return _int8_uniform(rng, shape) if cache_dtype == I8 else _fp8_uniform(rng, shape)
+
+
 def _int8_uniform(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.int8)
@@ -81,7 +97,7 @@ class PagedCase:
     H_kv: int
     D: int
     dtype: int                 # Q / output / new-row dtype
-    cache_dtype: int           # equals dtype, or I8
+    cache_dtype: int           # equals dtype, or I8 / FP8
     q: np.ndarray              # [T, H_q, D]
     cu_seqlens_q: np.ndarray   # int32 [B+1]
     past_seqlens: np.ndarray   # int32 [B]
@@ -92,7 +108,7 @@ class PagedCase:
     block_size: int            # block size, or capacity for a contiguous cache
     k_new: np.ndarray          # [T, H_kv, D] rows appended by this step (dtype)
     v_new: np.ndarray
-    key_scale: Optional[np.ndarray] = None    # float32 [H_kv, D] (I8 caches)
+    key_scale: Optional[np.ndarray] = None    # float32 [H_kv, D] (I8 / FP8 caches)
     value_scale: Optional[np.ndarray] = None
     sinks: Optional[np.ndarray] = None        # float32 [H_q]
     scale: float = 0.0
@@ -221,23 +237,25 @@ def paged_case(seed: int, *, kv_lens, q_lens, H_q: int, H_kv: int, D: int,
         shape = (nblk, H_kv, bs, D)
 
     q = _normal(rng, (T, H_q, D), dtype)
-    if cache_dtype == I8:
-        k_cache = _int8_uniform(rng, shape)
-        v_cache = _int8_uniform(rng, shape)
+    if cache_dtype in QUANTISED:
+        k_cache = _quantised_uniform(rng, shape, cache_dtype)
+        v_cache = _quantised_uniform(rng, shape, cache_dtype)
     else:
         k_cache = _normal(rng, shape, cache_dtype)
         v_cache = _normal(rng, shape, cache_dtype)
     sink_arr = _draw_sinks(rng, H_q, sinks)
     key_scale = value_scale = None
-    if cache_dtype == I8:
+    if cache_dtype in QUANTISED:
         key_scale, value_scale = _draw_scales(rng, H_kv, D)
     # rows appended by this step
-    if cache_dtype == I8:
+    if cache_dtype in QUANTISED:
         # values around the representable range so quantisation hits rounding and clamping
+        # (INT8: +-127; FP8 E4M3: +-448)
+        spread = 45.0 if cache_dtype == I8 else 150.0
         k_new = _cast(rng.standard_normal((T, H_kv, D), dtype=np.float32), dtype)
         v_new = _cast(rng.standard_normal((T, H_kv, D), dtype=np.float32), dtype)
-        k_new = _cast(k_new.astype(np.float32) * (45.0 * key_scale[None]), dtype)
-        v_new = _cast(v_new.astype(np.float32) * (45.0 * value_scale[None]), dtype)
+        k_new = _cast(k_new.astype(np.float32) * (spread * key_scale[None]), dtype)
+        v_new = _cast(v_new.astype(np.float32) * (spread * value_scale[None]), dtype)
     else:
         k_new = _normal(rng, (T, H_kv, D), cache_dtype)
         v_new = _normal(rng, (T, H_kv, D), cache_dtype)
@@ -253,8 +271,9 @@ def paged_case(seed: int, *, kv_lens, q_lens, H_q: int, H_kv: int, D: int,
             for j in range(int(past[b])):
                 live[slot_of(b, j)] = True
         dead = ~live
-        k_cache.transpose(0, 2, 1, 3)[dead] = np.nan
-        v_cache.transpose(0, 2, 1, 3)[dead] = np.nan
+        bad = np.uint8(0x7F) if cache_dtype == FP8 else np.nan   # the E4M3 NaN code
+        k_cache.transpose(0, 2, 1, 3)[dead] = bad
+        v_cache.transpose(0, 2, 1, 3)[dead] = bad
 
     if max_seqlen_q is None:
         max_seqlen_q = int(q_lens.max(initial=0))
@@ -335,15 +354,15 @@ def sparse_selected_case(seed: int, *, B: int, S_q: int, H_q: int, H_kv: int, D:
         bsz = capacity
     sel = _selected_indices(rng, T, H_kv, max_selected, counts, kv_lens[row_req], oor_frac)
     q = _normal(rng, (T, H_q, D), dtype)
-    if cache_dtype == I8:
-        k_cache = _int8_uniform(rng, shape)
-        v_cache = _int8_uniform(rng, shape)
+    if cache_dtype in QUANTISED:
+        k_cache = _quantised_uniform(rng, shape, cache_dtype)
+        v_cache = _quantised_uniform(rng, shape, cache_dtype)
     else:
         k_cache = _normal(rng, shape, cache_dtype)
         v_cache = _normal(rng, shape, cache_dtype)
     sink_arr = _draw_sinks(rng, H_q, sinks)
     ks = vs = None
-    if cache_dtype == I8:
+    if cache_dtype in QUANTISED:
         ks, vs = _draw_scales(rng, H_kv, D)
     if poison and cache_dtype != I8:
         # every main-cache row no (row, kv head) of its request selects becomes NaN
@@ -358,8 +377,9 @@ def sparse_selected_case(seed: int, *, B: int, S_q: int, H_q: int, H_kv: int, D:
                     keep[b, c, js] = True
                 else:
                     keep[bt[b, js // bsz], c, js % bsz] = True
-        k_cache[~keep] = np.nan
-        v_cache[~keep] = np.nan
+        bad = np.uint8(0x7F) if cache_dtype == FP8 else np.nan   # the E4M3 NaN code
+        k_cache[~keep] = bad
+        v_cache[~keep] = bad
     return SparseCase(
         name=name, mode=0, B=B, T=T, H_q=H_q, H_kv=H_kv, D=D, dtype=dtype,
         cache_dtype=cache_dtype, q=q, cu_seqlens_q=cu,
@@ -391,9 +411,9 @@ def sparse_local_aux_case(seed: int, *, B: int, S_q: int, H_q: int, H_kv: int, D
     sel = _selected_indices(rng, T, H_kv, max_selected, counts, np.full(T, aux_len), oor_frac)
     q = _normal(rng, (T, H_q, D), dtype)
     shape = (B, H_kv, capacity, D)
-    if cache_dtype == I8:
-        k_cache = _int8_uniform(rng, shape)
-        v_cache = _int8_uniform(rng, shape)
+    if cache_dtype in QUANTISED:
+        k_cache = _quantised_uniform(rng, shape, cache_dtype)
+        v_cache = _quantised_uniform(rng, shape, cache_dtype)
     else:
         k_cache = _normal(rng, shape, cache_dtype)
         v_cache = _normal(rng, shape, cache_dtype)
@@ -402,7 +422,7 @@ def sparse_local_aux_case(seed: int, *, B: int, S_q: int, H_q: int, H_kv: int, D
     aux_v = _normal(rng, (nb_aux, aux_len, H_kv, D), aux_dtype)
     sink_arr = _draw_sinks(rng, H_q, sinks)
     ks = vs = None
-    if cache_dtype == I8:
+    if cache_dtype in QUANTISED:
         ks, vs = _draw_scales(rng, H_kv, D)
     return SparseCase(
         name=name, mode=1, B=B, T=T, H_q=H_q, H_kv=H_kv, D=D, dtype=dtype,

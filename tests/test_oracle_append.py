@@ -151,3 +151,55 @@ def test_cursor_check_skips_only_the_inconsistent_request():
             want = (_walk(case.k_cache, case.block_table, case.block_size, b, j) if b == 1
                     else _walk(ref_k, case.block_table, case.block_size, b, j))
             assert np.array_equal(got, want, equal_nan=True), (b, j)
+
+
+def test_fp8_hand_worked_codes():
+    with open(os.path.join(GOLDEN, "fp8_codes.json")) as f:
+        data = json.load(f)
+    for case in data["cases"]:
+        x = np.float32(float(case["x"]))
+        s = np.float32(float(case["s"]))
+        assert int(oracle.quantize_fp8_e4m3(x, s)) == case["code"], case["note"]
+
+
+def test_fp8_decode_matches_library_type():
+    """Every one of the 256 codes decodes as the library's float8_e4m3fn type does."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(oracle.decode_fp8_e4m3(codes), lib, equal_nan=True)
+
+
+def test_fp8_encode_matches_library_in_range_and_round_trips():
+    """Inside +-464 (where no saturation applies) the code equals the library's round-to-
+    nearest-even conversion, including every exact value and every tie; each finite code
+    round-trips."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    vals = oracle.decode_fp8_e4m3(finite)
+    assert np.array_equal(oracle.quantize_fp8_e4m3(vals.astype(np.float32), np.float32(1)), finite)
+    pos = np.unique(vals[vals > 0])
+    mids = (pos[1:] + pos[:-1]) / 2
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(50000) * 100, mids, -mids, [464.0, -464.0]]).astype(np.float32)
+    x = x[np.abs(x) <= 464]
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.quantize_fp8_e4m3(x, np.float32(1)), lib)
+
+
+def test_append_fp8_quantises_with_channel_scales():
+    case = synth.paged_case(15, kv_lens=[9, 33], q_lens=[3, 8], H_q=8, H_kv=2, D=128,
+                            block_size=16, dtype=synth.F16, cache_dtype=synth.FP8, poison=True)
+    kc, vc, st = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, case.seqlens_k,
+                                        case.k_cache, case.v_cache, case.block_table, case.block_size,
+                                        case.key_scale, case.value_scale)
+    assert st == 0
+    b, j, r = 1, 32, int(case.cu_seqlens_q[2]) - 1
+    got = oracle.decode_fp8_e4m3(_walk(kc, case.block_table, case.block_size, b, j))
+    x = case.k_new[r].astype(np.float64) / case.key_scale.astype(np.float64)
+    inside = np.abs(x) <= 448
+    # relative error of round-to-nearest with 3 mantissa bits: at most 2^-4 (normals)
+    err = np.abs(got - x)
+    assert np.all(err[inside] <= np.maximum(np.abs(x[inside]) * 2.0 ** -4, 2.0 ** -10))
+    assert np.all(np.abs(got[~inside]) == 448)

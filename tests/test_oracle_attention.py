@@ -209,11 +209,15 @@ def test_selecting_every_position_equals_paged_causal():
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
 
 
-def test_int8_equals_dequantised_float_cache():
-    case = _small_case(seed=23, dtype=synth.F16, cache_dtype=synth.I8)
+@pytest.mark.parametrize("cache_dtype", [synth.I8, synth.FP8])
+def test_quantised_equals_dequantised_float_cache(cache_dtype):
+    case = _small_case(seed=23, dtype=synth.F16, cache_dtype=cache_dtype)
     a, _ = _run_paged(case)
-    kf = case.k_cache.astype(np.float64) * case.key_scale.astype(np.float64)[None, :, None, :]
-    vf = case.v_cache.astype(np.float64) * case.value_scale.astype(np.float64)[None, :, None, :]
+    def values(codes):
+        return (codes.astype(np.float64) if cache_dtype == synth.I8
+                else oracle.decode_fp8_e4m3(codes))
+    kf = values(case.k_cache) * case.key_scale.astype(np.float64)[None, :, None, :]
+    vf = values(case.v_cache) * case.value_scale.astype(np.float64)[None, :, None, :]
     b, _ = oracle.paged_attention(case.q, kf, vf, case.cu_seqlens_q, case.seqlens_k, H_kv=case.H_kv,
                                   block_table=case.block_table, block_size=case.block_size,
                                   scale=case.scale, sinks=case.sinks)
