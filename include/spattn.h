@@ -73,6 +73,7 @@ extern "C" {
 #define SPATTN_F16 1
 #define SPATTN_BF16 2
 #define SPATTN_I8 3 /* caches only */
+#define SPATTN_FP8 4 /* caches only: FP8 E4M3 codes (OCP E4M3FN), per-channel scales as for I8 */
 
 /* return codes */
 #define SPATTN_OK 0
@@ -128,7 +129,11 @@ SPATTN_API int prepare_seqlens(const int32_t* cu_seqlens_q, const int32_t* past_
  *   Float caches: cache_dtype == new_dtype, stored unchanged.  INT8 caches
  *   (cache_dtype = SPATTN_I8, new_dtype F32/F16/BF16): code = clamp(rint_even(x / s),
  *   -127, 127) with x, s float32 and an IEEE float32 division (NaN quotient -> 0);
- *   key_scale / value_scale [H_kv, D] float32 are then required.
+ *   key_scale / value_scale [H_kv, D] float32 are then required.  FP8 caches
+ *   (SPATTN_FP8; the pages name an FP8 KV cache, its format is taken as OCP E4M3FN): x / s
+ *   rounded to the nearest E4M3 value (ties to even), magnitudes above 448 saturate to
+ *   448, NaN -> code 0; the same scales are required.  Attention reads a code as
+ *   E4M3 value * scale[c][d] (0x7F / 0xFF are NaN).
  *   Rows without a slot are skipped: p < 0 (SHORT_KV), past the capacity (CAPACITY), a
  *   block id outside [0, num_blocks) (BAD_BLOCK).
  *   committed_length [B] (optional, may be NULL): the key count the caller's cursor says

@@ -10,13 +10,14 @@ using namespace spattn;
 namespace {
 
 bool float_dtype(int t) { return t == SPATTN_F32 || t == SPATTN_F16 || t == SPATTN_BF16; }
+bool quantised_cache(int t) { return t == SPATTN_I8 || t == SPATTN_FP8; }
 
 // Shared checks of a KV cache description; returns SPATTN_OK or an error code.
 int check_cache(const void* k_cache, const void* v_cache, int dtype, int cache_dtype,
                 const int32_t* block_table, int max_blocks, int block_size, int num_blocks,
                 const float* key_scale, const float* value_scale, int B, int H_kv, int D) {
   if (k_cache == nullptr || v_cache == nullptr) return SPATTN_ERR_NULL;
-  if (cache_dtype == SPATTN_I8) {
+  if (quantised_cache(cache_dtype)) {
     if (key_scale == nullptr || value_scale == nullptr) return SPATTN_ERR_NULL;
   } else if (cache_dtype != dtype) {
     return SPATTN_ERR_DTYPE;
@@ -65,7 +66,7 @@ int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
                     const int32_t* committed_length, int32_t* status, void* stream) {
   if (B < 0 || T < 0 || H_kv < 1 || D < 8 || D % 8 != 0) return SPATTN_ERR_SHAPE;
   if (!float_dtype(new_dtype)) return SPATTN_ERR_DTYPE;
-  if (cache_dtype != SPATTN_I8 && !float_dtype(cache_dtype)) return SPATTN_ERR_DTYPE;
+  if (!quantised_cache(cache_dtype) && !float_dtype(cache_dtype)) return SPATTN_ERR_DTYPE;
   if (T == 0) return SPATTN_OK;
   if (B == 0) return SPATTN_ERR_SHAPE;
   if (k_new == nullptr || v_new == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)

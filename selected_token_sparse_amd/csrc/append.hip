@@ -22,17 +22,22 @@ __device__ __forceinline__ int8_t quantize_one(float x, float s) {
   return (int8_t)(int)r;
 }
 
-template <typename NewT>
+// Eight consecutive elements of one KV head (D is a multiple of 8) into eight codes:
+// INT8 (kFp8 = false) or FP8 E4M3 (kFp8 = true).
+template <bool kFp8, typename NewT>
 __device__ __forceinline__ void quantize8(const NewT* __restrict__ src, const float* __restrict__ scale,
                                           int8_t* __restrict__ dst) {
-  // eight consecutive elements of one KV head (D is a multiple of 8)
   union { int8_t c[8]; int2 v; } u;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) u.c[e] = quantize_one(to_f32(src[e]), scale[e]);
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (kFp8) u.c[e] = (int8_t)quantize_fp8(to_f32(src[e]), scale[e]);
+    else u.c[e] = quantize_one(to_f32(src[e]), scale[e]);
+  }
   *reinterpret_cast<int2*>(dst) = u.v;
 }
 
-template <typename NewT, bool kInt8>
+// kQuant: 0 = float cache (rows stored as they are), 1 = INT8 codes, 2 = FP8 E4M3 codes
+template <typename NewT, int kQuant>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const NewT* __restrict__ k_new, const NewT* __restrict__ v_new, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seqlens_k, int B, void* __restrict__ k_cache,
@@ -60,13 +65,13 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
   const int row_elems = cd.H_kv * cd.D;
   const int64_t src = (int64_t)r * row_elems;
   const int64_t head_stride = (int64_t)cd.block_size * cd.D;  // between heads in a block
-  if constexpr (kInt8) {
+  if constexpr (kQuant != 0) {
     int8_t* kc = reinterpret_cast<int8_t*>(k_cache) + dst;
     int8_t* vc = reinterpret_cast<int8_t*>(v_cache) + dst;
     for (int e = threadIdx.x * 8; e < row_elems; e += kAppendThreads * 8) {
       const int c = e / cd.D, d = e - c * cd.D;
-      quantize8(k_new + src + e, key_scale + e, kc + c * head_stride + d);
-      quantize8(v_new + src + e, value_scale + e, vc + c * head_stride + d);
+      quantize8<kQuant == 2>(k_new + src + e, key_scale + e, kc + c * head_stride + d);
+      quantize8<kQuant == 2>(v_new + src + e, value_scale + e, vc + c * head_stride + d);
     }
   } else {
     constexpr int kPer = 16 / sizeof(NewT);
@@ -97,18 +102,23 @@ int launch_kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
   cd.H_kv = H_kv;
   cd.D = D;
   dim3 grid(T), block(kAppendThreads);
-  const bool i8 = cache_dtype == SPATTN_I8;
-#define SPATTN_APPEND(NT, I8)                                                              \
-  hipLaunchKernelGGL((kv_append_kernel<NT, I8>), grid, block, 0, stream,                   \
+  const int quant = cache_dtype == SPATTN_I8 ? 1 : (cache_dtype == SPATTN_FP8 ? 2 : 0);
+#define SPATTN_APPEND(NT, Q)                                                               \
+  hipLaunchKernelGGL((kv_append_kernel<NT, Q>), grid, block, 0, stream,                    \
                      reinterpret_cast<const NT*>(k_new), reinterpret_cast<const NT*>(v_new), \
                      cu, seqlens_k, B, k_cache, v_cache, cd, key_scale, value_scale, committed, \
                      status)
+#define SPATTN_APPEND_Q(NT)                         \
+  if (quant == 1) SPATTN_APPEND(NT, 1);             \
+  else if (quant == 2) SPATTN_APPEND(NT, 2);        \
+  else SPATTN_APPEND(NT, 0)
   switch (new_dtype) {
-    case SPATTN_F32: if (i8) SPATTN_APPEND(float, true); else SPATTN_APPEND(float, false); break;
-    case SPATTN_F16: if (i8) SPATTN_APPEND(f16, true); else SPATTN_APPEND(f16, false); break;
-    case SPATTN_BF16: if (i8) SPATTN_APPEND(bf16, true); else SPATTN_APPEND(bf16, false); break;
+    case SPATTN_F32: SPATTN_APPEND_Q(float); break;
+    case SPATTN_F16: SPATTN_APPEND_Q(f16); break;
+    case SPATTN_BF16: SPATTN_APPEND_Q(bf16); break;
     default: return SPATTN_ERR_DTYPE;
   }
+#undef SPATTN_APPEND_Q
 #undef SPATTN_APPEND
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_ERR_LAUNCH;
 }

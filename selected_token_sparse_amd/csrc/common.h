@@ -38,6 +38,47 @@ __device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(int8_t x) { return (float)x; }
 
+// ---------------------------------------------------------------------------------------
+// FP8 E4M3 cache codes (OCP "E4M3FN": sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// subnormals m * 2^-9, no infinities, 0x7F / 0xFF NaN).  Caches of this type are uint8_t
+// arrays of codes.  Moving the sign to bit 15 and the 7 magnitude bits up by 7 gives the
+// f16 whose value is exactly the code's value / 256 (f16 has the wider exponent and
+// mantissa, subnormals included), so kernels fold the factor 256 into the per-channel
+// scales.
+// ---------------------------------------------------------------------------------------
+constexpr float kFp8Unit = 256.0f;   // code value = f16 operand value * kFp8Unit
+
+__device__ __forceinline__ uint16_t fp8_to_f16_bits(uint32_t b) {
+  const uint32_t mag = b & 0x7Fu;
+  return (uint16_t)(((b & 0x80u) << 8) | (mag << 7) | (mag == 0x7Fu ? 0x7C00u : 0u));
+}
+// Exact value of a code (NaN codes give NaN).
+__device__ __forceinline__ float to_f32(uint8_t code) {
+  return (float)__builtin_bit_cast(f16, fp8_to_f16_bits(code)) * kFp8Unit;
+}
+// Code of x / s: one IEEE float32 division, rounded to the nearest E4M3 value with ties to
+// the even mantissa; magnitudes above 448 saturate to 448; a NaN quotient gives code 0.
+__device__ __forceinline__ uint8_t quantize_fp8(float x, float s) {
+  const float q = x / s;
+  if (q != q) return 0;
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  if (a > 448.0f) return (uint8_t)(sign | 0x7Eu);
+  uint32_t mag;
+  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9 (8 = 2^-6)
+    mag = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    int e = (int)(bits >> 23) - 127;
+    uint32_t r = (bits >> 20) & 7u;
+    const uint32_t rest = bits & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (r & 1u))) ++r;
+    if (r == 8u) { r = 0; ++e; }
+    mag = ((uint32_t)(e + 7) << 3) | r;
+  }
+  return (uint8_t)(sign | mag);
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }

@@ -26,8 +26,8 @@
 //     last-arriving workgroup instead needs an agent-scope release per workgroup, which on
 //     this chip writes back the L2 and measured several times slower.)
 //
-// INT8 caches: key_scale is folded into the query operand (f16), value_scale is applied
-// to the accumulator before it leaves the workgroup.
+// INT8 and FP8 E4M3 caches: key_scale is folded into the query operand (f16), value_scale
+// is applied to the accumulator before it leaves the workgroup.
 #include <type_traits>
 
 #include "common.h"
@@ -62,13 +62,21 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// 8 cache elements at `p` as an MFMA operand of type OpT (int8 codes convert exactly).
+// 8 cache elements at `p` as an MFMA operand of type OpT (int8 codes convert exactly; FP8
+// E4M3 codes, uint8_t, become f16 holding their value / kFp8Unit, also exactly).
 template <typename OpT, typename KT>
 __device__ __forceinline__ typename OpVec<OpT>::v8 load_op8(const KT* p) {
   typedef typename OpVec<OpT>::v8 V8;
   if constexpr (sizeof(KT) == 2) {
     i32x4 raw = load16(p);
     return __builtin_bit_cast(V8, raw);
+  } else if constexpr (std::is_same<KT, uint8_t>::value) {
+    int2 raw = *reinterpret_cast<const int2*>(p);
+    const uint8_t* c = reinterpret_cast<const uint8_t*>(&raw);
+    V8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(f16, fp8_to_f16_bits(c[e]));
+    return v;
   } else {
     int2 raw = *reinterpret_cast<const int2*>(p);
     const int8_t* c = reinterpret_cast<const int8_t*>(&raw);
@@ -185,7 +193,7 @@ __device__ __forceinline__ void issue_tile(TileRegs<OpT, KT, D>& t, const KT* __
 // Softmax update and both products for a tile whose loads have completed.
 template <typename OpT, typename KT, int D>
 __device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t valid,
-                                             const typename OpVec<OpT>::v8 (&qop)[D / 32],
+                                             const typename OpVec<OpT>::v8 (&qop)[2][D / 32],
                                              float scale_log2, unsigned char* vbuf, float& m_run,
                                              float& l_run, f32x4 (&acc)[D / 16], int lam, int grp) {
   typedef typename OpVec<OpT>::v8 V8;
@@ -208,7 +216,11 @@ __device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t v
   for (int st = 0; st < 2; ++st) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) c = mfma16(t.k[st][kc], qop[kc], c);
+    for (int kc = 0; kc < KC; ++kc) {
+      c = mfma16(t.k[st][kc], qop[0][kc], c);
+      // quantised caches: the low half of the folded query (see the query set-up)
+      if constexpr (sizeof(KT) == 1) c = mfma16(t.k[st][kc], qop[1][kc], c);
+    }
     s[st] = c;
   }
   float mt = kNegInf;
@@ -281,7 +293,7 @@ __device__ __forceinline__ uint32_t tile_valid(int row0, int row1) {
 template <typename OpT, typename KT, int D>
 __device__ __forceinline__ void wave_keys(const KT* __restrict__ kbase, const KT* __restrict__ vbase,
                                           const KT* dk, const KT* dv, const int32_t* rows, int n_keys,
-                                          const typename OpVec<OpT>::v8 (&qop)[D / 32],
+                                          const typename OpVec<OpT>::v8 (&qop)[2][D / 32],
                                           float scale_log2, unsigned char* vbuf2, float& m_run,
                                           float& l_run, f32x4 (&acc)[D / 16]) {
   constexpr int kTileBytes = (D / 32) * 2 * 1024;
@@ -383,12 +395,22 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
   return -1;
 }
 
-// Occupancy hint for D = 64: with two tiles in flight per wave, 5 waves per SIMD (the
-// register budget of that occupancy holds both tiles' K operands without spilling).
+// Occupancy hint for D = 64, where each wave keeps two tiles in flight: 5 waves per SIMD
+// for 16-bit caches (that register budget holds both tiles' K operands without spilling);
+// 4 when the kernel also carries the second (window) source; 3 for quantised caches, whose
+// tiles also hold the raw codes and whose query has a second (low) operand.
+template <int KIND, typename KT, int D>
+constexpr int split_waves_per_eu() {
+  return D != 64 ? 1 : sizeof(KT) == 1 ? 3 : KIND == SPATTN_KIND_LOCAL_AUX ? 4 : 5;
+}
+
 template <int KIND, typename QT, typename KT, typename AT, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 1, 8)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(split_waves_per_eu<KIND, KT, D>(), 8)))
 void split_attn_kernel(SplitParams P) {
   typedef typename std::conditional<sizeof(KT) == 1, f16, KT>::type OpM;  // main operand
+  // FP8 operands hold code values / kFp8Unit; the factor rides on the scales
+  constexpr float kUnit = std::is_same<KT, uint8_t>::value ? kFp8Unit : 1.0f;
   typedef QT OpA;                                                          // aux operand
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* area = smem;
@@ -463,17 +485,27 @@ void split_attn_kernel(SplitParams P) {
   const bool use_scale = sizeof(KT) == 1 && sr.src != SRC_AUX;
   if (sr.n_keys > 0) {
     if (KIND != SPATTN_KIND_LOCAL_AUX || sr.src != SRC_AUX) {
-      typename OpVec<OpM>::v8 qop[D / 32];
+      // Quantised caches fold the per-channel key scale into the query.  The folded value
+      // x = q * s is carried as hi + lo, two 16-bit operands (hi = x rounded, lo = the
+      // rounding error rounded), and S takes one product with each, so the scores keep
+      // about 22 bits of x instead of 11: a single 16-bit operand would put a relative
+      // error of 2^-11 on every term q_d k_d, i.e. score errors up to 2^-11 sum_d |q_d k_d|.
+      typename OpVec<OpM>::v8 qop[2][D / 32];
 #pragma unroll
       for (int kc = 0; kc < D / 32; ++kc) {
         const int col = kc * 32 + grp * 8;
         if constexpr (sizeof(KT) == 1) {
           const typename OpVec<QT>::v8 qv = __builtin_bit_cast(typename OpVec<QT>::v8, qraw[kc]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            qop[kc][e] = (OpM)(hv ? to_f32((QT)qv[e]) * P.key_scale[c * D + col + e] : 0.f);
+          for (int e = 0; e < 8; ++e) {
+            const float x = hv ? to_f32((QT)qv[e]) * (P.key_scale[c * D + col + e] * kUnit) : 0.f;
+            const OpM hi = (OpM)x;
+            qop[0][kc][e] = hi;
+            qop[1][kc][e] = (OpM)(x - (float)hi);
+          }
         } else {
-          qop[kc] = __builtin_bit_cast(typename OpVec<OpM>::v8, qraw[kc]);
+          qop[0][kc] = __builtin_bit_cast(typename OpVec<OpM>::v8, qraw[kc]);
+          qop[1][kc] = typename OpVec<OpM>::v8{};
         }
       }
       // masked keys read row 0 of the cache for K and, with 16-bit caches, the query row of
@@ -486,9 +518,12 @@ void split_attn_kernel(SplitParams P) {
                             reinterpret_cast<const KT*>(P.k_cache), dv, rows, sr.n_keys, qop,
                             P.scale_log2, area + wave * SplitLds<D>::kVTileBytes, m_run, l_run, acc);
     } else if constexpr (sizeof(AT) == 2) {
-      typename OpVec<OpA>::v8 qop[D / 32];
+      typename OpVec<OpA>::v8 qop[2][D / 32];
 #pragma unroll
-      for (int kc = 0; kc < D / 32; ++kc) qop[kc] = __builtin_bit_cast(typename OpVec<OpA>::v8, qraw[kc]);
+      for (int kc = 0; kc < D / 32; ++kc) {
+        qop[0][kc] = __builtin_bit_cast(typename OpVec<OpA>::v8, qraw[kc]);
+        qop[1][kc] = typename OpVec<OpA>::v8{};
+      }
       wave_keys<OpA, AT, D>(reinterpret_cast<const AT*>(P.aux_k),
                             reinterpret_cast<const AT*>(P.aux_v),
                             reinterpret_cast<const AT*>(q0row), reinterpret_cast<const AT*>(q0row),
@@ -525,7 +560,7 @@ void split_attn_kernel(SplitParams P) {
         L += cl[w * 16 + h] * f;
         A += ca[(w * 16 + h) * D + d] * f;
       }
-      if (use_scale) A *= P.value_scale[c * D + d];
+      if (use_scale) A *= P.value_scale[c * D + d] * kUnit;
     }
     const int head = h0 + h;
     const int64_t o = ((int64_t)r * P.H_q + head) * D + d;
@@ -805,12 +840,16 @@ static void launch_split_f32(const SplitParams& P, bool direct, hipStream_t stre
 
 template <int KIND, typename QT, int D>
 static void dispatch_cache(const AttnArgs& a, const SplitParams& P, bool direct, hipStream_t stream) {
+  // INT8 caches are int8_t, FP8 E4M3 caches uint8_t
   const bool i8 = a.cache_dtype == SPATTN_I8;
+  const bool fp8 = a.cache_dtype == SPATTN_FP8;
   if constexpr (std::is_same<QT, float>::value) {
     if (i8) launch_split_f32<KIND, int8_t, float, D>(P, direct, stream);
+    else if (fp8) launch_split_f32<KIND, uint8_t, float, D>(P, direct, stream);
     else launch_split_f32<KIND, float, float, D>(P, direct, stream);
   } else {
     if (i8) launch_split_typed<KIND, QT, int8_t, QT, D>(P, stream);
+    else if (fp8) launch_split_typed<KIND, QT, uint8_t, QT, D>(P, stream);
     else launch_split_typed<KIND, QT, QT, QT, D>(P, stream);
   }
 }

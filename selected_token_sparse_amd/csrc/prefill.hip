@@ -86,16 +86,24 @@ __device__ __forceinline__ void pf_wait_vm() {
 __device__ __forceinline__ void pf_wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // 4 waves per SIMD at D = 64 (128 registers: both tile buffers, the accumulators and the
-// query operand fit), 2 at D = 128.
+// query operand fit), 3 at D = 64 with a quantised cache (the query's low operand needs
+// 16 more registers), 2 at D = 128.
+template <typename KT, int D>
+constexpr int prefill_waves_per_eu() { return D != 64 ? 2 : sizeof(KT) == 1 ? 3 : 4; }
+
 template <typename QT, typename KT, int D, int RW>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, 8)))
+__global__ __launch_bounds__(kPfThreads)
+__attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<KT, D>(), 8)))
 void prefill_kernel(PrefillParams P) {
   constexpr int HW = 4 / RW;
   constexpr int KC = D / 16;          // QK k-steps
   constexpr int MT = D / 32;          // PV m-tiles
   constexpr int CH = D / 8;           // 8-element chunks per row
   constexpr int NCH = kPfTile * CH / kPfThreads;
-  constexpr bool kI8 = sizeof(KT) == 1;
+  constexpr bool kI8 = sizeof(KT) == 1;                       // INT8 or FP8 E4M3 codes
+  constexpr bool kFp8 = std::is_same<KT, uint8_t>::value;
+  // FP8 operands hold code values / kFp8Unit; the factor rides on the scales
+  constexpr float kUnit = kFp8 ? kFp8Unit : 1.0f;
   constexpr bool kDma = !kI8;
   typedef PfLds<D, kDma> L;
   constexpr int CHK = D / 8;          // 16-byte chunks per K/V row
@@ -189,7 +197,12 @@ void prefill_kernel(PrefillParams P) {
   // the exponent, so a negative scale is folded into the query's sign.
   const float c_scale = fabsf(P.scale_log2);
   const bool q_neg = P.scale_log2 < 0.f;
+  // Quantised caches fold the per-channel key scale into the query and carry the folded
+  // value x = q * s as hi + lo (hi = x rounded to the operand type, lo = its rounding error
+  // rounded); S takes one product with each, so the scores keep about 22 bits of x.  With
+  // hi alone every term q_d k_d would carry a relative error up to 2^-11.
   V8 qop[KC];
+  V8 qlo[kI8 ? KC : 1];
   {
     const QT* qr = reinterpret_cast<const QT*>(P.q) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
 #pragma unroll
@@ -198,15 +211,23 @@ void prefill_kernel(PrefillParams P) {
       if (row_ok) {
         if constexpr (kI8) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            qop[kc][e] = (OpT)(to_f32(qr[col + e]) * P.key_scale[c * D + col + e]);
+          for (int e = 0; e < 8; ++e) {
+            const float x = to_f32(qr[col + e]) * (P.key_scale[c * D + col + e] * kUnit);
+            const OpT hi = (OpT)x;
+            qop[kc][e] = hi;
+            qlo[kc][e] = (OpT)(x - (float)hi);
+          }
         } else {
           qop[kc] = __builtin_bit_cast(V8, load16(qr + col));
         }
       } else {
         qop[kc] = V8{};
+        if constexpr (kI8) qlo[kc] = V8{};
       }
-      if (q_neg) qop[kc] = -qop[kc];
+      if (q_neg) {
+        qop[kc] = -qop[kc];
+        if constexpr (kI8) qlo[kc] = -qlo[kc];
+      }
     }
   }
 
@@ -342,7 +363,15 @@ void prefill_kernel(PrefillParams P) {
       const int qi = tid + n * kPfThreads;
       const int key = qi / CH, col = (qi % CH) * 8;
       V8 kv, vv;
-      if constexpr (kI8) {
+      if constexpr (kFp8) {
+        const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(&tr.k[n]);
+        const uint8_t* vc8 = reinterpret_cast<const uint8_t*>(&tr.v[n]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kv[e] = __builtin_bit_cast(f16, fp8_to_f16_bits(kc8[e]));
+          vv[e] = __builtin_bit_cast(f16, fp8_to_f16_bits(vc8[e]));
+        }
+      } else if constexpr (kI8) {
         const int8_t* kc8 = reinterpret_cast<const int8_t*>(&tr.k[n]);
         const int8_t* vc8 = reinterpret_cast<const int8_t*>(&tr.v[n]);
 #pragma unroll
@@ -350,6 +379,11 @@ void prefill_kernel(PrefillParams P) {
       } else {
         kv = __builtin_bit_cast(V8, tr.k[n]);
         vv = __builtin_bit_cast(V8, tr.v[n]);
+      }
+      if constexpr (kI8) {
+        // a missing key read the cache's first row, whose FP8 codes may be NaN: its weight
+        // is 0, so its row must be finite
+        if (!tr.ok[n]) { kv = V8{}; vv = V8{}; }
       }
       *reinterpret_cast<V8*>(kl + key * L::kKld + col) = kv;
       *reinterpret_cast<V8*>(vl + key * L::kVld + col) = vv;
@@ -387,6 +421,7 @@ void prefill_kernel(PrefillParams P) {
         V8 a = *reinterpret_cast<const V8*>(reinterpret_cast<const unsigned char*>(kl) +
                                             k_chunk(l32, 2 * kc + h));
         s = mfma32(a, qop[kc], s);
+        if constexpr (kI8) s = mfma32(a, qlo[kc], s);
       }
       // lane holds keys 8*(i/4) + 4*h + i%4 of row l32.  Masks only on tiles some row of the
       // wave does not fully see (the diagonal, the window edge, missing keys).
@@ -534,7 +569,7 @@ void prefill_kernel(PrefillParams P) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x = acc[m][4 * g4 + e] * inv;
-          if constexpr (kI8) x *= P.value_scale[c * D + d0 + e];
+          if constexpr (kI8) x *= P.value_scale[c * D + d0 + e] * kUnit;
           w[e] = from_f32<QT>(x);
         }
         *reinterpret_cast<typename Op32<QT>::v4*>(o + d0) = w;
@@ -585,14 +620,19 @@ int launch_prefill_attention(const AttnArgs& a, hipStream_t stream) {
   if (total > 0x7fffffffL) return SPATTN_ERR_SHAPE;
   P.total = (int)total;
   P.xcd_pairs = (a.B * a.H_kv) % 8 == 0 ? 1 : 0;
+  // INT8 caches are int8_t, FP8 E4M3 caches uint8_t
   const bool i8 = a.cache_dtype == SPATTN_I8;
+  const bool fp8 = a.cache_dtype == SPATTN_FP8;
+#define SPATTN_PREFILL(QT, DD)                                                            \
+  if (i8) launch_prefill_typed<QT, int8_t, DD>(P, RW, stream);                            \
+  else if (fp8) launch_prefill_typed<QT, uint8_t, DD>(P, RW, stream);                     \
+  else launch_prefill_typed<QT, QT, DD>(P, RW, stream)
   if (a.D == 64) {
-    if (a.dtype == SPATTN_F16) { if (i8) launch_prefill_typed<f16, int8_t, 64>(P, RW, stream); else launch_prefill_typed<f16, f16, 64>(P, RW, stream); }
-    else { if (i8) launch_prefill_typed<bf16, int8_t, 64>(P, RW, stream); else launch_prefill_typed<bf16, bf16, 64>(P, RW, stream); }
+    if (a.dtype == SPATTN_F16) { SPATTN_PREFILL(f16, 64); } else { SPATTN_PREFILL(bf16, 64); }
   } else {
-    if (a.dtype == SPATTN_F16) { if (i8) launch_prefill_typed<f16, int8_t, 128>(P, RW, stream); else launch_prefill_typed<f16, f16, 128>(P, RW, stream); }
-    else { if (i8) launch_prefill_typed<bf16, int8_t, 128>(P, RW, stream); else launch_prefill_typed<bf16, bf16, 128>(P, RW, stream); }
+    if (a.dtype == SPATTN_F16) { SPATTN_PREFILL(f16, 128); } else { SPATTN_PREFILL(bf16, 128); }
   }
+#undef SPATTN_PREFILL
   return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_ERR_LAUNCH;
 }
 

@@ -27,7 +27,6 @@ import numpy as np
 F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4
 DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", I8: "i8", FP8: "fp8"}
 QUANTISED = (I8, FP8)           # cache dtypes with per-channel key / value scales
-_FP8_FINITE = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -65,12 +64,20 @@ def _normal(rng: np.random.Generator, shape, dtype: int, chunk: int = 1 << 26) -
 
 
 def _fp8_uniform(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
-    """FP8 E4M3 codes drawn uniformly from the 254 finite ones (uint8 arrays)."""
+    """FP8 E4M3 codes (uint8 arrays) shaped like scaled activations: random sign, uniform
+    3-bit mantissa, exponent field round(N(7, 1.5)) clipped to [0, 15] (values of order 1
+    with tails towards 2^-6 and 448), never the NaN code (exponent 15 with mantissa 7
+    becomes mantissa 6)."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint8)
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
-        out[s:e] = _FP8_FINITE[rng.integers(0, len(_FP8_FINITE), size=e - s)]
+        m = e - s
+        exp = np.clip(np.rint(rng.normal(7.0, 1.5, size=m)), 0, 15).astype(np.uint8)
+        man = rng.integers(0, 8, size=m, dtype=np.uint8)
+        man = np.where((exp == 15) & (man == 7), np.uint8(6), man)
+        sign = rng.integers(0, 2, size=m, dtype=np.uint8) << 7
+        out[s:e] = sign | (exp << 3) | man
     return out.reshape(shape)
 
 

@@ -24,6 +24,16 @@ TOL = {
 BF16_WEIGHT_ROUNDING = 2.0 ** -8
 
 
+def abs_values(v):
+    """|V| of a cache array: FP8 E4M3 codes (uint8) by clearing the sign bit (NaN codes stay
+    NaN), other arrays by their absolute value."""
+    if v is None:
+        return None
+    if v.dtype == np.uint8:
+        return (v & np.uint8(0x7F)).astype(np.uint8)
+    return np.abs(v)
+
+
 def assert_close(gpu: torch.Tensor, ref: np.ndarray, dtype: int, what: str = "", mag=None):
     g = gpu.detach().float().cpu().numpy().astype(np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
@@ -88,7 +98,7 @@ def oracle_paged_step(case, rows=None, append=True):
     out, st2 = oracle.paged_attention(case.q, kc, vc, case.cu_seqlens_q, sk, **kw)
     mag = None
     if case.dtype == synth.BF16:
-        mag, _ = oracle.paged_attention(case.q, kc, np.abs(vc), case.cu_seqlens_q, sk, **kw)
+        mag, _ = oracle.paged_attention(case.q, kc, abs_values(vc), case.cu_seqlens_q, sk, **kw)
     return out, st0 | st1 | st2, mag
 
 
@@ -120,5 +130,5 @@ def oracle_sparse(case, rows=None):
     out, st = run(case.v_cache, case.aux_v)
     mag = None
     if case.dtype == synth.BF16:
-        mag, _ = run(np.abs(case.v_cache), None if case.aux_v is None else np.abs(case.aux_v))
+        mag, _ = run(abs_values(case.v_cache), abs_values(case.aux_v))
     return out, st, mag

@@ -89,7 +89,16 @@ APPEND_CASES = [
     dict(name="paged_i8_from_f16", kv_lens=[9, 33, 3], q_lens=[3, 8, 3], dtype=synth.F16, cache_dtype=synth.I8, D=128),
     dict(name="paged_i8_from_bf16", kv_lens=[20], q_lens=[20], dtype=synth.BF16, cache_dtype=synth.I8),
     dict(name="contig_i8_from_f32", kv_lens=[16, 4], q_lens=[16, 4], dtype=synth.F32, cache_dtype=synth.I8, contiguous=True, capacity=16),
+    dict(name="paged_fp8_from_f16", kv_lens=[5, 0, 40, 17], q_lens=[2, 0, 40, 1], dtype=synth.F16, cache_dtype=synth.FP8, D=128),
+    dict(name="paged_fp8_from_bf16", kv_lens=[20], q_lens=[20], dtype=synth.BF16, cache_dtype=synth.FP8),
+    dict(name="contig_fp8_from_f32", kv_lens=[16, 4], q_lens=[16, 4], dtype=synth.F32, cache_dtype=synth.FP8, contiguous=True, capacity=16),
 ]
+
+
+def _bits(t):
+    """Raw bits of a tensor, for bit-exact comparison of any element type."""
+    n = t.element_size()
+    return t.view(torch.uint8 if n == 1 else torch.int16 if n == 2 else torch.int32)
 
 
 @pytest.mark.parametrize("spec", APPEND_CASES, ids=[c["name"] for c in APPEND_CASES])
@@ -110,8 +119,7 @@ def test_append_bit_exact(spec):
     for got, want in ((t["k_cache"], kc), (t["v_cache"], vc)):
         g = got.cpu()
         w = tensor(want, case.cache_dtype, "cpu")
-        assert torch.equal(g.view(torch.int8) if g.dtype == torch.int8 else g.view(torch.int16) if g.element_size() == 2 else g.view(torch.int32),
-                           w.view(torch.int8) if w.dtype == torch.int8 else w.view(torch.int16) if w.element_size() == 2 else w.view(torch.int32))
+        assert torch.equal(_bits(g), _bits(w))
     assert int(st.item()) == ost
 
 
@@ -198,3 +206,28 @@ def test_append_cursor_check_bit_exact(contiguous):
     assert int(st.item()) == ost == oracle.STATUS_CURSOR
     assert np.array_equal(t["k_cache"].cpu().numpy().view(np.uint16), kc.view(np.uint16))
     assert np.array_equal(t["v_cache"].cpu().numpy().view(np.uint16), vc.view(np.uint16))
+
+
+def test_append_fp8_hand_worked_codes():
+    # the hand-worked FP8 E4M3 codes through the device quantiser, eight per row
+    with open(os.path.join(GOLDEN, "fp8_codes.json")) as f:
+        cases = json.load(f)["cases"]
+    D = 8 * ((len(cases) + 7) // 8)
+    x = np.zeros((1, 1, D), dtype=np.float32)
+    s = np.ones((1, D), dtype=np.float32)
+    want = np.zeros(D, dtype=np.uint8)
+    for i, c in enumerate(cases):
+        x[0, 0, i] = np.float32(float(c["x"]))
+        s[0, i] = np.float32(float(c["s"]))
+        want[i] = c["code"]
+    print("append fp8 hand-worked codes", flush=True)
+    cu = tensor(np.array([0, 1], dtype=np.int32), None)
+    sk = tensor(np.array([0], dtype=np.int32), None)
+    kc = torch.zeros((1, 1, 1, D), dtype=torch.float8_e4m3fn, device="cuda")
+    vc = torch.zeros_like(kc)
+    xt = tensor(x, None)
+    st_ = tensor(s, None)
+    sta.kv_cache_append(xt, xt, cu, sk, kc, vc, None, st_, st_)
+    torch.cuda.synchronize()
+    got = kc.cpu().view(torch.uint8).numpy().reshape(-1)
+    assert got[:len(cases)].tolist() == want[:len(cases)].tolist()

@@ -51,6 +51,10 @@ DECODE = [
     ("f32_i8_cache", dict(kv_lens=[45], q_lens=[2], H_q=4, H_kv=2, D=64, dtype=synth.F32, cache_dtype=synth.I8)),
     ("f16_contig", dict(kv_lens=[120, 7, 64], q_lens=[1, 1, 1], H_q=8, H_kv=1, D=64, dtype=synth.F16, contiguous=True, capacity=128, sinks=True)),
     ("f16_long_splits", dict(kv_lens=[8192, 4000, 1], q_lens=[1, 1, 1], H_q=64, H_kv=8, D=64, dtype=synth.F16, sinks=True)),
+    ("f16_fp8_cache", dict(kv_lens=[70, 260], q_lens=[1, 3], H_q=12, H_kv=1, D=128, dtype=synth.F16, cache_dtype=synth.FP8, sinks=True)),
+    ("bf16_fp8_cache_w9", dict(kv_lens=[70, 33], q_lens=[2, 1], H_q=8, H_kv=2, D=64, dtype=synth.BF16, cache_dtype=synth.FP8, local_window=9)),
+    ("f32_fp8_cache", dict(kv_lens=[45, 130], q_lens=[2, 1], H_q=4, H_kv=2, D=64, dtype=synth.F32, cache_dtype=synth.FP8, sinks=True)),
+    ("f16_fp8_contig_long", dict(kv_lens=[3000, 9], q_lens=[1, 1], H_q=16, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.FP8, contiguous=True, capacity=3000, sinks=True)),
 ]
 
 
@@ -72,6 +76,8 @@ PREFILL = [
     ("f16_w1", dict(kv_lens=[40], q_lens=[40], H_q=8, H_kv=2, D=64, dtype=synth.F16, local_window=1)),
     ("f16_bs5", dict(kv_lens=[61, 20], q_lens=[61, 12], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=5, sinks=True)),
     ("f16_empty_mixed", dict(kv_lens=[0, 50, 0, 9], q_lens=[0, 50, 0, 9], H_q=8, H_kv=2, D=64, dtype=synth.F16, sinks=True)),
+    ("f16_fp8_prefill", dict(kv_lens=[90, 40], q_lens=[90, 20], H_q=8, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.FP8, sinks=True)),
+    ("bf16_fp8_prefill_d128_w20", dict(kv_lens=[120], q_lens=[70], H_q=8, H_kv=2, D=128, dtype=synth.BF16, cache_dtype=synth.FP8, local_window=20)),
     # a key range of more than 512 blocks (block size 4): block ids read from the table in
     # global memory instead of the staged copy
     ("f16_bs4_long_table", dict(kv_lens=[2100, 70], q_lens=[40, 70], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=4, sinks=True)),

@@ -34,6 +34,7 @@ SELECTED = [
     ("bf16_g4_d64", dict(B=2, S_q=3, H_q=8, H_kv=2, D=64, capacity=500, max_selected=64, dtype=synth.BF16, sinks=True, oor_frac=0.1)),
     ("f16_nocount", dict(B=2, S_q=2, H_q=8, H_kv=2, D=64, capacity=400, max_selected=40, dtype=synth.F16, sinks=True, pass_count=False)),
     ("f16_i8_main", dict(B=2, S_q=4, H_q=12, H_kv=1, D=128, capacity=900, max_selected=200, dtype=synth.F16, cache_dtype=synth.I8, sinks=True, oor_frac=0.02)),
+    ("f16_fp8_main", dict(B=2, S_q=4, H_q=12, H_kv=1, D=128, capacity=900, max_selected=200, dtype=synth.F16, cache_dtype=synth.FP8, sinks=True, oor_frac=0.02)),
     ("f32_g3", dict(B=2, S_q=2, H_q=6, H_kv=2, D=64, capacity=300, max_selected=50, dtype=synth.F32, sinks=True, oor_frac=0.05)),
     ("f16_paged_main", dict(B=3, S_q=2, H_q=16, H_kv=2, D=64, capacity=600, kv_lens=[600, 250, 17], max_selected=128, dtype=synth.F16, sinks=True, block_size=16, oor_frac=0.03)),
     ("f16_g20_two_tiles", dict(B=1, S_q=2, H_q=40, H_kv=2, D=64, capacity=300, max_selected=90, dtype=synth.F16, sinks=True)),
@@ -61,6 +62,8 @@ LOCAL_AUX = [
     ("f16_main_shared_aux", dict(B=3, S_q=2, H_q=8, H_kv=2, D=64, capacity=300, kv_lens=[300, 100, 5], local_window=20, aux_len=90, n_selected=30, max_selected=40, dtype=synth.F16, cache_dtype=synth.F16, shared_aux=True)),
     ("bf16_i8_main", dict(B=2, S_q=4, H_q=8, H_kv=2, D=64, capacity=200, local_window=7, aux_len=50, n_selected=9, max_selected=16, dtype=synth.BF16, cache_dtype=synth.I8, oor_frac=0.1)),
     ("f32_i8_main", dict(B=1, S_q=3, H_q=4, H_kv=1, D=64, capacity=64, local_window=10, aux_len=40, n_selected=12, dtype=synth.F32, cache_dtype=synth.I8)),
+    ("fp8_main_f16_aux", dict(B=2, S_q=8, H_q=24, H_kv=2, D=128, capacity=700, local_window=128, aux_len=600, n_selected=100, dtype=synth.F16, cache_dtype=synth.FP8)),
+    ("bf16_fp8_main", dict(B=2, S_q=4, H_q=8, H_kv=2, D=64, capacity=200, local_window=7, aux_len=50, n_selected=9, max_selected=16, dtype=synth.BF16, cache_dtype=synth.FP8, oor_frac=0.1)),
     ("f16_long_window", dict(B=1, S_q=2, H_q=12, H_kv=1, D=128, capacity=1000, local_window=600, aux_len=700, n_selected=500, max_selected=520, dtype=synth.F16, cache_dtype=synth.F16)),
 ]
 
