@@ -1,7 +1,8 @@
-"""Pins of the oracle's cache append and INT8 code (CPU only).
+"""Pins of the oracle's cache append, INT8 code and FP8 E4M3 code (CPU only).
 
-Against: hand-worked INT8 codes (golden fixture), the closed-form quantisation error
-bound, and the logical key sequence the inputs were laid out from (read back through
+Against: hand-worked INT8 and FP8 codes (golden fixtures), the closed-form quantisation
+error bounds, the library's float8_e4m3fn conversion, the cursor example of the pages'
+review, and the logical key sequence the inputs were laid out from (read back through
 the block table by this test's own walk).
 """
 import json
@@ -186,6 +187,26 @@ def test_fp8_encode_matches_library_in_range_and_round_trips():
     x = x[np.abs(x) <= 464]
     lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(oracle.quantize_fp8_e4m3(x, np.float32(1)), lib)
+
+
+def test_fp8_error_bound_and_saturation():
+    """E4M3 keeps 3 mantissa bits: for |x/s| in the normal range [2^-6, 448] the decoded
+    code is within 2^-4 of x/s relatively (half a step of 2^-3), in the subnormal range
+    within 2^-10 absolutely (half the 2^-9 spacing); beyond 448 the code saturates."""
+    rng = np.random.default_rng(8)
+    s = rng.uniform(0.005, 0.02, size=20000).astype(np.float32)
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), size=20000))
+    q = mag * rng.choice([-1.0, 1.0], size=20000)
+    x = (q * s).astype(np.float32)
+    code = oracle.quantize_fp8_e4m3(x, s)
+    got = oracle.decode_fp8_e4m3(code)
+    t = x.astype(np.float64) / s.astype(np.float64)
+    normal = np.abs(t) >= 2.0 ** -6
+    assert np.all(np.abs(got - t)[normal] <= 2.0 ** -4 * np.abs(t)[normal] * (1 + 1e-6))
+    assert np.all(np.abs(got - t)[~normal] <= 2.0 ** -10 * (1 + 1e-6))
+    big = np.array([449.0, 1e6, -500.0, np.inf, -np.inf], dtype=np.float32)
+    assert np.array_equal(oracle.decode_fp8_e4m3(oracle.quantize_fp8_e4m3(big, np.float32(1))),
+                          [448.0, 448.0, -448.0, 448.0, -448.0])
 
 
 def test_append_fp8_quantises_with_channel_scales():
