@@ -16,7 +16,9 @@ function that takes it.  Pages cited (by title and section):
   file summaries (scatter, token metadata, main/auxiliary partials, finalize).
 * "[WebGPU] Add DynamicSparseAttention" (onnxruntime PR 32529): Description (selected
   main-cache and local-plus-auxiliary modes, joint FP32 softmax with sink, guarded int32
-  indices, GQA head mapping) and the review comment on the count-bounded loop.
+  indices, GQA head mapping; packed QKV, QK RMSNorm, partial / interleaved RoPE with
+  offsets and position IDs) and the review comments on the count-bounded loop and on
+  reducing each head's RMS once.
 * DynamicSparseAttention INT8 KV cache / grouped decode (onnxruntime PR 33472): Key
   Changes table (INT8 per-channel K/V with key_scale / value_scale).
 * "ai.onnx.LinearAttention" kernel page: Attributes table (scale 0 selects 1/sqrt(d)).
@@ -27,8 +29,9 @@ page fixes (the sanitisation of malformed inputs and the status bits) are marked
 """
 from .status import (  # noqa: F401
     STATUS_BAD_CU, STATUS_Q_BOUND, STATUS_K_BOUND, STATUS_CAPACITY, STATUS_BAD_BLOCK,
-    STATUS_BAD_INDEX, STATUS_BAD_COUNT, STATUS_SHORT_KV, STATUS_CURSOR,
+    STATUS_BAD_INDEX, STATUS_BAD_COUNT, STATUS_SHORT_KV, STATUS_CURSOR, STATUS_POSITION,
 )
 from .metadata import prepare_seqlens  # noqa: F401
 from .append import quantize_int8, quantize_fp8_e4m3, decode_fp8_e4m3, kv_cache_append  # noqa: F401
 from .attention import attend, paged_attention, sparse_attention  # noqa: F401
+from .prologue import qkv_prologue  # noqa: F401

@@ -95,7 +95,7 @@ def _check_cu(cu, B, T):
 
 def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
                     block_table=None, block_size=None, key_scale=None, value_scale=None,
-                    committed_length=None):
+                    committed_length=None, skip_rows=None):
     """Write row ``cu[b] + i`` of ``k_new`` / ``v_new`` (``[T, H_kv, D]``) at key position
     ``p = (seqlens_k[b] + 1) - q_len_b + i`` of request ``b``.
 
@@ -113,6 +113,9 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
     Rows whose slot does not exist are skipped and flagged (parity unpinned): ``p < 0``
     (STATUS_SHORT_KV), ``p // bs >= max_blocks_per_seq`` or ``p >= cap``
     (STATUS_CAPACITY), a block id outside ``[0, nb)`` (STATUS_BAD_BLOCK).
+
+    ``skip_rows`` (optional, boolean ``[T]``): rows that are not written at all (the
+    prologue's rows whose rotary position is out of range); no other effect.
 
     Returns ``(k_cache_out, v_cache_out, status)``; the inputs are not modified.
     """
@@ -137,6 +140,8 @@ def kv_cache_append(k_new, v_new, cu_seqlens_q, seqlens_k, k_cache, v_cache,
         for i in range(q_len):
             r = cu[b] + i
             p = kv_len - q_len + i
+            if skip_rows is not None and skip_rows[r]:
+                continue
             if p < 0:
                 status |= STATUS_SHORT_KV
                 continue

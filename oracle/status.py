@@ -15,3 +15,4 @@ STATUS_BAD_INDEX = 1 << 5   # a selected index (inside the count) is neither -1 
 STATUS_BAD_COUNT = 1 << 6   # a selected count outside [0, max_selected] (clamped)
 STATUS_SHORT_KV = 1 << 7    # a request has fewer keys than query rows
 STATUS_CURSOR = 1 << 8      # committed_length disagrees with the append position: nothing appended
+STATUS_POSITION = 1 << 9    # a rotary position outside [0, max_position): row's Q is 0, K/V not appended

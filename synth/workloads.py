@@ -296,6 +296,118 @@ def paged_case(seed: int, *, kv_lens, q_lens, H_q: int, H_kv: int, D: int,
         max_seqlen_q=int(max_seqlen_q), max_seqlen_k=int(max_seqlen_k))
 
 
+@dataclass
+class PrologueCase:
+    """Inputs of the QKV prologue (split, QK RMSNorm, rotary embedding, cache append)."""
+    name: str
+    B: int
+    T: int
+    H_q: int
+    H_kv: int
+    D: int
+    dtype: int
+    cache_dtype: int
+    cu_seqlens_q: np.ndarray
+    past_seqlens: np.ndarray
+    seqlens_k: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_table: Optional[np.ndarray]
+    block_size: int
+    key_scale: Optional[np.ndarray]
+    value_scale: Optional[np.ndarray]
+    qkv: Optional[np.ndarray]          # [T, (H_q + 2 H_kv) * D] when packed, else None
+    q: np.ndarray                      # [T, H_q, D] (views of qkv when packed)
+    k: np.ndarray                      # [T, H_kv, D]
+    v: np.ndarray
+    qk_norm: bool
+    q_norm_weight: Optional[np.ndarray]   # float32 [D]
+    k_norm_weight: Optional[np.ndarray]
+    norm_eps: float
+    cos_table: Optional[np.ndarray]       # float32 [max_position, rotary_dim / 2]
+    sin_table: Optional[np.ndarray]
+    rotary_dim: int
+    interleaved: bool
+    position_ids: Optional[np.ndarray]    # int32 [T]
+    rotary_offsets: Optional[np.ndarray]  # int32 [B]
+    committed_length: Optional[np.ndarray] = None
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return 0 if self.block_table is None else int(self.block_table.shape[1])
+
+    @property
+    def max_position(self) -> int:
+        return 0 if self.cos_table is None else int(self.cos_table.shape[0])
+
+
+def rotary_tables(max_position: int, rotary_dim: int, base: float = 10000.0):
+    """Rotary cos / sin tables as a model ships them (an input of the prologue, not part
+    of it): angle(pos, i) = pos * base^(-2i / rotary_dim), evaluated in float64 and stored
+    as float32 [max_position, rotary_dim / 2]."""
+    half = rotary_dim // 2
+    theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / rotary_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def prologue_case(seed: int, *, kv_lens, q_lens, H_q: int, H_kv: int, D: int, dtype: int = F16,
+                  cache_dtype: Optional[int] = None, packed: bool = False, rotary_dim: int = 0,
+                  interleaved: bool = False, max_position: Optional[int] = None,
+                  qk_norm: bool = False, norm_weights: bool = True, norm_eps: float = 1e-6,
+                  explicit_positions: bool = False, offsets: bool = False,
+                  block_size: int = 16, contiguous: bool = False, num_blocks: Optional[int] = None,
+                  poison: bool = True, q_scale: float = 1.0, name: str = "prologue") -> PrologueCase:
+    """A prologue case: the caches, block table and new rows of ``paged_case`` (same
+    draws), the new rows as raw activations (packed into one ``[T, (H_q + 2 H_kv) D]``
+    array when ``packed``), norm weights U[0.5, 2], rotary tables of base 10000, and
+    optionally explicit positions (U[0, max_position)) and per-request offsets U{0..31}.
+    ``q_scale`` multiplies the raw query and key activations (pre-norm activations of a
+    real model are not unit-scale)."""
+    rng = np.random.default_rng(seed)
+    pc = paged_case(seed, kv_lens=kv_lens, q_lens=q_lens, H_q=H_q, H_kv=H_kv, D=D,
+                    block_size=block_size, dtype=dtype, cache_dtype=cache_dtype,
+                    num_blocks=num_blocks, contiguous=contiguous, poison=poison, rng=rng)
+    T = pc.T
+    q = _cast(pc.q.astype(np.float32) * np.float32(q_scale), dtype)
+    k = _cast(pc.k_new.astype(np.float32) * np.float32(q_scale if qk_norm else 1.0), dtype)
+    v = pc.v_new
+    qkv = None
+    if packed:
+        qkv = np.concatenate([q.reshape(T, -1), k.reshape(T, -1), v.reshape(T, -1)], axis=1)
+        qkv = np.ascontiguousarray(qkv)
+        a = qkv.reshape(T, H_q + 2 * H_kv, D)
+        q, k, v = a[:, :H_q], a[:, H_q:H_q + H_kv], a[:, H_q + H_kv:]
+    qw = kw = None
+    if qk_norm and norm_weights:
+        qw = rng.uniform(0.5, 2.0, size=D).astype(np.float32)
+        kw = rng.uniform(0.5, 2.0, size=D).astype(np.float32)
+    cos = sin = None
+    if max_position is None:
+        max_position = int(np.max(kv_lens)) + 64
+    if rotary_dim > 0:
+        cos, sin = rotary_tables(max_position, rotary_dim)
+    pos_ids = None
+    if explicit_positions:
+        pos_ids = rng.integers(0, max_position - 32, size=T).astype(np.int32)
+    offs = None
+    if offsets:
+        offs = rng.integers(0, 32, size=pc.B).astype(np.int32)
+    return PrologueCase(
+        name=name, B=pc.B, T=T, H_q=H_q, H_kv=H_kv, D=D, dtype=dtype, cache_dtype=pc.cache_dtype,
+        cu_seqlens_q=pc.cu_seqlens_q, past_seqlens=pc.past_seqlens, seqlens_k=pc.seqlens_k,
+        k_cache=pc.k_cache, v_cache=pc.v_cache, block_table=pc.block_table,
+        block_size=pc.block_size, key_scale=pc.key_scale, value_scale=pc.value_scale,
+        qkv=qkv, q=q, k=k, v=v, qk_norm=qk_norm, q_norm_weight=qw, k_norm_weight=kw,
+        norm_eps=float(norm_eps), cos_table=cos, sin_table=sin, rotary_dim=int(rotary_dim),
+        interleaved=bool(interleaved), position_ids=pos_ids, rotary_offsets=offs)
+
+
 def _selected_indices(rng, T, H_kv, max_selected, counts, hi_of_row, oor_frac=0.0):
     """Per (row, kv head): ``counts`` distinct indices from [0, hi), shuffled, padded with -1.
     A fraction ``oor_frac`` of in-count entries is replaced with out-of-range values, half
