@@ -86,6 +86,23 @@ def _queue_ahead():
     torch.cuda._sleep(4_000_000)
 
 
+class ColdCache:
+    """Before each timed call: read (not write) a 1 GiB buffer, so neither the L2 nor the
+    256 MB Infinity Cache holds the call's inputs, and neither holds dirty lines that the
+    call would have to write back (a 1 GiB write leaves up to 256 MB of them, which cost
+    the sparse and prologue calls 10-40 us of extra HBM writes)."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(1 << 27, dtype=torch.int64, device="cuda")
+        self.buf.zero_()
+        self.out = torch.empty(1, dtype=torch.int64, device="cuda")
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, dim=0, keepdim=True, out=self.out)
+
+
 def _events():
     import torch
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -296,7 +313,7 @@ def bench_sparse(which, steps, warmup):
                                          case.max_selected, case.local_window, case.H_q,
                                          case.H_kv, case.D)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = ColdCache()
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def call():
@@ -313,7 +330,7 @@ def bench_sparse(which, steps, warmup):
     torch.cuda.synchronize()
     evs = [_events() for _ in range(steps)]
     for a, b in evs:
-        flush.zero_()          # outside the events: the Infinity Cache holds none of the rows
+        flush()                # outside the events: the caches hold none of the rows
         a.record()
         call()
         b.record()
@@ -326,6 +343,70 @@ def bench_sparse(which, steps, warmup):
             "avg_us": round(sum(ms) / len(ms) * 1e3, 2), "algorithmic_bytes": alg,
             "main_keys": main_keys, "aux_keys": aux_keys, "gbs": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "status": int(status.item())}
+
+
+def _prologue_bytes(case):
+    """Algorithmic bytes of one qkv_prologue call: each row's packed Q/K/V read once, its
+    cos / sin table rows, the query row written, the key and value rows written to the
+    cache, the two norm weight vectors."""
+    es = 2 if case.dtype != 0 else 4
+    ces = {0: 4, 1: 2, 2: 2, 3: 1, 4: 1}[case.cache_dtype]
+    per_row = ((case.H_q + 2 * case.H_kv) * case.D * es + case.H_q * case.D * es
+               + 2 * case.H_kv * case.D * ces + (case.rotary_dim // 2) * 4 * 2)
+    return case.T * per_row + 2 * case.D * 4
+
+
+def bench_prologue(shape, steps, warmup):
+    """qkv_prologue (packed f16 rows, QK RMSNorm, full-width rotation, f16 paged cache) at the
+    GQA decode shape (31 rows) or the windowed prefill shape (5120 rows)."""
+    import numpy as np
+    import torch
+
+    import selected_token_sparse_amd as sta
+    import synth
+    from synth.device import tensor
+
+    if shape == "decode":
+        base = synth.config_gqa_paged_decode()
+        kv, ql = base.seqlens_k + 1, np.diff(base.cu_seqlens_q)
+        name = "prologue_gqa_decode_f16 (31 rows, H 64/8, D 64)"
+    else:
+        kv = ql = np.array([1024, 512, 2048, 1536])
+        name = "prologue_prefill_f16 (5120 rows, H 64/8, D 64)"
+    case = synth.prologue_case(seed=1006, kv_lens=kv, q_lens=ql, H_q=64, H_kv=8, D=64,
+                               dtype=synth.F16, packed=True, rotary_dim=64, qk_norm=True,
+                               poison=False)
+    d = lambda x, dt=None: tensor(x, dt)   # noqa: E731
+    qkv, cu, sk = d(case.qkv, case.dtype), d(case.cu_seqlens_q), d(case.seqlens_k)
+    kc, vc, bt = d(case.k_cache, case.cache_dtype), d(case.v_cache, case.cache_dtype), d(case.block_table)
+    qw, kw, cos, sin = d(case.q_norm_weight), d(case.k_norm_weight), d(case.cos_table), d(case.sin_table)
+    q_out = torch.empty((case.T, case.H_q, case.D), dtype=torch.float16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flush = ColdCache()
+
+    def call():
+        sta.qkv_prologue(q_out, kc, vc, cu, sk, H_q=case.H_q, H_kv=case.H_kv, qkv=qkv, qk_norm=True,
+                         q_norm_weight=qw, k_norm_weight=kw, rotary_dim=64, cos_table=cos,
+                         sin_table=sin, block_table=bt, status=status)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [_events() for _ in range(steps)]
+    for a, b in evs:
+        flush()                # outside the events: the caches hold none of the rows
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ms[len(ms) // 2]
+    alg = _prologue_bytes(case)
+    gbs = alg / (med * 1e-3) / 1e9
+    return {"workload": name, "median_us": round(med * 1e3, 2),
+            "avg_us": round(sum(ms) / len(ms) * 1e3, 2), "algorithmic_bytes": alg,
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "status": int(status.item())}
 
 
 def copy_calibration(mib, reps=4):
@@ -384,6 +465,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sparse", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -434,6 +516,9 @@ def main():
     if not args.no_sparse:
         line["selected_decode"] = bench_sparse("selected", 50, 5)
         line["local_plus_aux"] = bench_sparse("local_aux", 50, 5)
+    if not args.no_prologue:
+        line["prologue_decode"] = bench_prologue("decode", 50, 5)
+        line["prologue_prefill"] = bench_prologue("prefill", 50, 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

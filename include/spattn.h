@@ -94,6 +94,7 @@ extern "C" {
 #define SPATTN_STATUS_BAD_COUNT (1 << 6)  /* a selected count outside [0, max_selected]; clamped */
 #define SPATTN_STATUS_SHORT_KV (1 << 7)   /* fewer keys than query rows: rows before key 0 see nothing */
 #define SPATTN_STATUS_CURSOR (1 << 8)     /* committed_length disagrees with the append position */
+#define SPATTN_STATUS_POSITION (1 << 9)   /* qkv_prologue: a rotary position outside [0, max_position) */
 
 /* attention kinds for attention_workspace_bytes */
 #define SPATTN_KIND_PAGED 0
@@ -149,6 +150,47 @@ SPATTN_API int kv_cache_append(const void* k_new, const void* v_new, int new_dty
                     void* k_cache, void* v_cache, int cache_dtype, const int32_t* block_table,
                     int max_blocks_per_seq, int block_size, int num_blocks,
                     const float* key_scale, const float* value_scale, int H_kv, int D,
+                    const int32_t* committed_length, int32_t* status, void* stream);
+
+/*
+ * qkv_prologue - the step before attention, fused with the cache append ([DSA]
+ * Description, "QKV and cache" and "Position processing": packed or unpacked QKV, QK
+ * RMSNorm, partial and interleaved RoPE, rotary offsets, explicit position IDs; [DSA]
+ * review: a head's RMS is reduced once per (token, head); [SPA] overview: the
+ * PagedAttention prologue of packed-QKV split, RoPE and block-table scatter).  The pages
+ * print no formula for these steps; the textbook definitions below are the readings taken.
+ *
+ *   Input rows: qkv [T, (H_q + 2 H_kv) * D] (each row: the H_q query heads, then the H_kv
+ *   key heads, then the H_kv value heads, D elements each) or, when qkv is NULL, q
+ *   [T, H_q, D], k [T, H_kv, D], v [T, H_kv, D]; all of `dtype` (F32 / F16 / BF16).
+ *   qk_norm != 0: every query and key head x becomes x / sqrt(mean(x^2) + norm_eps) * w,
+ *   w = q_norm_weight / k_norm_weight [D] float32 (NULL = ones).
+ *   rotary_dim > 0 (even, <= D): the channel pairs (i, i + rotary_dim/2) -- or (2i, 2i+1)
+ *   when rotary_interleaved != 0 -- of every query and key head, i < rotary_dim/2, become
+ *   (a cos - b sin, b cos + a sin) with cos = cos_table[pos][i], sin = sin_table[pos][i]
+ *   (float32 [max_position, rotary_dim/2], row-major); channels >= rotary_dim pass
+ *   unchanged.  pos = (position_ids ? position_ids[t] : p) + (rotary_offsets ?
+ *   rotary_offsets[b] : 0), p the row's key position.  A pos outside [0, max_position)
+ *   sets SPATTN_STATUS_POSITION; that row's q_out is 0 and its K/V row is not appended.
+ *   Value heads are neither normalised nor rotated.
+ *   The arithmetic is float32 (norm, then rotation).  q_out [T, H_q, D] (dtype) receives
+ *   the query heads rounded once to dtype; the key heads are rounded once to dtype too,
+ *   and the key and value rows are then stored exactly as kv_cache_append stores
+ *   k_new / v_new, with the same cache arguments, INT8 / FP8 quantisation, committed_length
+ *   cursor check and status bits.  Rows of no request (malformed cu): q_out 0,
+ *   SPATTN_STATUS_BAD_CU, nothing appended.
+ *   Limits: 8 <= D <= 256, D % 8 == 0; norm_eps >= 0.  qkv / q / k / v must not overlap
+ *   q_out or the caches.
+ */
+SPATTN_API int qkv_prologue(const void* qkv, const void* q, const void* k, const void* v, int dtype,
+                    const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int B, int T,
+                    int H_q, int H_kv, int D, int qk_norm, const float* q_norm_weight,
+                    const float* k_norm_weight, float norm_eps, int rotary_dim,
+                    int rotary_interleaved, const float* cos_table, const float* sin_table,
+                    int max_position, const int32_t* position_ids, const int32_t* rotary_offsets,
+                    void* q_out, void* k_cache, void* v_cache, int cache_dtype,
+                    const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                    int num_blocks, const float* key_scale, const float* value_scale,
                     const int32_t* committed_length, int32_t* status, void* stream);
 
 /*

@@ -26,6 +26,7 @@ STATUS_BAD_INDEX = 1 << 5
 STATUS_BAD_COUNT = 1 << 6
 STATUS_SHORT_KV = 1 << 7
 STATUS_CURSOR = 1 << 8
+STATUS_POSITION = 1 << 9
 
 _ERRORS = {-1: "null pointer", -2: "shape", -3: "dtype", -4: "unsupported", -5: "workspace too small",
            -6: "launch failed"}
@@ -115,6 +116,49 @@ def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, cu_seqlens_q: torc
         _dt(k_cache), _i32(block_table, "block_table"), mbps, bs, nb,
         _ptr(key_scale, "key_scale"), _ptr(value_scale, "value_scale"), H_kv, D,
         _i32(committed_length, "committed_length"), _i32(status, "status"), _stream(k_new)))
+
+
+def qkv_prologue(q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 cu_seqlens_q: torch.Tensor, seqlens_k: torch.Tensor, *, H_q: int, H_kv: int,
+                 qkv: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+                 k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                 qk_norm: bool = False, q_norm_weight: Optional[torch.Tensor] = None,
+                 k_norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+                 rotary_dim: int = 0, interleaved: bool = False,
+                 cos_table: Optional[torch.Tensor] = None, sin_table: Optional[torch.Tensor] = None,
+                 position_ids: Optional[torch.Tensor] = None,
+                 rotary_offsets: Optional[torch.Tensor] = None,
+                 block_table: Optional[torch.Tensor] = None,
+                 key_scale: Optional[torch.Tensor] = None,
+                 value_scale: Optional[torch.Tensor] = None,
+                 committed_length: Optional[torch.Tensor] = None,
+                 status: Optional[torch.Tensor] = None) -> None:
+    """Split (packed `qkv` [T, (H_q + 2 H_kv) * D], or `q`, `k`, `v`), QK RMSNorm, rotary
+    embedding; the queries go to `q_out` [T, H_q, D], the key and value rows into the cache
+    as kv_cache_append stores them."""
+    T, _, D = (int(x) for x in q_out.shape)
+    B = int(seqlens_k.shape[0])
+    src = qkv if qkv is not None else q
+    if src is None or src.dtype != q_out.dtype:
+        raise TypeError("the input rows and q_out must share one dtype")
+    for what, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight),
+                    ("cos_table", cos_table), ("sin_table", sin_table)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{what} must be float32")
+    max_position = int(cos_table.shape[0]) if cos_table is not None else 0
+    nb, bs, mbps = _cache_dims(k_cache, block_table)
+    lib = _lib.load()
+    _check("qkv_prologue", lib.qkv_prologue(
+        _ptr(qkv, "qkv"), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _dt(q_out),
+        _i32(cu_seqlens_q, "cu_seqlens_q"), _i32(seqlens_k, "seqlens_k"), B, T, int(H_q),
+        int(H_kv), D, int(bool(qk_norm)), _ptr(q_norm_weight, "q_norm_weight"),
+        _ptr(k_norm_weight, "k_norm_weight"), float(norm_eps), int(rotary_dim),
+        int(bool(interleaved)), _ptr(cos_table, "cos_table"), _ptr(sin_table, "sin_table"),
+        max_position, _i32(position_ids, "position_ids"), _i32(rotary_offsets, "rotary_offsets"),
+        _ptr(q_out, "q_out"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"), _dt(k_cache),
+        _i32(block_table, "block_table"), mbps, bs, nb, _ptr(key_scale, "key_scale"),
+        _ptr(value_scale, "value_scale"), _i32(committed_length, "committed_length"),
+        _i32(status, "status"), _stream(q_out)))
 
 
 def attention_workspace_bytes(kind: int, dtype: int, B: int, T: int, max_seqlen_q: int,

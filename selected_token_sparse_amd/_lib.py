@@ -19,6 +19,11 @@ _SIGNATURES = {
     "kv_cache_append": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_int,
                                 c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "qkv_prologue": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                             c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                             c_float, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
+                             c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int,
+                             c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "attention_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                              c_int, c_int, c_int, c_int]),
     "paged_attention_fwd": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_int,

@@ -4,6 +4,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "prologue.h"
 
 using namespace spattn;
 
@@ -78,6 +79,47 @@ int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
                                 v_cache, cache_dtype, block_table, max_blocks_per_seq, block_size,
                                 num_blocks, key_scale, value_scale, H_kv, D, committed_length,
                                 status, (hipStream_t)stream);
+}
+
+int qkv_prologue(const void* qkv, const void* q, const void* k, const void* v, int dtype,
+                 const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int B, int T, int H_q,
+                 int H_kv, int D, int qk_norm, const float* q_norm_weight,
+                 const float* k_norm_weight, float norm_eps, int rotary_dim,
+                 int rotary_interleaved, const float* cos_table, const float* sin_table,
+                 int max_position, const int32_t* position_ids, const int32_t* rotary_offsets,
+                 void* q_out, void* k_cache, void* v_cache, int cache_dtype,
+                 const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                 int num_blocks, const float* key_scale, const float* value_scale,
+                 const int32_t* committed_length, int32_t* status, void* stream) {
+  if (B < 0 || T < 0 || H_q < 1 || H_kv < 1 || D < 8 || D > 256 || D % 8 != 0)
+    return SPATTN_ERR_SHAPE;
+  if (!float_dtype(dtype)) return SPATTN_ERR_DTYPE;
+  if (!quantised_cache(cache_dtype) && !float_dtype(cache_dtype)) return SPATTN_ERR_DTYPE;
+  if (rotary_dim < 0 || rotary_dim > D || rotary_dim % 2 != 0) return SPATTN_ERR_SHAPE;
+  if (rotary_dim > 0 && (cos_table == nullptr || sin_table == nullptr)) return SPATTN_ERR_NULL;
+  if (rotary_dim > 0 && max_position < 1) return SPATTN_ERR_SHAPE;
+  if (qk_norm && !(norm_eps >= 0.f && norm_eps < __builtin_huge_valf())) return SPATTN_ERR_SHAPE;
+  if (T == 0) return SPATTN_OK;
+  if (B == 0) return SPATTN_ERR_SHAPE;
+  if (qkv == nullptr && (q == nullptr || k == nullptr || v == nullptr)) return SPATTN_ERR_NULL;
+  if (q_out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr) return SPATTN_ERR_NULL;
+  int rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
+                       block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+  spattn::PrologueArgs a{};
+  a.qkv = qkv; a.q = q; a.k = k; a.v = v; a.dtype = dtype;
+  a.cu = cu_seqlens_q; a.seqlens_k = seqlens_k;
+  a.B = B; a.T = T; a.H_q = H_q; a.H_kv = H_kv; a.D = D;
+  a.qk_norm = qk_norm != 0; a.q_norm_weight = q_norm_weight; a.k_norm_weight = k_norm_weight;
+  a.norm_eps = norm_eps;
+  a.rotary_dim = rotary_dim; a.interleaved = rotary_interleaved != 0;
+  a.cos_table = cos_table; a.sin_table = sin_table; a.max_position = max_position;
+  a.position_ids = position_ids; a.rotary_offsets = rotary_offsets;
+  a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+  a.block_table = block_table; a.max_blocks = max_blocks_per_seq; a.block_size = block_size;
+  a.num_blocks = num_blocks; a.key_scale = key_scale; a.value_scale = value_scale;
+  a.committed = committed_length; a.status = status;
+  return spattn::launch_qkv_prologue(a, (hipStream_t)stream);
 }
 
 size_t attention_workspace_bytes(int kind, int dtype, int B, int T, int max_seqlen_q,

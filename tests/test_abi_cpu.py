@@ -19,8 +19,9 @@ def _declared():
 
 def test_header_declares_the_abi():
     names = _declared()
-    assert set(names) == {"prepare_seqlens", "kv_cache_append", "paged_attention_fwd",
-                          "sparse_attention_fwd", "attention_workspace_bytes"}
+    assert set(names) == {"prepare_seqlens", "kv_cache_append", "qkv_prologue",
+                          "paged_attention_fwd", "sparse_attention_fwd",
+                          "attention_workspace_bytes"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -118,6 +119,40 @@ def test_append_argument_errors(lib):
     assert call(17, 60) == -2        # head_dim not a multiple of 8
     assert call(12, 0) == -2         # block size
     assert call(6, 0) == 0           # nothing to append
+
+
+def test_prologue_argument_errors(lib):
+    """Argument errors return before anything is enqueued (fake device pointers are never
+    touched)."""
+    f = lib.qkv_prologue
+    # qkv, q, k, v, dtype, cu, sk, B, T, H_q, H_kv, D, qk_norm, qw, kw, eps, rd, inter, cos,
+    # sin, max_pos, pos_ids, offs, q_out, kc, vc, cache_dtype, bt, mbps, bs, nb, ks, vs,
+    # committed, status, stream
+    base = [FAKE, None, None, None, 1, FAKE, FAKE, 2, 4, 8, 2, 64, 1, None, None, 1e-6, 32, 0,
+            FAKE, FAKE, 128, None, None, FAKE, FAKE, FAKE, 1, FAKE, 4, 16, 8, None, None,
+            None, None, None]
+    def call(**kv):
+        a = list(base)
+        for i, v in kv.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a4=3) == -3                    # int8 activations
+    assert call(a26=2) == -3                   # cache dtype differs from the rows'
+    assert call(a26=4) == -1                   # FP8 cache without scales
+    assert call(a0=None) == -1                 # neither packed rows nor q, k, v
+    assert call(a0=None, a1=FAKE, a2=FAKE) == -1
+    assert call(a11=60) == -2                  # head_dim not a multiple of 8
+    assert call(a11=264) == -2                 # head_dim above 256
+    assert call(a16=33) == -2                  # odd rotary_dim
+    assert call(a16=72) == -2                  # rotary_dim above head_dim
+    assert call(a18=None) == -1                # rotation without tables
+    assert call(a20=0) == -2                   # empty tables
+    assert call(a15=-1.0) == -2                # negative eps
+    assert call(a15=float("inf")) == -2
+    assert call(a23=None) == -1                # no q_out
+    assert call(a29=0) == -2                   # block size
+    assert call(a8=0) == 0                     # no rows: nothing to do
+    assert call(a7=0) == -2                    # rows but no request
 
 
 def test_prepare_argument_errors(lib):
