@@ -20,7 +20,9 @@ function that takes it.  Pages cited (by title and section):
   offsets and position IDs) and the review comments on the count-bounded loop and on
   reducing each head's RMS once.
 * DynamicSparseAttention INT8 KV cache / grouped decode (onnxruntime PR 33472): Key
-  Changes table (INT8 per-channel K/V with key_scale / value_scale).
+  Changes table (INT8 per-channel K/V with key_scale / value_scale; hierarchical / compact
+  TopK selection) and its follow-up description (TopK properties: stable keys, causal
+  tails, capacity padding).
 * "ai.onnx.LinearAttention" kernel page: Attributes table (scale 0 selects 1/sqrt(d)).
 
 Parity status of each function is stated in its docstring; functions whose results no
@@ -35,3 +37,4 @@ from .metadata import prepare_seqlens  # noqa: F401
 from .append import quantize_int8, quantize_fp8_e4m3, decode_fp8_e4m3, kv_cache_append  # noqa: F401
 from .attention import attend, paged_attention, sparse_attention  # noqa: F401
 from .prologue import qkv_prologue  # noqa: F401
+from .topk import topk_select  # noqa: F401

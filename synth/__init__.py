@@ -9,8 +9,8 @@ uses for its worked examples), chosen together with the other lengths it draws.
 """
 from .workloads import (  # noqa: F401
     BF16, F16, F32, I8, FP8, QUANTISED, DTYPE_NAMES,
-    PagedCase, SparseCase, PrologueCase,
-    paged_case, prologue_case, rotary_tables, sparse_selected_case, sparse_local_aux_case,
+    PagedCase, SparseCase, PrologueCase, TopkCase,
+    paged_case, prologue_case, rotary_tables, topk_case, sparse_selected_case, sparse_local_aux_case,
     config_tiny_paged_decode, config_gqa_paged_decode, config_paged_prefill_window,
     config_selected_decode, config_local_plus_aux_int8,
     round_bf16,

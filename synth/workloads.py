@@ -408,6 +408,49 @@ def prologue_case(seed: int, *, kv_lens, q_lens, H_q: int, H_kv: int, D: int, dt
         interleaved=bool(interleaved), position_ids=pos_ids, rotary_offsets=offs)
 
 
+@dataclass
+class TopkCase:
+    """Inputs of the TopK selection: per-key scores of each (row, KV head)."""
+    name: str
+    B: int
+    T: int
+    H_kv: int
+    L: int
+    scores: np.ndarray          # float32 [T, H_kv, L]
+    cu_seqlens_q: np.ndarray
+    seqlens_k: np.ndarray
+    k: int
+    tail: int
+    capacity: int
+
+
+def topk_case(seed: int, *, kv_lens, q_lens, H_kv: int, L: Optional[int] = None, k: int,
+              tail: int = 0, capacity: Optional[int] = None, ties: float = 0.0,
+              specials: float = 0.0, name: str = "topk") -> TopkCase:
+    """Scores N(0, 1) in float32 (an indexer's output stands in as synthetic values); a
+    fraction ``ties`` is rounded to multiples of 1/4 (many equal scores), a fraction
+    ``specials`` replaced by NaN, +-inf or +-0.0."""
+    rng = np.random.default_rng(seed)
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    B = len(kv_lens)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    T = int(cu[-1])
+    L = int(L if L is not None else max(1, int(kv_lens.max(initial=1))))
+    scores = rng.standard_normal((T, H_kv, L), dtype=np.float32)
+    if ties > 0:
+        m = rng.random(scores.shape) < ties
+        scores[m] = np.round(scores[m] * 4) / 4
+    if specials > 0:
+        m = rng.random(scores.shape) < specials
+        pool = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0], dtype=np.float32)
+        scores[m] = pool[rng.integers(0, len(pool), size=int(m.sum()))]
+    return TopkCase(name=name, B=B, T=T, H_kv=H_kv, L=L, scores=scores, cu_seqlens_q=cu,
+                    seqlens_k=(kv_lens - 1).astype(np.int32), k=int(k), tail=int(tail),
+                    capacity=int(capacity if capacity is not None else k))
+
+
 def _selected_indices(rng, T, H_kv, max_selected, counts, hi_of_row, oor_frac=0.0):
     """Per (row, kv head): ``counts`` distinct indices from [0, hi), shuffled, padded with -1.
     A fraction ``oor_frac`` of in-count entries is replaced with out-of-range values, half
