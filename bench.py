@@ -409,6 +409,45 @@ def bench_prologue(shape, steps, warmup):
             "status": int(status.item())}
 
 
+def bench_topk(steps, warmup):
+    """topk_select at the selected grouped decode shape: 128 rows x 4 KV heads, 65536
+    candidates each (float32 scores, 134 MB), k = 2048 with a 64-key causal tail."""
+    import torch
+
+    import selected_token_sparse_amd as sta
+    import synth
+    from synth.device import tensor
+
+    case = synth.topk_case(1007, kv_lens=[65536] * 16, q_lens=[8] * 16, H_kv=4, L=65536, k=2048,
+                           tail=64, capacity=2048, ties=0.05, specials=0.001)
+    scores, cu, sk = tensor(case.scores), tensor(case.cu_seqlens_q), tensor(case.seqlens_k)
+    sel = torch.empty((case.T, case.H_kv, case.capacity), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((case.T, case.H_kv), dtype=torch.int32, device="cuda")
+    flush = ColdCache()
+
+    def call():
+        sta.topk_select(scores, cu, sk, case.k, sel, cnt, tail=case.tail)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [_events() for _ in range(steps)]
+    for a, b in evs:
+        flush()                # outside the events: the caches hold none of the scores
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ms[len(ms) // 2]
+    alg = case.scores.nbytes + sel.numel() * 4 + cnt.numel() * 4
+    gbs = alg / (med * 1e-3) / 1e9
+    return {"workload": "topk_selected_decode (128 rows x 4 KV heads, 65536 scores, k 2048, tail 64)",
+            "median_us": round(med * 1e3, 2), "avg_us": round(sum(ms) / len(ms) * 1e3, 2),
+            "algorithmic_bytes": alg, "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def copy_calibration(mib, reps=4):
     """A plain device-to-device copy of `mib` MiB, for scaling the HBM byte counters: the
     copy reads and writes exactly mib * 2^20 bytes each."""
@@ -466,6 +505,7 @@ def main():
     ap.add_argument("--no-sparse", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
+    ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -519,6 +559,8 @@ def main():
     if not args.no_prologue:
         line["prologue_decode"] = bench_prologue("decode", 50, 5)
         line["prologue_prefill"] = bench_prologue("prefill", 50, 5)
+    if not args.no_topk:
+        line["topk"] = bench_topk(30, 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

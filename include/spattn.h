@@ -194,6 +194,29 @@ SPATTN_API int qkv_prologue(const void* qkv, const void* q, const void* k, const
                     const int32_t* committed_length, int32_t* status, void* stream);
 
 /*
+ * topk_select - the k highest-scoring key positions of every (row, KV head): the producer of
+ * sel_idx / sel_count for sparse_attention_fwd mode 0 (DynamicSparseAttention INT8 / fast
+ * QSA decode page, Key Changes table: hierarchical / compact TopK selection; follow-up
+ * description: stable keys, causal tails, capacity stride and padding).  The pages name
+ * those properties only; this is the reading taken.
+ *
+ *   scores [T, H_kv, L] float32 (row-major; the score of key position j is scores[t][c][j]).
+ *   Row t of request b sees positions 0 .. p, p = (seqlens_k[b] + 1) - q_len_b + i, so it
+ *   has n = clamp(p + 1, 0, L) candidates.  If n <= k all are selected.  Otherwise the last
+ *   min(tail, k) candidates (the causal tail) are selected, and the other selections are
+ *   the highest-scoring remaining candidates: equal scores by position, lower first; NaN
+ *   below every number; -0.0 equal to +0.0.
+ *   Outputs: sel_idx [T, H_kv, capacity] int32 -- the min(k, n) selected positions in
+ *   ascending order, then -1 -- and sel_count [T, H_kv] int32 = min(k, n).  Rows owned by
+ *   no request (malformed cu): count 0, SPATTN_STATUS_BAD_CU.
+ *   Limits: 1 <= L <= 65536, 0 <= k <= capacity, tail >= 0.
+ */
+SPATTN_API int topk_select(const float* scores, int L, const int32_t* cu_seqlens_q,
+                    const int32_t* seqlens_k, int B, int T, int H_kv, int k, int tail,
+                    int32_t* sel_idx, int capacity, int32_t* sel_count, int32_t* status,
+                    void* stream);
+
+/*
  * attention_workspace_bytes - device workspace (bytes) an attention call with these
  * arguments needs for its split-K partial softmax states ([SPA] file summaries and
  * follow-up description: FP32 partial states merged by a finalize stage).  Pure host

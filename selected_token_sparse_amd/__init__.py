@@ -161,6 +161,24 @@ def qkv_prologue(q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
         _i32(status, "status"), _stream(q_out)))
 
 
+def topk_select(scores: torch.Tensor, cu_seqlens_q: torch.Tensor, seqlens_k: torch.Tensor,
+                k: int, sel_idx: torch.Tensor, sel_count: torch.Tensor, tail: int = 0,
+                status: Optional[torch.Tensor] = None) -> None:
+    """The k highest-scoring causal key positions of every (row, KV head) of `scores`
+    [T, H_kv, L] (float32), the last `tail` always kept, into `sel_idx` [T, H_kv, capacity]
+    (ascending, -1 padded) and `sel_count` [T, H_kv]."""
+    if scores.dtype != torch.float32:
+        raise TypeError("scores must be float32")
+    T, H_kv, L = (int(x) for x in scores.shape)
+    capacity = int(sel_idx.shape[-1])
+    B = int(seqlens_k.shape[0])
+    lib = _lib.load()
+    _check("topk_select", lib.topk_select(
+        _ptr(scores, "scores"), L, _i32(cu_seqlens_q, "cu_seqlens_q"), _i32(seqlens_k, "seqlens_k"),
+        B, T, H_kv, int(k), int(tail), _i32(sel_idx, "sel_idx"), capacity,
+        _i32(sel_count, "sel_count"), _i32(status, "status"), _stream(scores)))
+
+
 def attention_workspace_bytes(kind: int, dtype: int, B: int, T: int, max_seqlen_q: int,
                               max_seqlen_k: int, max_selected: int, local_window: int,
                               H_q: int, H_kv: int, D: int) -> int:

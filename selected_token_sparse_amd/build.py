@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libspattn.so")
-SOURCES = ["metadata.hip", "append.hip", "prologue.hip", "decode.hip", "prefill.hip", "api.hip"]
+SOURCES = ["metadata.hip", "append.hip", "prologue.hip", "topk.hip", "decode.hip", "prefill.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

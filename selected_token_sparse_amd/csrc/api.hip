@@ -5,6 +5,7 @@
 #include "common.h"
 #include "launch.h"
 #include "prologue.h"
+#include "topk.h"
 
 using namespace spattn;
 
@@ -120,6 +121,23 @@ int qkv_prologue(const void* qkv, const void* q, const void* k, const void* v, i
   a.num_blocks = num_blocks; a.key_scale = key_scale; a.value_scale = value_scale;
   a.committed = committed_length; a.status = status;
   return spattn::launch_qkv_prologue(a, (hipStream_t)stream);
+}
+
+int topk_select(const float* scores, int L, const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                int B, int T, int H_kv, int k, int tail, int32_t* sel_idx, int capacity,
+                int32_t* sel_count, int32_t* status, void* stream) {
+  if (B < 0 || T < 0 || H_kv < 1 || L < 1 || L > 65536) return L > 65536 ? SPATTN_ERR_UNSUPPORTED : SPATTN_ERR_SHAPE;
+  if (k < 0 || tail < 0 || capacity < k) return SPATTN_ERR_SHAPE;
+  if (T == 0) return SPATTN_OK;
+  if (B == 0) return SPATTN_ERR_SHAPE;
+  if (scores == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr || sel_count == nullptr ||
+      (capacity > 0 && sel_idx == nullptr))
+    return SPATTN_ERR_NULL;
+  spattn::TopkArgs a{};
+  a.scores = scores; a.L = L; a.cu = cu_seqlens_q; a.seqlens_k = seqlens_k;
+  a.B = B; a.T = T; a.H_kv = H_kv; a.k = k; a.tail = tail; a.capacity = capacity;
+  a.sel_idx = sel_idx; a.sel_count = sel_count; a.status = status;
+  return spattn::launch_topk_select(a, (hipStream_t)stream);
 }
 
 size_t attention_workspace_bytes(int kind, int dtype, int B, int T, int max_seqlen_q,

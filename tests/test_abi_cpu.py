@@ -19,7 +19,7 @@ def _declared():
 
 def test_header_declares_the_abi():
     names = _declared()
-    assert set(names) == {"prepare_seqlens", "kv_cache_append", "qkv_prologue",
+    assert set(names) == {"prepare_seqlens", "kv_cache_append", "qkv_prologue", "topk_select",
                           "paged_attention_fwd", "sparse_attention_fwd",
                           "attention_workspace_bytes"}
 
@@ -153,6 +153,27 @@ def test_prologue_argument_errors(lib):
     assert call(a29=0) == -2                   # block size
     assert call(a8=0) == 0                     # no rows: nothing to do
     assert call(a7=0) == -2                    # rows but no request
+
+
+def test_topk_argument_errors(lib):
+    f = lib.topk_select
+    # scores, L, cu, sk, B, T, H_kv, k, tail, sel_idx, capacity, sel_count, status, stream
+    base = [FAKE, 4096, FAKE, FAKE, 2, 8, 4, 512, 16, FAKE, 512, FAKE, None, None]
+    def call(**kv):
+        a = list(base)
+        for i, v in kv.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a1=0) == -2            # no score columns
+    assert call(a1=65537) == -4        # longer than one workgroup's registers hold
+    assert call(a7=-1) == -2
+    assert call(a8=-1) == -2
+    assert call(a10=511) == -2         # capacity below k
+    assert call(a0=None) == -1
+    assert call(a11=None) == -1
+    assert call(a9=None) == -1
+    assert call(a5=0) == 0             # no rows
+    assert call(a4=0) == -2            # rows but no request
 
 
 def test_prepare_argument_errors(lib):
