@@ -131,7 +131,8 @@ template <int D>
 struct SplitLds {
   static constexpr bool kDeep = D == 64;  // two tiles in flight per wave at D = 64
   static constexpr int kVTileBytes = (kDeep ? 2 : 1) * kTile * D * 2;  // a wave's V tiles
-  static constexpr int kCombineBytes = kWaves * 16 * (D + 2) * 4;
+  static constexpr int kCombineRow = D + 4;   // floats per (wave, head) row of the combine area
+  static constexpr int kCombineBytes = (kWaves * 16 * kCombineRow + 4 * kWaves * 16) * 4;
   static constexpr int kAreaBytes = (kWaves * kVTileBytes > kCombineBytes) ? kWaves * kVTileBytes : kCombineBytes;
 };
 
@@ -534,14 +535,34 @@ void split_attn_kernel(SplitParams P) {
   __syncthreads();
 
   // ---- 4. merge the four wave states (head lam, dims 16m + 4grp + i) ----
+  // Rows of the accumulator area are padded by 4 floats so the 16-byte stores of the 16
+  // heads of a lane group fall in different banks; the merge factors of each (wave, head)
+  // are computed once, by 16 threads.
+  constexpr int CR = SplitLds<D>::kCombineRow;
   float* cm = reinterpret_cast<float*>(area);              // [wave][16] m
   float* cl = cm + kWaves * 16;                           // [wave][16] l
-  float* ca = cl + kWaves * 16;                           // [wave][16][D] acc
+  float* cf = cl + kWaves * 16;                           // [wave][16] merge factor
+  float* cML = cf + kWaves * 16;                          // [16] (M, L)
+  float* ca = cML + kWaves * 16;                          // [wave][16][CR] acc
   if (grp == 0) { cm[wave * 16 + lam] = m_run; cl[wave * 16 + lam] = l_run; }
 #pragma unroll
   for (int m = 0; m < D / 16; ++m)
+    *reinterpret_cast<f32x4*>(ca + (wave * 16 + lam) * CR + 16 * m + 4 * grp) = acc[m];
+  __syncthreads();
+  if (tid < 16) {
+    float M = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ca[(wave * 16 + lam) * D + 16 * m + 4 * grp + i] = acc[m][i];
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + tid]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = M != kNegInf ? exp2_safe(cm[w * 16 + tid] - M) : 0.f;
+      cf[w * 16 + tid] = f;
+      L += cl[w * 16 + tid] * f;
+    }
+    cML[2 * tid] = M;
+    cML[2 * tid + 1] = L;
+  }
   __syncthreads();
 
   const bool single = P.n_splits == 1;
@@ -549,17 +570,11 @@ void split_attn_kernel(SplitParams P) {
   for (int e = tid; e < 16 * D; e += kThreads) {
     const int h = e / D, d = e - h * D;
     if (h >= nh) continue;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + h]);
-    float L = 0.f, A = 0.f;
+    const float M = cML[2 * h], L = cML[2 * h + 1];
+    float A = 0.f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = exp2_safe(cm[w * 16 + h] - M);
-        L += cl[w * 16 + h] * f;
-        A += ca[(w * 16 + h) * D + d] * f;
-      }
+      for (int w = 0; w < kWaves; ++w) A += ca[(w * 16 + h) * CR + d] * cf[w * 16 + h];
       if (use_scale) A *= P.value_scale[c * D + d] * kUnit;
     }
     const int head = h0 + h;
