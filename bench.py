@@ -1,8 +1,9 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: prepare_seqlens (device metadata)
--> kv_cache_append (this step's K/V rows into the paged cache) -> paged_attention_fwd
-(split-K decode over the block table, merge with sinks).  Workload: GQA paged decode,
+and kv_cache_append (this step's K/V rows into the paged cache), made as one launch by
+prepare_and_append -> paged_attention_fwd (split-K decode over the block table, merge
+with sinks).  Workload: GQA paged decode,
 fp16, B=32 requests with key counts ~ U{0..8192} (one forced empty), H_q=64, H_kv=8,
 head_dim 64, block 16, a 20000-block pool, sinks ~ N(0,1).  Inputs are resident in HBM
 before the timed region; three copies of the KV pool are rotated so that consecutive
@@ -10,7 +11,9 @@ steps never find their 260 MB of keys/values in the 256 MB Infinity Cache.
 
 value = decode KV bytes per step / time per step (GB/s, 1 GB = 1e9 B).  The prefill
 TFLOP/s of the windowed paged prefill workload (B=4, lengths 1024/512/2048/1536, W=128)
-and of the same without a window are reported alongside, as the metric names both.
+and of the same without a window are reported alongside, as the metric names both; so
+are the selected-token and local-plus-auxiliary decode, the QKV prologue and the TopK
+selection (each call preceded by a 1 GiB read, so the caches hold none of its inputs).
 
 `--gpus N` with N > 1 is not supported: this build runs on one GPU.
 """
@@ -132,9 +135,9 @@ def bench_decode(steps, warmup, copies=3):
 
     def step(i, ev=None):
         t = sets[i % copies]
-        sta.prepare_seqlens(t["cu"], t["past"], T, sq, sk, status=status)
-        sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], sk, t["k_cache"], t["v_cache"],
-                            t["block_table"], status=status)
+        # metadata and the cache append of this step's rows: one launch
+        sta.prepare_and_append(t["cu"], t["past"], T, sq, sk, t["k_new"], t["v_new"], t["k_cache"],
+                               t["v_cache"], t["block_table"], status=status)
         if ev is not None:
             ev[0].record()
         sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], sk, case.max_seqlen_q,

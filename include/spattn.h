@@ -153,6 +153,23 @@ SPATTN_API int kv_cache_append(const void* k_new, const void* v_new, int new_dty
                     const int32_t* committed_length, int32_t* status, void* stream);
 
 /*
+ * prepare_and_append - prepare_seqlens followed by kv_cache_append with the seqlens_k it
+ * produced, as one launch when B <= 255 (two otherwise).  Its outputs and status are
+ * those of the two calls made in order (same citations): seqlens_q, seqlens_k, token_req /
+ * token_pos (may be NULL), the appended rows, and the status bits of both.  For a decode
+ * step it removes one kernel launch; no device metadata is read back either way.
+ *   Arguments: those of prepare_seqlens, then those of kv_cache_append after its
+ *   seqlens_k (which is this call's output).  Limits: 0 <= B <= 8192.
+ */
+SPATTN_API int prepare_and_append(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B,
+                    int T, int32_t* seqlens_q, int32_t* seqlens_k, int32_t* token_req,
+                    int32_t* token_pos, const void* k_new, const void* v_new, int new_dtype,
+                    void* k_cache, void* v_cache, int cache_dtype, const int32_t* block_table,
+                    int max_blocks_per_seq, int block_size, int num_blocks,
+                    const float* key_scale, const float* value_scale, int H_kv, int D,
+                    const int32_t* committed_length, int32_t* status, void* stream);
+
+/*
  * qkv_prologue - the step before attention, fused with the cache append ([DSA]
  * Description, "QKV and cache" and "Position processing": packed or unpacked QKV, QK
  * RMSNorm, partial and interleaved RoPE, rotary offsets, explicit position IDs; [DSA]

@@ -118,6 +118,31 @@ def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, cu_seqlens_q: torc
         _i32(committed_length, "committed_length"), _i32(status, "status"), _stream(k_new)))
 
 
+def prepare_and_append(cu_seqlens_q: torch.Tensor, past_seqlens: torch.Tensor, T: int,
+                       seqlens_q: torch.Tensor, seqlens_k: torch.Tensor, k_new: torch.Tensor,
+                       v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       block_table: Optional[torch.Tensor] = None,
+                       token_req: Optional[torch.Tensor] = None,
+                       token_pos: Optional[torch.Tensor] = None,
+                       key_scale: Optional[torch.Tensor] = None,
+                       value_scale: Optional[torch.Tensor] = None,
+                       committed_length: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None) -> None:
+    """prepare_seqlens then kv_cache_append with the seqlens_k it produced, in one launch."""
+    B = int(past_seqlens.shape[0])
+    _, H_kv, D = (int(x) for x in k_new.shape)
+    nb, bs, mbps = _cache_dims(k_cache, block_table)
+    lib = _lib.load()
+    _check("prepare_and_append", lib.prepare_and_append(
+        _i32(cu_seqlens_q, "cu_seqlens_q"), _i32(past_seqlens, "past_seqlens"), B, int(T),
+        _i32(seqlens_q, "seqlens_q"), _i32(seqlens_k, "seqlens_k"), _i32(token_req, "token_req"),
+        _i32(token_pos, "token_pos"), _ptr(k_new, "k_new"), _ptr(v_new, "v_new"), _dt(k_new),
+        _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"), _dt(k_cache),
+        _i32(block_table, "block_table"), mbps, bs, nb, _ptr(key_scale, "key_scale"),
+        _ptr(value_scale, "value_scale"), H_kv, D, _i32(committed_length, "committed_length"),
+        _i32(status, "status"), _stream(cu_seqlens_q)))
+
+
 def qkv_prologue(q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  cu_seqlens_q: torch.Tensor, seqlens_k: torch.Tensor, *, H_q: int, H_kv: int,
                  qkv: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,

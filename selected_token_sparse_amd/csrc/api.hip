@@ -4,6 +4,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "append.h"
 #include "prologue.h"
 #include "topk.h"
 
@@ -80,6 +81,35 @@ int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
                                 v_cache, cache_dtype, block_table, max_blocks_per_seq, block_size,
                                 num_blocks, key_scale, value_scale, H_kv, D, committed_length,
                                 status, (hipStream_t)stream);
+}
+
+int prepare_and_append(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B, int T,
+                       int32_t* seqlens_q, int32_t* seqlens_k, int32_t* token_req,
+                       int32_t* token_pos, const void* k_new, const void* v_new, int new_dtype,
+                       void* k_cache, void* v_cache, int cache_dtype, const int32_t* block_table,
+                       int max_blocks_per_seq, int block_size, int num_blocks,
+                       const float* key_scale, const float* value_scale, int H_kv, int D,
+                       const int32_t* committed_length, int32_t* status, void* stream) {
+  // the checks of both calls, before anything is enqueued
+  if (B < 0 || B > 8192 || T < 0) return SPATTN_ERR_SHAPE;
+  if (cu_seqlens_q == nullptr || past_seqlens == nullptr || seqlens_q == nullptr || seqlens_k == nullptr)
+    return SPATTN_ERR_NULL;
+  if (H_kv < 1 || D < 8 || D % 8 != 0) return SPATTN_ERR_SHAPE;
+  if (!float_dtype(new_dtype)) return SPATTN_ERR_DTYPE;
+  if (!quantised_cache(cache_dtype) && !float_dtype(cache_dtype)) return SPATTN_ERR_DTYPE;
+  if (T > 0) {
+    if (B == 0) return SPATTN_ERR_SHAPE;
+    if (k_new == nullptr || v_new == nullptr) return SPATTN_ERR_NULL;
+    const int rc = check_cache(k_cache, v_cache, new_dtype, cache_dtype, block_table,
+                               max_blocks_per_seq, block_size, num_blocks, key_scale, value_scale,
+                               B, H_kv, D);
+    if (rc != SPATTN_OK) return rc;
+  }
+  return spattn::launch_prepare_and_append(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k,
+                                           token_req, token_pos, k_new, v_new, new_dtype, k_cache,
+                                           v_cache, cache_dtype, block_table, max_blocks_per_seq,
+                                           block_size, num_blocks, key_scale, value_scale, H_kv, D,
+                                           committed_length, status, (hipStream_t)stream);
 }
 
 int qkv_prologue(const void* qkv, const void* q, const void* k, const void* v, int dtype,

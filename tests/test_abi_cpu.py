@@ -19,7 +19,8 @@ def _declared():
 
 def test_header_declares_the_abi():
     names = _declared()
-    assert set(names) == {"prepare_seqlens", "kv_cache_append", "qkv_prologue", "topk_select",
+    assert set(names) == {"prepare_seqlens", "kv_cache_append", "prepare_and_append",
+                          "qkv_prologue", "topk_select",
                           "paged_attention_fwd", "sparse_attention_fwd",
                           "attention_workspace_bytes"}
 
@@ -153,6 +154,28 @@ def test_prologue_argument_errors(lib):
     assert call(a29=0) == -2                   # block size
     assert call(a8=0) == 0                     # no rows: nothing to do
     assert call(a7=0) == -2                    # rows but no request
+
+
+def test_prepare_and_append_argument_errors(lib):
+    f = lib.prepare_and_append
+    # cu, past, B, T, sq, sk, treq, tpos, k_new, v_new, new_dt, kc, vc, cache_dt, bt, mbps,
+    # bs, nb, ks, vs, H_kv, D, committed, status, stream
+    base = [FAKE, FAKE, 2, 4, FAKE, FAKE, None, None, FAKE, FAKE, 1, FAKE, FAKE, 1, FAKE, 4, 16,
+            8, None, None, 2, 64, None, None, None]
+    def call(**kv):
+        a = list(base)
+        for i, v in kv.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a2=8193) == -2
+    assert call(a1=None) == -1
+    assert call(a5=None) == -1
+    assert call(a10=3) == -3           # int8 rows
+    assert call(a13=3) == -1           # int8 cache without scales
+    assert call(a21=60) == -2
+    assert call(a16=0) == -2           # block size
+    assert call(a2=0) == -2            # rows but no request
+    assert call(a8=None) == -1
 
 
 def test_topk_argument_errors(lib):

@@ -49,9 +49,8 @@ def test_decode_prefill_sparse_step_in_one_graph():
                         tp["v_cache"], tp["block_table"])
 
     def step():
-        sta.prepare_seqlens(td["cu"], td["past"], dec.T, sq, sk, status=st)
-        sta.kv_cache_append(td["k_new"], td["v_new"], td["cu"], sk, td["k_cache"], td["v_cache"],
-                            td["block_table"], status=st)
+        sta.prepare_and_append(td["cu"], td["past"], dec.T, sq, sk, td["k_new"], td["v_new"],
+                               td["k_cache"], td["v_cache"], td["block_table"], status=st)
         sta.paged_attention_fwd(td["q"], td["k_cache"], td["v_cache"], td["cu"], sk,
                                 dec.max_seqlen_q, dec.max_seqlen_k, out_d,
                                 block_table=td["block_table"], scale=dec.scale,

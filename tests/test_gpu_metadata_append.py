@@ -231,3 +231,85 @@ def test_append_fp8_hand_worked_codes():
     torch.cuda.synchronize()
     got = kc.cpu().view(torch.uint8).numpy().reshape(-1)
     assert got[:len(cases)].tolist() == want[:len(cases)].tolist()
+
+
+# ---- prepare_and_append: the two calls above in one launch -------------------------------
+
+def _fused_vs_separate(case, cu=None, past=None, committed=None):
+    """Run prepare_and_append and (on copies of the caches) prepare_seqlens then
+    kv_cache_append; every output, every cache byte and the status must be identical."""
+    t = case_tensors(case)
+    cu_t = tensor(np.asarray(cu if cu is not None else case.cu_seqlens_q, dtype=np.int32))
+    past_t = tensor(np.asarray(past if past is not None else case.past_seqlens, dtype=np.int32))
+    cm = tensor(committed) if committed is not None else None
+    B, T = int(past_t.shape[0]), case.T
+    out = {}
+    for mode in ("fused", "separate"):
+        kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
+        sq = torch.full((B,), 777, dtype=torch.int32, device="cuda")
+        sk = torch.full((B,), 777, dtype=torch.int32, device="cuda")
+        req = torch.full((T,), 777, dtype=torch.int32, device="cuda")
+        pos = torch.full((T,), 777, dtype=torch.int32, device="cuda")
+        st = status_tensor()
+        if mode == "fused":
+            sta.prepare_and_append(cu_t, past_t, T, sq, sk, t["k_new"], t["v_new"], kc, vc,
+                                   t["block_table"], token_req=req, token_pos=pos,
+                                   key_scale=t["key_scale"], value_scale=t["value_scale"],
+                                   committed_length=cm, status=st)
+        else:
+            sta.prepare_seqlens(cu_t, past_t, T, sq, sk, req, pos, st)
+            sta.kv_cache_append(t["k_new"], t["v_new"], cu_t, sk, kc, vc, t["block_table"],
+                                t["key_scale"], t["value_scale"], status=st, committed_length=cm)
+        torch.cuda.synchronize()
+        out[mode] = (sq.cpu(), sk.cpu(), req.cpu(), pos.cpu(), _bits(kc).cpu(), _bits(vc).cpu(),
+                     int(st.item()))
+    for name, a, b in zip(("seqlens_q", "seqlens_k", "token_req", "token_pos", "k_cache", "v_cache"),
+                          out["fused"][:6], out["separate"][:6]):
+        assert torch.equal(a, b), name
+    assert out["fused"][6] == out["separate"][6]
+    return out["fused"]
+
+
+@pytest.mark.parametrize("cache_dtype", [None, synth.I8, synth.FP8])
+def test_prepare_and_append_decode_step(cache_dtype):
+    print("prepare_and_append decode", cache_dtype, flush=True)
+    base = synth.config_gqa_paged_decode(B=32, max_len=3000, seed=41)
+    case = synth.paged_case(42, kv_lens=base.seqlens_k + 1, q_lens=np.diff(base.cu_seqlens_q), H_q=8,
+                            H_kv=8, D=64, dtype=synth.F16, cache_dtype=cache_dtype, poison=True)
+    sq, sk, req, pos, _, _, st = _fused_vs_separate(case)
+    o = oracle.prepare_seqlens(case.cu_seqlens_q, case.past_seqlens, case.T)
+    assert np.array_equal(sk.numpy(), o[1]) and np.array_equal(pos.numpy(), o[3]) and st == 0
+
+
+def test_prepare_and_append_prefill_and_cursor():
+    print("prepare_and_append prefill", flush=True)
+    case = synth.paged_case(43, kv_lens=[300, 77, 1, 64], q_lens=[300, 20, 1, 0], H_q=4, H_kv=2, D=128,
+                            dtype=synth.BF16, poison=True)
+    _fused_vs_separate(case)
+    committed = np.array([0, 57, 5, 64], dtype=np.int32)   # request 2 disagrees
+    *_, st = _fused_vs_separate(case, committed=committed)
+    assert st == sta.STATUS_CURSOR
+
+
+@pytest.mark.parametrize("cu,past", [
+    ([0, 3, 2, 5], [0, 0, 0]),          # decreasing boundary
+    ([1, 3, 5], [4, 0]),                # cu[0] != 0
+    ([0, 2, 9], [0, 0]),                # cu[B] > T
+    ([0, 1, 5], [-4, 0]),               # negative past
+])
+def test_prepare_and_append_malformed(cu, past):
+    """Malformed metadata: both paths sanitise and flag the same way, byte for byte."""
+    print("prepare_and_append malformed", cu, past, flush=True)
+    case = synth.paged_case(44, kv_lens=[8, 8], q_lens=[2, 3], H_q=4, H_kv=2, D=64, dtype=synth.F16,
+                            num_blocks=8)
+    _fused_vs_separate(case, cu=cu, past=past)
+
+
+def test_prepare_and_append_many_requests_fall_back():
+    """More than 255 requests: the two kernels run in order behind the same call."""
+    print("prepare_and_append B=300", flush=True)
+    rng = np.random.default_rng(45)
+    kv = rng.integers(1, 40, size=300)
+    case = synth.paged_case(46, kv_lens=kv, q_lens=np.ones(300, dtype=np.int64), H_q=4, H_kv=2, D=64,
+                            dtype=synth.F16)
+    _fused_vs_separate(case)
