@@ -513,8 +513,9 @@ def main():
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
-              "(the path needs no cross-GPU exchange; see DESIGN.md for how it would shard)",
+        print(f"bench.py: --gpus {args.gpus} is not supported: bench.py measures one GPU "
+              "(the path shards by request or by KV head with no exchange; a key range split over "
+              "GPUs needs one all-gather of split partials before the merge)",
               file=sys.stderr)
         sys.exit(2)
     import torch
