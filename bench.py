@@ -15,7 +15,7 @@ and of the same without a window are reported alongside, as the metric names bot
 are the selected-token and local-plus-auxiliary decode, the QKV prologue and the TopK
 selection (each call preceded by a 1 GiB read, so the caches hold none of its inputs).
 
-`--gpus N` with N > 1 is not supported: this build runs on one GPU.
+`--gpus N` with N > 1 is not supported: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
