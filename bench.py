@@ -38,8 +38,8 @@ METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged
 # WRITE_SIZE counter passes scaled by the same counters' reading on a plain device copy of
 # known size (profiles/decode_gqa_paged_f16_traffic.md).  Valid only for the kernel sources
 # whose digest is recorded with it; any other source reports traffic = null.
-MEASURED_TRAFFIC = {"sources_sha1": "0e9a92249b17b3d2193bdda8617836d13c8a05d2",
-                    "bytes_per_call": 286123040}
+MEASURED_TRAFFIC = {"sources_sha1": "83b19a89f7cffdd89b4f5060976f39e0e5448cd0",
+                    "bytes_per_call": 286082135}
 KERNEL_SOURCES = ("selected_token_sparse_amd/csrc/decode.hip", "selected_token_sparse_amd/csrc/common.h",
                   "selected_token_sparse_amd/csrc/launch.h")
 
