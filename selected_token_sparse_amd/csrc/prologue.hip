@@ -22,7 +22,7 @@ namespace spattn {
 
 constexpr int kProWaves = 4;
 constexpr int kProThreads = kProWaves * 64;
-constexpr int kProDeepMinBlocks = 1024;   // workgroups a 4-batch launch must still have
+constexpr int kProDeepMinBlocks = 1024;   // workgroups a 2-batch launch must still have
 
 struct PrologueParams {
   const void* qkv;          // packed rows, or nullptr
@@ -345,21 +345,22 @@ int launch_qkv_prologue(const PrologueArgs& a, hipStream_t stream) {
   P.G = a.D / 8;
   P.rows_per_wave = 64 / P.G;
   P.n_rows = (int64_t)a.T * (a.H_q + 2 * a.H_kv);
-  // four row batches per wave once there are enough rows to fill the chip that way
-  // (more bytes in flight per wave); one batch otherwise (more workgroups)
+  // two row batches per wave once there are enough rows to fill the chip that way (more
+  // bytes in flight per wave; measured at 5120 rows: 1 batch 49.6 us, 2 batches 42.8,
+  // 4 batches 51.8, 8 batches 61.7, as registers cut occupancy); one batch otherwise
   const int64_t rows_one = (int64_t)kProWaves * P.rows_per_wave;
-  // (the tokens a wave spans must fit its 64 lanes: 4 * rows_per_wave rows span at most
-  // (4 * rows_per_wave - 1) / NH + 2 tokens)
+  // (the tokens a wave spans must fit its 64 lanes: 2 * rows_per_wave rows span at most
+  // (2 * rows_per_wave - 1) / NH + 2 tokens)
   const int NH = a.H_q + 2 * a.H_kv;
-  const bool deep = P.n_rows >= (int64_t)kProDeepMinBlocks * 4 * rows_one &&
-                    (4 * P.rows_per_wave - 1) / NH + 2 <= 64;
-  const int64_t rows_per_block = rows_one * (deep ? 4 : 1);
+  const bool deep = P.n_rows >= (int64_t)kProDeepMinBlocks * 2 * rows_one &&
+                    (2 * P.rows_per_wave - 1) / NH + 2 <= 64;
+  const int64_t rows_per_block = rows_one * (deep ? 2 : 1);
   const int64_t blocks = (P.n_rows + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7FFFFFFF) return SPATTN_ERR_SHAPE;
   dim3 grid((unsigned)blocks), block(kProThreads);
   const int quant = a.cache_dtype == SPATTN_I8 ? 1 : (a.cache_dtype == SPATTN_FP8 ? 2 : 0);
 #define SPATTN_PROLOGUE(TT, Q)                                                                \
-  if (deep) hipLaunchKernelGGL((qkv_prologue_kernel<TT, Q, 4>), grid, block, 0, stream, P);  \
+  if (deep) hipLaunchKernelGGL((qkv_prologue_kernel<TT, Q, 2>), grid, block, 0, stream, P);  \
   else hipLaunchKernelGGL((qkv_prologue_kernel<TT, Q, 1>), grid, block, 0, stream, P)
 #define SPATTN_PROLOGUE_Q(TT)                   \
   if (quant == 1) { SPATTN_PROLOGUE(TT, 1); }   \

@@ -247,8 +247,8 @@ def test_full_size_prefill_shape():
                                         cache_dtype=synth.I8, explicit_positions=True)),
 ], ids=lambda v: v if isinstance(v, str) else "")
 def test_many_rows_take_the_batched_launch(name, kw):
-    """Enough rows (>= 131072 at D = 64) for the launch that gives each wave four row
-    batches; the other shapes take one batch per wave."""
+    """Enough rows (>= 65536 at D = 64, 57344 at D = 72, 32768 at D = 128) for the launch
+    that gives each wave two row batches; the other shapes take one batch per wave."""
     case = synth.prologue_case(seed=26, dtype=synth.F16, poison=False, **kw)
     _check(case, name)
 
