@@ -129,8 +129,8 @@ __device__ __forceinline__ int wave_or_flags(int flags) {
 // loop), then the split's cache-row indices, then the staged metadata.
 template <int D>
 struct SplitLds {
-  static constexpr bool kDeep = D == 64;  // two tiles in flight per wave at D = 64
-  static constexpr int kVTileBytes = (kDeep ? 2 : 1) * kTile * D * 2;  // a wave's V tiles
+  // two tiles in flight per wave: a wave's two V tile buffers
+  static constexpr int kVTileBytes = 2 * kTile * D * 2;
   static constexpr int kCombineRow = D + 4;   // floats per (wave, head) row of the combine area
   static constexpr int kCombineBytes = (kWaves * 16 * kCombineRow + 4 * kWaves * 16) * 4;
   static constexpr int kAreaBytes = (kWaves * kVTileBytes > kCombineBytes) ? kWaves * kVTileBytes : kCombineBytes;
@@ -299,7 +299,6 @@ __device__ __forceinline__ void wave_keys(const KT* __restrict__ kbase, const KT
                                           float& l_run, f32x4 (&acc)[D / 16]) {
   constexpr int kTileBytes = (D / 32) * 2 * 1024;
   constexpr int kOps = 4 * (D / 32);   // vector memory instructions per tile
-  constexpr bool kDeep = SplitLds<D>::kDeep;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lam = lane & 15;
@@ -312,18 +311,6 @@ __device__ __forceinline__ void wave_keys(const KT* __restrict__ kbase, const KT
   TileRegs<OpT, KT, D> ta, tb;
   int tile = wave;
   if (tile >= n_tiles) return;
-  if constexpr (!kDeep) {
-    // one tile at a time (wider heads need the registers for more waves instead)
-    for (; tile < n_tiles; tile += kWaves) {
-      const int r0 = row_of(tile, lam), r1 = row_of(tile, 16 + lam);
-      const uint32_t v = tile_valid(r0, r1);
-      wait_lgkm0();
-      issue_tile<OpT, KT, D>(ta, kbase, vbase, dk, dv, r0, r1, vbuf2, grp);
-      wait_vm<0>();
-      consume_tile<OpT, KT, D>(ta, v, qop, scale_log2, vbuf2, m_run, l_run, acc, lam, grp);
-    }
-    return;
-  }
   int a0 = row_of(tile, lam), a1 = row_of(tile, 16 + lam);
   uint32_t va = tile_valid(a0, a1);
   issue_tile<OpT, KT, D>(ta, kbase, vbase, dk, dv, a0, a1, vbuf2, grp);
