@@ -38,8 +38,8 @@ METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged
 # WRITE_SIZE counter passes scaled by the same counters' reading on a plain device copy of
 # known size (profiles/decode_gqa_paged_f16_traffic.md).  Valid only for the kernel sources
 # whose digest is recorded with it; any other source reports traffic = null.
-MEASURED_TRAFFIC = {"sources_sha1": "83b19a89f7cffdd89b4f5060976f39e0e5448cd0",
-                    "bytes_per_call": 286082135}
+MEASURED_TRAFFIC = {"sources_sha1": "625ea71fc11bbf9ca25ed753a21cc3d066fed212",
+                    "bytes_per_call": 286086350}
 KERNEL_SOURCES = ("selected_token_sparse_amd/csrc/decode.hip", "selected_token_sparse_amd/csrc/common.h",
                   "selected_token_sparse_amd/csrc/launch.h")
 
