@@ -23,6 +23,16 @@ constexpr int kPfThreads = 256;
 constexpr int kPfTile = 32;
 
 template <typename T> struct Op32;
+
+// a + b + c in fp32 for two 16-bit values (v_dot2c_f32_{f16,bf16} against (1, 1))
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_ones(f16 a, f16 b, float c) {
+  return __builtin_amdgcn_fdot2(f16x2{a, b}, f16x2{(f16)1.f, (f16)1.f}, c, false);
+}
+__device__ __forceinline__ float dot2_ones(bf16 a, bf16 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a, b}, bf16x2{(bf16)1.f, (bf16)1.f}, c, false);
+}
 template <> struct Op32<f16> { typedef f16x8 v8; typedef f16x4 v4; };
 template <> struct Op32<bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
 
@@ -331,6 +341,15 @@ void prefill_kernel(PrefillParams P) {
   // (wave w issues q = w * kDmaPerWave + n) fills 16-byte positions 64q .. 64q + 63, i.e.
   // key p / CHK, slot p % CHK, which holds the key's chunk slot ^ (key mod CHK).
   constexpr int kDmaPerWave = kPfTile * CHK / (64 * (kPfThreads / 64));
+  // Paged cache with a power-of-two block size and blocks under 4 GiB apart: the byte
+  // address of key j is  base + blk * blk_bytes + (j mod bs) * row_bytes + column bytes,
+  // formed with one 32 x 32 -> 64-bit multiply-add per tile instead of the general
+  // element-offset arithmetic of key_row.
+  const uint64_t blk_bytes64 = (uint64_t)blk_stride * sizeof(KT);
+  const bool dma_fast = paged && pow2 && blk_bytes64 < (1ull << 32);
+  const uint32_t blk_bytes = (uint32_t)P.cd.H_kv * (uint32_t)bs * (uint32_t)(D * sizeof(KT));
+  const char* kbytes = reinterpret_cast<const char*>(kcache + head_off);
+  const char* vbytes = reinterpret_cast<const char*>(vcache + head_off);
   auto issue_dma = [&](int kt, int stage) {
     unsigned char* base = smem + stage * L::kStage;
     int32_t* vb = reinterpret_cast<int32_t*>(base + L::kKBytes + L::kVBytes);
@@ -342,9 +361,27 @@ void prefill_kernel(PrefillParams P) {
       const int key = p / CHK, slot = p % CHK;
       const int col = (slot ^ (key & (CHK - 1))) * 8;
       bool ok;
-      const int64_t off = key_row(kt + key, ok) + col;
-      const KT* kp = ok ? kcache + off : safe_k + col;
-      const KT* vp = ok ? vcache + off : safe_v + col;
+      const KT* kp;
+      const KT* vp;
+      if (dma_fast) {
+        const int j = kt + key;
+        const int lb = j >> P.cd.bs_shift;
+        const int blk = bt_lds[min(max(lb - win_lb, 0), L::kBtCap - 1)];
+        const bool in_range = j >= j_lo && j <= j_hi;
+        const bool in_tab = lb < P.cd.max_blocks;
+        const bool blk_ok = (unsigned)blk < (unsigned)P.cd.num_blocks;
+        if (in_range && !(in_tab && blk_ok))
+          flags |= in_tab ? SPATTN_STATUS_BAD_BLOCK : SPATTN_STATUS_CAPACITY;
+        ok = in_range && in_tab && blk_ok;
+        const uint32_t in_blk = (uint32_t)((j & (bs - 1)) * D + col) * (uint32_t)sizeof(KT);
+        const uint64_t boff = (uint64_t)(uint32_t)blk * blk_bytes + in_blk;
+        kp = ok ? reinterpret_cast<const KT*>(kbytes + boff) : safe_k + col;
+        vp = ok ? reinterpret_cast<const KT*>(vbytes + boff) : safe_v + col;
+      } else {
+        const int64_t off = key_row(kt + key, ok) + col;
+        kp = ok ? kcache + off : safe_k + col;
+        vp = ok ? vcache + off : safe_v + col;
+      }
       pf_dma16(kp, base + q * 1024);
       pf_dma16(vp, base + L::kKBytes + q * 1024);
       if (slot == 0) vb[key] = ok ? 1 : 0;
@@ -462,11 +499,12 @@ void prefill_kernel(PrefillParams P) {
       const float nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
       V8 pop[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2_safe(__builtin_fmaf(s[i], c_scale, nm));
-        l_run += p;                                 // this lane's part of the row sum
-        pop[i >> 3][i & 7] = (OpT)p;
-      }
+      for (int i = 0; i < 16; ++i)
+        pop[i >> 3][i & 7] = (OpT)exp2_safe(__builtin_fmaf(s[i], c_scale, nm));
+      // this lane's part of the row sum, over the rounded weights the PV product uses, two
+      // per instruction (products with 1 are exact; the sum is fp32)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) l_run = dot2_ones(pop[i >> 3][i & 7], pop[i >> 3][(i & 7) + 1], l_run);
       {
         const int grp = lane >> 4, lam = lane & 15;
 #pragma unroll

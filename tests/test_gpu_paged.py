@@ -131,6 +131,20 @@ def test_deterministic_repeat():
     assert torch.equal(a.cpu().view(torch.int16), b.cpu().view(torch.int16))
 
 
+def test_host_bounds_change_only_the_plan():
+    """The host bounds size the launch, not the result: a loose key bound (more, partly empty
+    splits) and a query bound above 8 (the MFMA prefill kernel on decode rows) both match the
+    oracle on the same decode step."""
+    base = synth.paged_case(41, kv_lens=[700, 1, 0, 2500, 64], q_lens=[1, 1, 0, 1, 1], H_q=16,
+                            H_kv=2, D=64, dtype=synth.F16, sinks=True, poison=True)
+    for mq, mk in ((base.max_seqlen_q, base.max_seqlen_k), (base.max_seqlen_q, 8 * base.max_seqlen_k),
+                   (16, base.max_seqlen_k)):
+        case = synth.paged_case(41, kv_lens=[700, 1, 0, 2500, 64], q_lens=[1, 1, 0, 1, 1], H_q=16,
+                                H_kv=2, D=64, dtype=synth.F16, sinks=True, poison=True)
+        case.max_seqlen_q, case.max_seqlen_k = mq, mk
+        _check_full(case, f"bounds_q{mq}_k{mk}")
+
+
 def test_bound_violations_zero_rows():
     for mq in (4, 40):
         case = synth.paged_case(31, kv_lens=[40, 100, 30], q_lens=[10, 1, 30], H_q=8, H_kv=2, D=64,
