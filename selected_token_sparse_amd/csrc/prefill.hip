@@ -66,8 +66,8 @@ struct PrefillParams {
 
 // LDS stage of a 32-key K/V tile.  16-bit caches arrive by LDS DMA, which writes each
 // lane's 16 bytes at a fixed place, so their rows are unpadded and the 16-byte chunks of key
-// k are XOR-swizzled by k (chunk c sits in slot c ^ (k mod D/8)) to spread the operand reads
-// over the banks; INT8 caches are converted in registers and stored with padded rows.
+// k are XOR-swizzled by k (pf_swizzle) to spread the operand reads over the banks; INT8
+// caches are converted in registers and stored with padded rows.
 template <int D, bool kDma>
 struct PfLds {
   static constexpr int kKld = kDma ? D : D + 8;    // K tile row (elements)
@@ -82,6 +82,17 @@ struct PfLds {
   static constexpr int kTotal = kBtOffset + kBtCap * 4;
   static_assert(kStage % 16 == 0, "DMA destinations are 16-byte aligned");
 };
+
+// Slot XOR of key kk's 16-byte chunks in a DMA-staged tile row (chunk c sits in slot
+// c ^ pf_swizzle(kk)).  At D = 64 the XOR is a bit rotation of kk mod 8, so the four keys
+// one transposed V read of 16 lanes covers (kk = 4i .. 4i + 3) land in four different
+// 32-byte slot pairs, while any 8 consecutive keys still get 8 different XORs for the K
+// operand reads; measured, it halves the LDS bank-conflict cycles of the kernel.
+template <int D>
+__device__ __forceinline__ int pf_swizzle(int kk) {
+  if constexpr (D == 64) return ((kk & 3) << 1) | ((kk >> 2) & 1);
+  else return kk & (D / 8 - 1);
+}
 
 // LDS-DMA of 16 bytes per lane (lane l's bytes land at lds + 16 * l) and the waits the
 // compiler does not insert for it.
@@ -339,7 +350,7 @@ void prefill_kernel(PrefillParams P) {
   };
   // 16-bit caches: DMA of a tile straight into an LDS stage.  Instruction q of the tile
   // (wave w issues q = w * kDmaPerWave + n) fills 16-byte positions 64q .. 64q + 63, i.e.
-  // key p / CHK, slot p % CHK, which holds the key's chunk slot ^ (key mod CHK).
+  // key p / CHK, slot p % CHK, which holds the key's chunk slot ^ pf_swizzle(key).
   constexpr int kDmaPerWave = kPfTile * CHK / (64 * (kPfThreads / 64));
   // Paged cache with a power-of-two block size and blocks under 4 GiB apart: the byte
   // address of key j is  base + blk * blk_bytes + (j mod bs) * row_bytes + column bytes,
@@ -359,7 +370,7 @@ void prefill_kernel(PrefillParams P) {
       const int q = wave * kDmaPerWave + n;
       const int p = q * 64 + lane;
       const int key = p / CHK, slot = p % CHK;
-      const int col = (slot ^ (key & (CHK - 1))) * 8;
+      const int col = (slot ^ pf_swizzle<D>(key)) * 8;
       bool ok;
       const KT* kp;
       const KT* vp;
@@ -436,11 +447,11 @@ void prefill_kernel(PrefillParams P) {
 
   // byte offset of logical 16-byte chunk c of key kk within a K / V tile
   auto k_chunk = [&](int kk, int c) -> int {
-    if constexpr (kDma) return kk * D * 2 + ((c ^ (kk & (CHK - 1))) << 4);
+    if constexpr (kDma) return kk * D * 2 + ((c ^ pf_swizzle<D>(kk)) << 4);
     else return (kk * L::kKld + c * 8) * 2;
   };
   auto v_chunk = [&](int kk, int c) -> int {
-    if constexpr (kDma) return kk * D * 2 + ((c ^ (kk & (CHK - 1))) << 4);
+    if constexpr (kDma) return kk * D * 2 + ((c ^ pf_swizzle<D>(kk)) << 4);
     else return (kk * L::kVld + c * 8) * 2;
   };
   auto compute_tile = [&](int it, int stage) {
