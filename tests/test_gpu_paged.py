@@ -55,6 +55,9 @@ DECODE = [
     ("bf16_fp8_cache_w9", dict(kv_lens=[70, 33], q_lens=[2, 1], H_q=8, H_kv=2, D=64, dtype=synth.BF16, cache_dtype=synth.FP8, local_window=9)),
     ("f32_fp8_cache", dict(kv_lens=[45, 130], q_lens=[2, 1], H_q=4, H_kv=2, D=64, dtype=synth.F32, cache_dtype=synth.FP8, sinks=True)),
     ("f16_fp8_contig_long", dict(kv_lens=[3000, 9], q_lens=[1, 1], H_q=16, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.FP8, contiguous=True, capacity=3000, sinks=True)),
+    # long contexts: 100k keys (391 splits of the key range) and a 4096-key window at 70k
+    ("f16_long_context_100k", dict(kv_lens=[100000, 3, 40000], q_lens=[1, 1, 2], H_q=8, H_kv=1, D=64, dtype=synth.F16, sinks=True)),
+    ("bf16_d128_70k_w4096", dict(kv_lens=[70000], q_lens=[3], H_q=12, H_kv=1, D=128, dtype=synth.BF16, local_window=4096)),
 ]
 
 
@@ -82,6 +85,8 @@ PREFILL = [
     # global memory instead of the staged copy
     ("f16_bs4_long_table", dict(kv_lens=[2100, 70], q_lens=[40, 70], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=4, sinks=True)),
     ("bf16_bs4_long_table_d128", dict(kv_lens=[2300], q_lens=[33], H_q=4, H_kv=1, D=128, dtype=synth.BF16, block_size=4)),
+    # a chunk of 700 rows appended at position 5300 of a 6000-key history, window 256
+    ("f16_long_history_chunk_w256", dict(kv_lens=[6000], q_lens=[700], H_q=8, H_kv=2, D=64, dtype=synth.F16, local_window=256, sinks=True)),
 ]
 
 

@@ -38,6 +38,8 @@ SELECTED = [
     ("f32_g3", dict(B=2, S_q=2, H_q=6, H_kv=2, D=64, capacity=300, max_selected=50, dtype=synth.F32, sinks=True, oor_frac=0.05)),
     ("f16_paged_main", dict(B=3, S_q=2, H_q=16, H_kv=2, D=64, capacity=600, kv_lens=[600, 250, 17], max_selected=128, dtype=synth.F16, sinks=True, block_size=16, oor_frac=0.03)),
     ("f16_g20_two_tiles", dict(B=1, S_q=2, H_q=40, H_kv=2, D=64, capacity=300, max_selected=90, dtype=synth.F16, sinks=True)),
+    # 16384 selected positions of a 100k-key cache
+    ("f16_16k_of_100k", dict(B=1, S_q=2, H_q=12, H_kv=1, D=128, capacity=100000, max_selected=16384, dtype=synth.F16, sinks=True, oor_frac=0.01)),
 ]
 
 
