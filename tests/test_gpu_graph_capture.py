@@ -1,5 +1,6 @@
-"""The calls need no host synchronisation: the metadata pass, the cache append and both
-attention entry points are recorded into one HIP graph and replayed.  ("[WebGPU] Add
+"""The calls need no host synchronisation: the metadata pass, the cache append, both
+attention entry points, the QKV prologue and the TopK selection are recorded into HIP
+graphs and replayed.  ("[WebGPU] Add
 PagedAttention metadata and GPT-OSS support", Description: sequence lengths are produced
 on the device so the step needs no readback and can be replayed.)
 
@@ -11,9 +12,10 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import selected_token_sparse_amd as sta
 import synth
-from synth.device import TORCH_DTYPE, case_tensors
+from synth.device import TORCH_DTYPE, case_tensors, tensor
 
 from harness import assert_close, oracle_paged_step, oracle_sparse, status_tensor
 
@@ -163,4 +165,68 @@ def test_multi_layer_decode_step_in_one_graph():
         torch.cuda.synchronize()
         for i, (o, e) in enumerate(zip(outs, eager)):
             assert torch.equal(o.view(torch.int16), e.view(torch.int16)), (rep, i)
+    assert int(st.item()) == 0
+
+
+def test_prologue_and_topk_in_one_graph():
+    """The prologue (norm, rotation, cache append) and the TopK selection record into one
+    graph too: every replay reproduces the eager query rows, cache and selection bit for
+    bit, and the eager selection matches the oracle exactly."""
+    pc = synth.prologue_case(97, kv_lens=[300, 41], q_lens=[4, 1], H_q=16, H_kv=2, D=128,
+                             packed=True, rotary_dim=64, qk_norm=True, explicit_positions=True,
+                             max_position=4096, offsets=True)
+    tk = synth.topk_case(98, kv_lens=[5000, 3000], q_lens=[4, 1], H_kv=2, L=5000, k=300,
+                         tail=16, capacity=320, ties=0.2, specials=0.01)
+    dt = pc.dtype
+    t = dict(qkv=tensor(pc.qkv, dt), cu=tensor(pc.cu_seqlens_q), sk=tensor(pc.seqlens_k),
+             kc=tensor(pc.k_cache, pc.cache_dtype), vc=tensor(pc.v_cache, pc.cache_dtype),
+             bt=tensor(pc.block_table), qw=tensor(pc.q_norm_weight), kw=tensor(pc.k_norm_weight),
+             cos=tensor(pc.cos_table), sin=tensor(pc.sin_table), pos=tensor(pc.position_ids),
+             offs=tensor(pc.rotary_offsets))
+    scores, tcu, tsk = tensor(tk.scores), tensor(tk.cu_seqlens_q), tensor(tk.seqlens_k)
+    q_out = torch.empty((pc.T, pc.H_q, pc.D), dtype=TORCH_DTYPE[dt], device="cuda")
+    sel = torch.empty((tk.T, tk.H_kv, tk.capacity), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((tk.T, tk.H_kv), dtype=torch.int32, device="cuda")
+    st = status_tensor()
+
+    def step():
+        sta.qkv_prologue(q_out, t["kc"], t["vc"], t["cu"], t["sk"], H_q=pc.H_q, H_kv=pc.H_kv,
+                         qkv=t["qkv"], qk_norm=True, q_norm_weight=t["qw"], k_norm_weight=t["kw"],
+                         norm_eps=pc.norm_eps, rotary_dim=pc.rotary_dim,
+                         interleaved=pc.interleaved, cos_table=t["cos"], sin_table=t["sin"],
+                         position_ids=t["pos"], rotary_offsets=t["offs"], block_table=t["bt"],
+                         status=st)
+        sta.topk_select(scores, tcu, tsk, tk.k, sel, cnt, tail=tk.tail, status=st)
+
+    print("graph: eager prologue + topk", flush=True)
+    step()
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in (q_out, t["kc"], t["vc"], sel, cnt)]
+    assert int(st.item()) == 0
+    want_sel, want_cnt = oracle.topk_select(tk.scores, tk.cu_seqlens_q, tk.seqlens_k, k=tk.k,
+                                            tail=tk.tail, capacity=tk.capacity)
+    assert np.array_equal(cnt.cpu().numpy(), want_cnt)
+    assert np.array_equal(sel.cpu().numpy(), want_sel)
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    noise = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        print(f"graph: prologue + topk replay {rep}", flush=True)
+        q_out.fill_(float("nan"))
+        sel.fill_(-7)
+        cnt.fill_(-7)
+        (noise * 3.0).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((q_out, t["kc"], t["vc"], sel, cnt), eager):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), rep
     assert int(st.item()) == 0
