@@ -107,6 +107,13 @@ class ColdCache:
         torch.sum(self.buf, dim=0, keepdim=True, out=self.out)
 
 
+def _p10_p90(ms_sorted):
+    """10th and 90th percentiles (us) of sorted per-call times in ms."""
+    n = len(ms_sorted)
+    return (round(ms_sorted[min(n - 1, n // 10)] * 1e3, 2),
+            round(ms_sorted[min(n - 1, (9 * n) // 10)] * 1e3, 2))
+
+
 def _events():
     import torch
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -269,6 +276,7 @@ def bench_prefill(window, steps, warmup):
     tfl = flops / (med * 1e-3) / 1e12
     return {
         "workload": case.name, "window": window, "median_us": round(med * 1e3, 2),
+        "p10_p90_us": _p10_p90(ms),
         "tflops": round(tfl, 2), "frac_mfma_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         "algorithmic_gflop": round(flops / 1e9, 3),
         "qo_gbs": round(qo_bytes / (med * 1e-3) / 1e9, 1),
@@ -345,7 +353,8 @@ def bench_sparse(which, steps, warmup):
     alg, main_keys, aux_keys = _sparse_bytes(case)
     gbs = alg / (med * 1e-3) / 1e9
     return {"workload": case.name, "median_us": round(med * 1e3, 2),
-            "avg_us": round(sum(ms) / len(ms) * 1e3, 2), "algorithmic_bytes": alg,
+            "avg_us": round(sum(ms) / len(ms) * 1e3, 2), "p10_p90_us": _p10_p90(ms),
+            "algorithmic_bytes": alg,
             "main_keys": main_keys, "aux_keys": aux_keys, "gbs": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "status": int(status.item())}
 
@@ -409,7 +418,8 @@ def bench_prologue(shape, steps, warmup):
     alg = _prologue_bytes(case)
     gbs = alg / (med * 1e-3) / 1e9
     return {"workload": name, "median_us": round(med * 1e3, 2),
-            "avg_us": round(sum(ms) / len(ms) * 1e3, 2), "algorithmic_bytes": alg,
+            "avg_us": round(sum(ms) / len(ms) * 1e3, 2), "p10_p90_us": _p10_p90(ms),
+            "algorithmic_bytes": alg,
             "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "status": int(status.item())}
 
@@ -449,6 +459,7 @@ def bench_topk(steps, warmup):
     gbs = alg / (med * 1e-3) / 1e9
     return {"workload": "topk_selected_decode (128 rows x 4 KV heads, 65536 scores, k 2048, tail 64)",
             "median_us": round(med * 1e3, 2), "avg_us": round(sum(ms) / len(ms) * 1e3, 2),
+            "p10_p90_us": _p10_p90(ms),
             "algorithmic_bytes": alg, "gbs": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
@@ -552,6 +563,7 @@ def main():
                      "kernel": "paged_attention_fwd decode call: split-K kernel + merge kernel",
                      "kernel_sources_sha1": digest,
                      "avg_us": round(attn_avg * 1e3, 2), "median_us": round(attn_med * 1e3, 2),
+                     "p10_p90_us": _p10_p90(attn_ms),
                      "algorithmic_bytes": alg},
     }
     if not args.no_prefill:

@@ -72,3 +72,9 @@ def test_selected_bytes_count_visible_entries_one_by_one():
     total, main_keys, aux_keys = bench._sparse_bytes(case)
     assert main_keys == visible and aux_keys == 0
     assert total == visible * 2 * case.D * 2 + 2 * case.T * case.H_q * case.D * 2
+
+
+def test_percentiles_of_sorted_call_times():
+    ms = [0.001 * (i + 1) for i in range(100)]        # 1 .. 100 us
+    assert bench._p10_p90(ms) == (11.0, 91.0)
+    assert bench._p10_p90([0.005]) == (5.0, 5.0)
