@@ -119,14 +119,14 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_decode(steps, warmup, copies=3):
+def bench_decode(steps, warmup, copies=3, cache_dtype=None):
     import torch
 
     import selected_token_sparse_amd as sta
     import synth
     from synth.device import case_tensors, tensor
 
-    case = synth.config_gqa_paged_decode()
+    case = synth.config_gqa_paged_decode(cache_dtype=synth.F16 if cache_dtype is None else cache_dtype)
     base = case_tensors(case)
     sets = [base]
     for _ in range(copies - 1):
@@ -145,11 +145,13 @@ def bench_decode(steps, warmup, copies=3):
         t = sets[i % copies]
         # metadata and the cache append of this step's rows: one launch
         sta.prepare_and_append(t["cu"], t["past"], T, sq, sk, t["k_new"], t["v_new"], t["k_cache"],
-                               t["v_cache"], t["block_table"], status=status)
+                               t["v_cache"], t["block_table"], key_scale=t["key_scale"],
+                               value_scale=t["value_scale"], status=status)
         if ev is not None:
             ev[0].record()
         sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], sk, case.max_seqlen_q,
                                 case.max_seqlen_k, out, block_table=t["block_table"],
+                                key_scale=t["key_scale"], value_scale=t["value_scale"],
                                 scale=case.scale, sinks=t["sinks"], workspace=ws, status=status)
         if ev is not None:
             ev[1].record()
@@ -522,6 +524,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
+    ap.add_argument("--no-quant", action="store_true", help="skip the FP8-cache decode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -571,6 +574,17 @@ def main():
         line["prefill_no_window"] = bench_prefill(-1, 30, 3)
     if not args.no_graph:
         line["decode_graph"] = bench_decode_graph()
+    if not args.no_quant:
+        import synth
+        qcase, q_ms_step, q_attn, q_st = bench_decode(50, 5, cache_dtype=synth.FP8)
+        q_kv = _kv_bytes(qcase)
+        q_avg = sum(q_attn) / len(q_attn)
+        line["decode_fp8"] = {
+            "workload": "the GQA paged decode with an FP8 E4M3 cache (per-channel scales)",
+            "kv_bytes_per_step": q_kv, "avg_us": round(q_avg * 1e3, 2),
+            "median_us": round(q_attn[len(q_attn) // 2] * 1e3, 2), "p10_p90_us": _p10_p90(q_attn),
+            "gbs": round(q_kv / (q_avg * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(q_kv / (q_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "status": q_st}
     if not args.no_sparse:
         line["selected_decode"] = bench_sparse("selected", 50, 5)
         line["local_plus_aux"] = bench_sparse("local_aux", 50, 5)

@@ -52,6 +52,19 @@ __device__ __forceinline__ uint16_t fp8_to_f16_bits(uint32_t b) {
   const uint32_t mag = b & 0x7Fu;
   return (uint16_t)(((b & 0x80u) << 8) | (mag << 7) | (mag == 0x7Fu ? 0x7C00u : 0u));
 }
+// Eight codes (the bytes of two 32-bit words, lowest first) as the same f16 operands, code
+// value / 256, by the gfx950 conversion instruction with a 2^-8 scale: two codes per
+// instruction instead of a few bit operations per code.  (Checked on the device for all
+// 256 codes: the values match the construction above exactly; NaN codes give NaN.)
+__device__ __forceinline__ f16x8 fp8x8_to_f16(int lo, int hi) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f / kFp8Unit, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f / kFp8Unit, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f / kFp8Unit, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f / kFp8Unit, true);
+  const i32x4 w = {__builtin_bit_cast(int32_t, a), __builtin_bit_cast(int32_t, b),
+                   __builtin_bit_cast(int32_t, c), __builtin_bit_cast(int32_t, d)};
+  return __builtin_bit_cast(f16x8, w);
+}
 // Exact value of a code (NaN codes give NaN).
 __device__ __forceinline__ float to_f32(uint8_t code) {
   return (float)__builtin_bit_cast(f16, fp8_to_f16_bits(code)) * kFp8Unit;

@@ -71,12 +71,8 @@ __device__ __forceinline__ typename OpVec<OpT>::v8 load_op8(const KT* p) {
     i32x4 raw = load16(p);
     return __builtin_bit_cast(V8, raw);
   } else if constexpr (std::is_same<KT, uint8_t>::value) {
-    int2 raw = *reinterpret_cast<const int2*>(p);
-    const uint8_t* c = reinterpret_cast<const uint8_t*>(&raw);
-    V8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(f16, fp8_to_f16_bits(c[e]));
-    return v;
+    const int2 raw = *reinterpret_cast<const int2*>(p);
+    return fp8x8_to_f16(raw.x, raw.y);
   } else {
     int2 raw = *reinterpret_cast<const int2*>(p);
     const int8_t* c = reinterpret_cast<const int8_t*>(&raw);

@@ -412,13 +412,8 @@ void prefill_kernel(PrefillParams P) {
       const int key = qi / CH, col = (qi % CH) * 8;
       V8 kv, vv;
       if constexpr (kFp8) {
-        const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(&tr.k[n]);
-        const uint8_t* vc8 = reinterpret_cast<const uint8_t*>(&tr.v[n]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kv[e] = __builtin_bit_cast(f16, fp8_to_f16_bits(kc8[e]));
-          vv[e] = __builtin_bit_cast(f16, fp8_to_f16_bits(vc8[e]));
-        }
+        kv = fp8x8_to_f16(tr.k[n].x, tr.k[n].y);
+        vv = fp8x8_to_f16(tr.v[n].x, tr.v[n].y);
       } else if constexpr (kI8) {
         const int8_t* kc8 = reinterpret_cast<const int8_t*>(&tr.k[n]);
         const int8_t* vc8 = reinterpret_cast<const int8_t*>(&tr.v[n]);

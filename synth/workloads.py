@@ -612,16 +612,18 @@ def config_tiny_paged_decode(poison: bool = False) -> PagedCase:
 
 
 def config_gqa_paged_decode(poison: bool = False, B: int = 32, max_len: int = 8192,
-                            seed: int = 1002) -> PagedCase:
+                            seed: int = 1002, cache_dtype: int = F16) -> PagedCase:
     """fp16, B=32, one new row per non-empty request, H 64/8, D 64, block 16, key counts
     ~ U{0..8192} with one request forced to 0 (an empty request owns no rows: its
-    seqlens_k is -1), a 20000-block pool, 512 table entries per request, sinks ~ N(0,1)."""
+    seqlens_k is -1), a 20000-block pool, 512 table entries per request, sinks ~ N(0,1).
+    ``cache_dtype`` I8 / FP8 stores the cache as codes with per-channel scales."""
     rng = np.random.default_rng(seed)
     L = rng.integers(0, max_len + 1, size=B)
     L[int(rng.integers(0, B))] = 0
     q_lens = (L > 0).astype(np.int64)
     return paged_case(seed, kv_lens=L, q_lens=q_lens, H_q=64, H_kv=8, D=64, block_size=16,
-                      dtype=F16, num_blocks=max(20000, int(((L + 15) // 16).sum())),
+                      dtype=F16, cache_dtype=cache_dtype,
+                      num_blocks=max(20000, int(((L + 15) // 16).sum())),
                       max_blocks_per_seq=(max_len + 15) // 16, sinks=True,
                       scale=1.0 / 8.0, poison=poison, max_seqlen_k=max_len, rng=rng,
                       name="gqa_paged_decode_f16")
