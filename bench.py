@@ -524,7 +524,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
-    ap.add_argument("--no-quant", action="store_true", help="skip the FP8-cache decode")
+    ap.add_argument("--no-quant", action="store_true", help="skip the INT8 / FP8-cache decodes")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -576,15 +576,18 @@ def main():
         line["decode_graph"] = bench_decode_graph()
     if not args.no_quant:
         import synth
-        qcase, q_ms_step, q_attn, q_st = bench_decode(50, 5, cache_dtype=synth.FP8)
-        q_kv = _kv_bytes(qcase)
-        q_avg = sum(q_attn) / len(q_attn)
-        line["decode_fp8"] = {
-            "workload": "the GQA paged decode with an FP8 E4M3 cache (per-channel scales)",
-            "kv_bytes_per_step": q_kv, "avg_us": round(q_avg * 1e3, 2),
-            "median_us": round(q_attn[len(q_attn) // 2] * 1e3, 2), "p10_p90_us": _p10_p90(q_attn),
-            "gbs": round(q_kv / (q_avg * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(q_kv / (q_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "status": q_st}
+        for key, cdt, what in (("decode_int8", synth.I8, "an INT8 cache"),
+                               ("decode_fp8", synth.FP8, "an FP8 E4M3 cache")):
+            qcase, _, q_attn, q_st = bench_decode(50, 5, cache_dtype=cdt)
+            q_kv = _kv_bytes(qcase)
+            q_avg = sum(q_attn) / len(q_attn)
+            line[key] = {
+                "workload": f"the GQA paged decode with {what} (per-channel scales), attention call",
+                "kv_bytes_per_step": q_kv, "avg_us": round(q_avg * 1e3, 2),
+                "median_us": round(q_attn[len(q_attn) // 2] * 1e3, 2),
+                "p10_p90_us": _p10_p90(q_attn), "gbs": round(q_kv / (q_avg * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": round(q_kv / (q_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "status": q_st}
     if not args.no_sparse:
         line["selected_decode"] = bench_sparse("selected", 50, 5)
         line["local_plus_aux"] = bench_sparse("local_aux", 50, 5)

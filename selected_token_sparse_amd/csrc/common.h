@@ -65,6 +65,25 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(int lo, int hi) {
                    __builtin_bit_cast(int32_t, c), __builtin_bit_cast(int32_t, d)};
   return __builtin_bit_cast(f16x8, w);
 }
+// Eight INT8 codes (the bytes of two 32-bit words, lowest first) as exact f16 values: with
+// the sign bit flipped a code c becomes u = c + 128 in [0, 255], the f16 with bits
+// 0x6400 | u is 1024 + u exactly (spacing 1 in [1024, 2048)), and subtracting 1152 leaves
+// c exactly.  Two codes per byte permute and per packed f16 subtraction.
+__device__ __forceinline__ f16x8 int8x8_to_f16(int lo, int hi) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t ul = (uint32_t)lo ^ 0x80808080u, uh = (uint32_t)hi ^ 0x80808080u;
+  // byte selectors: result bytes (u_a, 0x64, u_b, 0x64), 0x64 taken from the first source
+  const uint32_t w0 = __builtin_amdgcn_perm(0x64646464u, ul, 0x04010400u);
+  const uint32_t w1 = __builtin_amdgcn_perm(0x64646464u, ul, 0x04030402u);
+  const uint32_t w2 = __builtin_amdgcn_perm(0x64646464u, uh, 0x04010400u);
+  const uint32_t w3 = __builtin_amdgcn_perm(0x64646464u, uh, 0x04030402u);
+  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const h2 r0 = __builtin_bit_cast(h2, w0) - bias, r1 = __builtin_bit_cast(h2, w1) - bias;
+  const h2 r2 = __builtin_bit_cast(h2, w2) - bias, r3 = __builtin_bit_cast(h2, w3) - bias;
+  const i32x4 w = {__builtin_bit_cast(int32_t, r0), __builtin_bit_cast(int32_t, r1),
+                   __builtin_bit_cast(int32_t, r2), __builtin_bit_cast(int32_t, r3)};
+  return __builtin_bit_cast(f16x8, w);
+}
 // Exact value of a code (NaN codes give NaN).
 __device__ __forceinline__ float to_f32(uint8_t code) {
   return (float)__builtin_bit_cast(f16, fp8_to_f16_bits(code)) * kFp8Unit;

@@ -74,12 +74,8 @@ __device__ __forceinline__ typename OpVec<OpT>::v8 load_op8(const KT* p) {
     const int2 raw = *reinterpret_cast<const int2*>(p);
     return fp8x8_to_f16(raw.x, raw.y);
   } else {
-    int2 raw = *reinterpret_cast<const int2*>(p);
-    const int8_t* c = reinterpret_cast<const int8_t*>(&raw);
-    V8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (OpT)(float)c[e];
-    return v;
+    const int2 raw = *reinterpret_cast<const int2*>(p);
+    return int8x8_to_f16(raw.x, raw.y);
   }
 }
 

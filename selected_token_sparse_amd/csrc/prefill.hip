@@ -415,10 +415,8 @@ void prefill_kernel(PrefillParams P) {
         kv = fp8x8_to_f16(tr.k[n].x, tr.k[n].y);
         vv = fp8x8_to_f16(tr.v[n].x, tr.v[n].y);
       } else if constexpr (kI8) {
-        const int8_t* kc8 = reinterpret_cast<const int8_t*>(&tr.k[n]);
-        const int8_t* vc8 = reinterpret_cast<const int8_t*>(&tr.v[n]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { kv[e] = (OpT)(float)kc8[e]; vv[e] = (OpT)(float)vc8[e]; }
+        kv = int8x8_to_f16(tr.k[n].x, tr.k[n].y);
+        vv = int8x8_to_f16(tr.v[n].x, tr.v[n].y);
       } else {
         kv = __builtin_bit_cast(V8, tr.k[n]);
         vv = __builtin_bit_cast(V8, tr.v[n]);
