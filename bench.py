@@ -39,8 +39,8 @@ METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged
 # WRITE_SIZE counter passes scaled by the same counters' reading on a plain device copy of
 # known size (profiles/decode_gqa_paged_f16_traffic.md).  Valid only for the kernel sources
 # whose digest is recorded with it; any other source reports traffic = null.
-MEASURED_TRAFFIC = {"sources_sha1": "1f658efea461d334191f33b809625fba0ee58540",
-                    "bytes_per_call": 286085349}
+MEASURED_TRAFFIC = {"sources_sha1": "764a1376d2913a03aa6f5b7ffa8e0dd81ee2b3f5",
+                    "bytes_per_call": 286087958}
 KERNEL_SOURCES = ("selected_token_sparse_amd/csrc/decode.hip", "selected_token_sparse_amd/csrc/common.h",
                   "selected_token_sparse_amd/csrc/launch.h")
 

@@ -62,21 +62,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// 8 cache elements at `p` as an MFMA operand of type OpT (int8 codes convert exactly; FP8
-// E4M3 codes, uint8_t, become f16 holding their value / kFp8Unit, also exactly).
+// Eight 16-bit cache elements as an MFMA operand.
 template <typename OpT, typename KT>
 __device__ __forceinline__ typename OpVec<OpT>::v8 load_op8(const KT* p) {
-  typedef typename OpVec<OpT>::v8 V8;
-  if constexpr (sizeof(KT) == 2) {
-    i32x4 raw = load16(p);
-    return __builtin_bit_cast(V8, raw);
-  } else if constexpr (std::is_same<KT, uint8_t>::value) {
-    const int2 raw = *reinterpret_cast<const int2*>(p);
-    return fp8x8_to_f16(raw.x, raw.y);
-  } else {
-    const int2 raw = *reinterpret_cast<const int2*>(p);
-    return int8x8_to_f16(raw.x, raw.y);
-  }
+  static_assert(sizeof(KT) == 2, "8-bit caches load raw codes (see issue_tile)");
+  return __builtin_bit_cast(typename OpVec<OpT>::v8, load16(p));
 }
 
 // Parameters of the split kernels (by value).
@@ -157,11 +147,23 @@ __device__ __forceinline__ void wait_vm() {
 // in-bounds rows `dk` / `dv`: its score is replaced by -inf and its V row, which must be
 // finite, gets weight 0), so each tile costs exactly 4*D/32 vector memory instructions and
 // can be waited for with a fixed vmcnt.
-template <typename OpT, typename KT, int D>
+template <typename OpT, typename KT, int D, bool kQuant = sizeof(KT) == 1>
 struct TileRegs {
-  typename OpVec<OpT>::v8 k[2][D / 32];
-  typename OpVec<OpT>::v8 v[2][D / 32];   // INT8 caches only
+  typename OpVec<OpT>::v8 k[2][D / 32];   // 16-bit caches: the K operands as loaded
 };
+template <typename OpT, typename KT, int D>
+struct TileRegs<OpT, KT, D, true> {
+  i32x4 kq[2][D / 64], vq[2][D / 64];     // 8-bit caches: raw codes, 16 per lane and load
+};
+
+// Dimensions of the K operand of QK step kc held by lane group grp: 8 at 32 kc + 8 grp for
+// 16-bit caches (16-byte loads); for 8-bit caches one 16-byte load brings 16 codes, dims
+// 64 j + 16 grp .. + 15, which feed steps 2j and 2j + 1.  The query operand uses the same
+// dimensions (the contraction does not depend on their order).
+template <typename KT>
+__device__ __forceinline__ int qk_col(int kc, int grp) {
+  return sizeof(KT) == 2 ? 32 * kc + 8 * grp : 64 * (kc >> 1) + 16 * grp + 8 * (kc & 1);
+}
 
 template <typename OpT, typename KT, int D>
 __device__ __forceinline__ void issue_tile(TileRegs<OpT, KT, D>& t, const KT* __restrict__ kbase,
@@ -170,17 +172,43 @@ __device__ __forceinline__ void issue_tile(TileRegs<OpT, KT, D>& t, const KT* __
                                            int grp) {
   constexpr int KC = D / 32;
   const int rows[2] = {row0, row1};
+  if constexpr (sizeof(KT) == 2) {
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int col = kc * 32 + grp * 8;
-      const KT* kp = rows[st] >= 0 ? kbase + (int64_t)rows[st] * D + col : dk + col;
-      const KT* vp = rows[st] >= 0 ? vbase + (int64_t)rows[st] * D + col : dv + col;
-      if constexpr (sizeof(KT) == 2) dma16(vp, vbuf + (st * KC + kc) * 1024);
-      else t.v[st][kc] = load_op8<OpT>(vp);
-      t.k[st][kc] = load_op8<OpT>(kp);
-    }
+      for (int kc = 0; kc < KC; ++kc) {
+        const int col = kc * 32 + grp * 8;
+        const KT* kp = rows[st] >= 0 ? kbase + (int64_t)rows[st] * D + col : dk + col;
+        const KT* vp = rows[st] >= 0 ? vbase + (int64_t)rows[st] * D + col : dv + col;
+        dma16(vp, vbuf + (st * KC + kc) * 1024);
+        t.k[st][kc] = load_op8<OpT>(kp);
+      }
+  } else {
+    // raw codes stay in flight; they are converted when the tile is consumed
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) {
+        const int col = 64 * j + 16 * grp;
+        const KT* kp = rows[st] >= 0 ? kbase + (int64_t)rows[st] * D + col : dk + col;
+        const KT* vp = rows[st] >= 0 ? vbase + (int64_t)rows[st] * D + col : dv + col;
+        t.vq[st][j] = load16(vp);
+        t.kq[st][j] = load16(kp);
+      }
+  }
+}
+
+// The f16 operands of 16 codes (an E4M3 code as value / 256, the factor riding on the
+// scales; an INT8 code exactly).
+template <typename KT>
+__device__ __forceinline__ void codes_to_f16(i32x4 r, f16x8& a, f16x8& b) {
+  if constexpr (std::is_same<KT, uint8_t>::value) {
+    a = fp8x8_to_f16(r[0], r[1]);
+    b = fp8x8_to_f16(r[2], r[3]);
+  } else {
+    a = int8x8_to_f16(r[0], r[1]);
+    b = int8x8_to_f16(r[2], r[3]);
+  }
 }
 
 // Softmax update and both products for a tile whose loads have completed.
@@ -192,16 +220,27 @@ __device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t v
   typedef typename OpVec<OpT>::v8 V8;
   constexpr int KC = D / 32;
   constexpr int MT = D / 16;
-  if constexpr (sizeof(KT) == 1) {
-    // INT8 V: into the LDS buffer in the DMA lane layout (masked keys as zeros)
+  constexpr bool kQuant = sizeof(KT) == 1;
+  V8 kop[2][kQuant ? KC : 1];   // 8-bit caches: the converted K operands
+  if constexpr (kQuant) {
+    // V codes to f16, into the LDS buffer in the DMA lane layout (block (st, dim / 32),
+    // slot key % 16 + 16 * ((dim % 32) / 8)), masked keys as zeros; then the K codes
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bool ok = (valid >> (16 * st + lam)) & 1u;
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) {
+        V8 v0, v1;
+        codes_to_f16<KT>(t.vq[st][j], v0, v1);
+        unsigned char* blk = vbuf + (st * KC + 2 * j + (grp >> 1)) * 1024 + 16 * (lam + 32 * (grp & 1));
+        *reinterpret_cast<V8*>(blk) = ok ? v0 : V8{};
+        *reinterpret_cast<V8*>(blk + 256) = ok ? v1 : V8{};
+      }
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const bool ok = (valid >> (16 * st + lam)) & 1u;
-        *reinterpret_cast<V8*>(vbuf + (st * KC + kc) * 1024 + 16 * (threadIdx.x & 63)) =
-            ok ? t.v[st][kc] : V8{};
-      }
+      for (int j = 0; j < D / 64; ++j) codes_to_f16<KT>(t.kq[st][j], kop[st][2 * j], kop[st][2 * j + 1]);
   }
   // S^T[key][head] for keys 16*st + 4*grp + i, head lam
   f32x4 s[2];
@@ -210,9 +249,13 @@ __device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t v
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      c = mfma16(t.k[st][kc], qop[0][kc], c);
-      // quantised caches: the low half of the folded query (see the query set-up)
-      if constexpr (sizeof(KT) == 1) c = mfma16(t.k[st][kc], qop[1][kc], c);
+      if constexpr (kQuant) {
+        c = mfma16(kop[st][kc], qop[0][kc], c);
+        // the low half of the folded query (see the query set-up)
+        c = mfma16(kop[st][kc], qop[1][kc], c);
+      } else {
+        c = mfma16(t.k[st][kc], qop[0][kc], c);
+      }
     }
     s[st] = c;
   }
@@ -290,7 +333,8 @@ __device__ __forceinline__ void wave_keys(const KT* __restrict__ kbase, const KT
                                           float scale_log2, unsigned char* vbuf2, float& m_run,
                                           float& l_run, f32x4 (&acc)[D / 16]) {
   constexpr int kTileBytes = (D / 32) * 2 * 1024;
-  constexpr int kOps = 4 * (D / 32);   // vector memory instructions per tile
+  // vector memory instructions per tile (K and V, both key halves)
+  constexpr int kOps = sizeof(KT) == 2 ? 4 * (D / 32) : 4 * (D / 64);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lam = lane & 15;
@@ -377,14 +421,15 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
 
 // Occupancy hint for D = 64, where each wave keeps two tiles in flight: 5 waves per SIMD
 // for 16-bit caches (that register budget holds both tiles' K operands without spilling);
-// one fewer when the kernel also carries the second (window) source; 4 for quantised
-// caches, whose tiles also hold the V codes and whose query has a second (low) operand
-// (measured: 3 waves 63.1 / 62.5 us, 4 waves 58.1 / 57.0 us for the INT8 / FP8 decode).
+// one fewer when the kernel also carries the second (window) source; 4 for INT8 caches,
+// whose tiles hold the raw K and V codes and whose query has a second (low) operand; 3
+// for FP8 caches, whose conversion needs a few more registers (at 4 it spills inside the
+// key loop: 63.6 us against 56.6 at 3 for the FP8 decode; INT8 at 4: 53.1 us).
 template <int KIND, typename KT, int D>
 constexpr int split_waves_per_eu() {
   if (D != 64) return 1;
   if (KIND == SPATTN_KIND_LOCAL_AUX) return sizeof(KT) == 1 ? 3 : 4;
-  return sizeof(KT) == 1 ? 4 : 5;
+  return std::is_same<KT, uint8_t>::value ? 3 : sizeof(KT) == 1 ? 4 : 5;
 }
 
 template <int KIND, typename QT, typename KT, typename AT, int D>
@@ -476,9 +521,11 @@ void split_attn_kernel(SplitParams P) {
       typename OpVec<OpM>::v8 qop[2][D / 32];
 #pragma unroll
       for (int kc = 0; kc < D / 32; ++kc) {
-        const int col = kc * 32 + grp * 8;
+        const int col = qk_col<KT>(kc, grp);
         if constexpr (sizeof(KT) == 1) {
-          const typename OpVec<QT>::v8 qv = __builtin_bit_cast(typename OpVec<QT>::v8, qraw[kc]);
+          // the query dims of this step's K operand (not those of qraw's layout)
+          const typename OpVec<QT>::v8 qv = __builtin_bit_cast(
+              typename OpVec<QT>::v8, hv ? load16(qrow + col) : i32x4{0, 0, 0, 0});
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float x = hv ? to_f32((QT)qv[e]) * (P.key_scale[c * D + col + e] * kUnit) : 0.f;
