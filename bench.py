@@ -240,24 +240,25 @@ def bench_decode_graph(layers=24, steps=20, warmup=3, copies=3):
             "graph_kv_gbs": round(kv / (graph_us * 1e-6) / 1e9, 1)}
 
 
-def bench_prefill(window, steps, warmup):
+def bench_prefill(window, steps, warmup, cache_dtype=None):
     import torch
 
     import selected_token_sparse_amd as sta
     import synth
     from synth.device import case_tensors
 
-    case = synth.config_paged_prefill_window(window=window)
+    case = synth.config_paged_prefill_window(window=window, cache_dtype=cache_dtype)
     t = case_tensors(case)
     # the prompt rows are appended once, outside the timed region
     sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], t["seqlens_k"], t["k_cache"], t["v_cache"],
-                        t["block_table"])
+                        t["block_table"], t["key_scale"], t["value_scale"])
     out = torch.empty((case.T, case.H_q, case.D), dtype=torch.float16, device="cuda")
 
     def call():
         sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], t["seqlens_k"],
                                 case.max_seqlen_q, case.max_seqlen_k, out,
-                                block_table=t["block_table"], scale=case.scale,
+                                block_table=t["block_table"], key_scale=t["key_scale"],
+                                value_scale=t["value_scale"], scale=case.scale,
                                 local_window=case.local_window, sinks=t["sinks"])
 
     flush = ColdCache()
@@ -524,7 +525,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
-    ap.add_argument("--no-quant", action="store_true", help="skip the INT8 / FP8-cache decodes")
+    ap.add_argument("--no-quant", action="store_true", help="skip the INT8 / FP8-cache workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -576,18 +577,20 @@ def main():
         line["decode_graph"] = bench_decode_graph()
     if not args.no_quant:
         import synth
-        for key, cdt, what in (("decode_int8", synth.I8, "an INT8 cache"),
-                               ("decode_fp8", synth.FP8, "an FP8 E4M3 cache")):
+        for tag, cdt, what in (("int8", synth.I8, "an INT8 cache"),
+                               ("fp8", synth.FP8, "an FP8 E4M3 cache")):
             qcase, _, q_attn, q_st = bench_decode(50, 5, cache_dtype=cdt)
             q_kv = _kv_bytes(qcase)
             q_avg = sum(q_attn) / len(q_attn)
-            line[key] = {
+            line[f"decode_{tag}"] = {
                 "workload": f"the GQA paged decode with {what} (per-channel scales), attention call",
                 "kv_bytes_per_step": q_kv, "avg_us": round(q_avg * 1e3, 2),
                 "median_us": round(q_attn[len(q_attn) // 2] * 1e3, 2),
                 "p10_p90_us": _p10_p90(q_attn), "gbs": round(q_kv / (q_avg * 1e-3) / 1e9, 1),
                 "frac_hbm_peak": round(q_kv / (q_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "status": q_st}
+            if not args.no_prefill:
+                line[f"prefill_{tag}_no_window"] = bench_prefill(-1, 20, 3, cache_dtype=cdt)
     if not args.no_sparse:
         line["selected_decode"] = bench_sparse("selected", 50, 5)
         line["local_plus_aux"] = bench_sparse("local_aux", 50, 5)

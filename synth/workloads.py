@@ -630,15 +630,18 @@ def config_gqa_paged_decode(poison: bool = False, B: int = 32, max_len: int = 81
 
 
 def config_paged_prefill_window(window: int = 128, poison: bool = False,
-                                lens=(1024, 512, 2048, 1536)) -> PagedCase:
+                                lens=(1024, 512, 2048, 1536),
+                                cache_dtype: Optional[int] = None) -> PagedCase:
     """fp16 fresh prompts (past = 0), B=4 with query lengths 1024, 512, 2048, 1536 in that
     order, H 64/8, D 64, block 16, a 1024-block pool, window 128, sinks ~ N(0,1)."""
     rng = np.random.default_rng(1003)
     return paged_case(1003, kv_lens=list(lens), q_lens=list(lens), H_q=64, H_kv=8, D=64,
-                      block_size=16, dtype=F16, num_blocks=max(1024, sum((x + 15) // 16 for x in lens)),
+                      block_size=16, dtype=F16, cache_dtype=cache_dtype,
+                      num_blocks=max(1024, sum((x + 15) // 16 for x in lens)),
                       sinks=True, scale=1.0 / 8.0,
                       local_window=window, poison=poison, rng=rng,
-                      name=f"paged_prefill_w{window}_f16" if window > 0 else "paged_prefill_f16")
+                      name=(f"paged_prefill_w{window}_f16" if window > 0 else "paged_prefill_f16")
+                      + {None: "", F16: "", I8: "_int8_cache", FP8: "_fp8_cache"}.get(cache_dtype, ""))
 
 
 def config_selected_decode(sinks: bool = True, poison: bool = False, B: int = 16,
