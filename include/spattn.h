@@ -23,7 +23,9 @@
  *   and device, or logs.  All calls can therefore be recorded into a HIP graph.
  * - Return value: 0 = enqueued.  A negative value is a host-detectable argument error and
  *   then NOTHING was enqueued: SPATTN_ERR_NULL (a required pointer is NULL),
- *   SPATTN_ERR_SHAPE (a size is negative or inconsistent), SPATTN_ERR_DTYPE (dtype
+ *   SPATTN_ERR_SHAPE (a size is negative or inconsistent, or a data pointer is not 16-byte
+ *   aligned: activations, outputs, caches and auxiliary stores are accessed 16 bytes at a
+ *   time; allocations are aligned), SPATTN_ERR_DTYPE (dtype
  *   combination not supported), SPATTN_ERR_UNSUPPORTED (e.g. is_causal = 0, head_dim not
  *   64/128, H_q not a multiple of H_kv), SPATTN_ERR_WORKSPACE (workspace too small),
  *   SPATTN_ERR_LAUNCH (the HIP launch itself failed; work before the failing launch of

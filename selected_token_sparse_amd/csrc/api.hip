@@ -15,11 +15,17 @@ namespace {
 bool float_dtype(int t) { return t == SPATTN_F32 || t == SPATTN_F16 || t == SPATTN_BF16; }
 bool quantised_cache(int t) { return t == SPATTN_I8 || t == SPATTN_FP8; }
 
+// The kernels read and write activations and cache rows with 16-byte vector accesses (a
+// row of D elements is a multiple of 16 bytes), so every data pointer must be 16-byte
+// aligned; null pointers are checked separately.
+bool misaligned(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) != 0; }
+
 // Shared checks of a KV cache description; returns SPATTN_OK or an error code.
 int check_cache(const void* k_cache, const void* v_cache, int dtype, int cache_dtype,
                 const int32_t* block_table, int max_blocks, int block_size, int num_blocks,
                 const float* key_scale, const float* value_scale, int B, int H_kv, int D) {
   if (k_cache == nullptr || v_cache == nullptr) return SPATTN_ERR_NULL;
+  if (misaligned(k_cache) || misaligned(v_cache)) return SPATTN_ERR_SHAPE;
   if (quantised_cache(cache_dtype)) {
     if (key_scale == nullptr || value_scale == nullptr) return SPATTN_ERR_NULL;
   } else if (cache_dtype != dtype) {
@@ -74,6 +80,7 @@ int kv_cache_append(const void* k_new, const void* v_new, int new_dtype,
   if (B == 0) return SPATTN_ERR_SHAPE;
   if (k_new == nullptr || v_new == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
     return SPATTN_ERR_NULL;
+  if (misaligned(k_new) || misaligned(v_new)) return SPATTN_ERR_SHAPE;
   int rc = check_cache(k_cache, v_cache, new_dtype, cache_dtype, block_table, max_blocks_per_seq,
                        block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
   if (rc != SPATTN_OK) return rc;
@@ -100,6 +107,7 @@ int prepare_and_append(const int32_t* cu_seqlens_q, const int32_t* past_seqlens,
   if (T > 0) {
     if (B == 0) return SPATTN_ERR_SHAPE;
     if (k_new == nullptr || v_new == nullptr) return SPATTN_ERR_NULL;
+    if (misaligned(k_new) || misaligned(v_new)) return SPATTN_ERR_SHAPE;
     const int rc = check_cache(k_cache, v_cache, new_dtype, cache_dtype, block_table,
                                max_blocks_per_seq, block_size, num_blocks, key_scale, value_scale,
                                B, H_kv, D);
@@ -134,6 +142,8 @@ int qkv_prologue(const void* qkv, const void* q, const void* k, const void* v, i
   if (B == 0) return SPATTN_ERR_SHAPE;
   if (qkv == nullptr && (q == nullptr || k == nullptr || v == nullptr)) return SPATTN_ERR_NULL;
   if (q_out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr) return SPATTN_ERR_NULL;
+  if (misaligned(qkv) || misaligned(q) || misaligned(k) || misaligned(v) || misaligned(q_out))
+    return SPATTN_ERR_SHAPE;
   int rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
                        block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
   if (rc != SPATTN_OK) return rc;
@@ -202,6 +212,7 @@ int paged_attention_fwd(const void* q, int dtype, const void* k_cache, const voi
   if (B == 0) return SPATTN_ERR_SHAPE;
   if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
     return SPATTN_ERR_NULL;
+  if (misaligned(q) || misaligned(out)) return SPATTN_ERR_SHAPE;
   rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
                    block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
   if (rc != SPATTN_OK) return rc;
@@ -250,6 +261,8 @@ int sparse_attention_fwd(const void* q, int dtype, int mode, const void* k_cache
   if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
     return SPATTN_ERR_NULL;
   if (max_selected > 0 && sel_idx == nullptr) return SPATTN_ERR_NULL;
+  if (misaligned(q) || misaligned(out) || misaligned(aux_k) || misaligned(aux_v))
+    return SPATTN_ERR_SHAPE;
   rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
                    block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
   if (rc != SPATTN_OK) return rc;

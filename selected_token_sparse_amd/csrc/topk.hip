@@ -164,7 +164,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkParams P) {
   // bit e = bit b of the word's key e)
   const float* row = P.scores + (int64_t)seg * P.L;
   constexpr int NV = R / (4 * kTkThreads);   // float4 loads per thread and round
-  const bool vec = (P.L & 3) == 0;
+  // float4 loads when every row starts on a 16-byte boundary
+  const bool vec = (P.L & 3) == 0 && (reinterpret_cast<uintptr_t>(P.scores) & 15u) == 0;
   f32x4 buf[NV];
   auto load_round = [&](int w) {
     const int r0 = w * R;

@@ -204,3 +204,39 @@ def test_prepare_argument_errors(lib):
     assert f(None, FAKE, 2, 4, FAKE, FAKE, None, None, None, None) == -1
     assert f(FAKE, FAKE, -1, 4, FAKE, FAKE, None, None, None, None) == -2
     assert f(FAKE, FAKE, 9000, 4, FAKE, FAKE, None, None, None, None) == -2
+
+
+MIS = FAKE + 8  # an 8-byte offset: not a 16-byte boundary
+
+
+@pytest.mark.parametrize("kw", [dict(q=MIS), dict(out=MIS), dict(k=MIS), dict(v=MIS)])
+def test_paged_misaligned_pointers(lib, kw):
+    assert _paged(lib, **kw) == -2
+
+
+@pytest.mark.parametrize("kw", [dict(q=MIS), dict(out=MIS), dict(k=MIS),
+                                dict(mode=1, win=8, ak=MIS, av=FAKE, alen=10, astride=0),
+                                dict(mode=1, win=8, ak=FAKE, av=MIS, alen=10, astride=0)])
+def test_sparse_misaligned_pointers(lib, kw):
+    assert _sparse(lib, **kw) == -2
+
+
+def test_append_and_prologue_misaligned_pointers(lib):
+    base = [FAKE, FAKE, 1, FAKE, FAKE, 2, 4, FAKE, FAKE, 1, FAKE, 4, 16, 8, None, None, 2, 64, None, None, None]
+    for i in (0, 1, 7, 8):               # k_new, v_new, k_cache, v_cache
+        a = list(base)
+        a[i] = MIS
+        assert lib.kv_cache_append(*a) == -2, i
+    pa = [FAKE, FAKE, 2, 4, FAKE, FAKE, None, None, FAKE, FAKE, 1, FAKE, FAKE, 1, FAKE, 4, 16,
+          8, None, None, 2, 64, None, None, None]
+    for i in (8, 9, 11):                 # k_new, v_new, k_cache
+        a = list(pa)
+        a[i] = MIS
+        assert lib.prepare_and_append(*a) == -2, i
+    pro = [FAKE, None, None, None, 1, FAKE, FAKE, 2, 4, 8, 2, 64, 1, None, None, 1e-6, 32, 0,
+           FAKE, FAKE, 128, None, None, FAKE, FAKE, FAKE, 1, FAKE, 4, 16, 8, None, None,
+           None, None, None]
+    for i in (0, 23, 24):                # qkv, q_out, k_cache
+        a = list(pro)
+        a[i] = MIS
+        assert lib.qkv_prologue(*a) == -2, i
