@@ -1,9 +1,11 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: prepare_seqlens (device metadata)
-and kv_cache_append (this step's K/V rows into the paged cache), made as one launch by
-prepare_and_append -> paged_attention_fwd (split-K decode over the block table, merge
-with sinks).  Workload: GQA paged decode,
+A step is one pass of the whole path over one batch: prepare_seqlens (device metadata),
+kv_cache_append (this step's K/V rows into the paged cache) and paged_attention_fwd
+(split-K decode over the block table, merge with sinks), made by one paged_decode_step
+call (the split-K kernel derives the lengths and writes the new rows itself, then the
+merge).  The same step as prepare_and_append -> paged_attention_fwd is reported beside
+it.  Workload: GQA paged decode,
 fp16, B=32 requests with key counts ~ U{0..8192} (one forced empty), H_q=64, H_kv=8,
 head_dim 64, block 16, a 20000-block pool, sinks ~ N(0,1).  Inputs are resident in HBM
 before the timed region; three copies of the KV pool are rotated so that consecutive
@@ -35,14 +37,14 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2516.6    # MI355X dense fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged attn"
 
-# HBM bytes per paged_attention_fwd call on the decode workload, from rocprofv3 FETCH_SIZE and
+# HBM bytes per paged_decode_step call on the decode workload, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE counter passes scaled by the same counters' reading on a plain device copy of
 # known size (profiles/decode_gqa_paged_f16_traffic.md).  Valid only for the kernel sources
 # whose digest is recorded with it; any other source reports traffic = null.
 MEASURED_TRAFFIC = {"sources_sha1": "764a1376d2913a03aa6f5b7ffa8e0dd81ee2b3f5",
                     "bytes_per_call": 286087958}
 KERNEL_SOURCES = ("selected_token_sparse_amd/csrc/decode.hip", "selected_token_sparse_amd/csrc/common.h",
-                  "selected_token_sparse_amd/csrc/launch.h")
+                  "selected_token_sparse_amd/csrc/launch.h", "selected_token_sparse_amd/csrc/append.h")
 
 
 def kernel_sources_sha1():
@@ -119,7 +121,10 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_decode(steps, warmup, copies=3, cache_dtype=None):
+def bench_decode(steps, warmup, copies=3, cache_dtype=None, fused=False):
+    """The GQA paged decode step, `steps` timed after `warmup`.  fused: one paged_decode_step
+    call per step (events around it); otherwise prepare_and_append, then paged_attention_fwd
+    (events around the attention call)."""
     import torch
 
     import selected_token_sparse_amd as sta
@@ -143,6 +148,17 @@ def bench_decode(steps, warmup, copies=3, cache_dtype=None):
 
     def step(i, ev=None):
         t = sets[i % copies]
+        if fused:
+            if ev is not None:
+                ev[0].record()
+            sta.paged_decode_step(t["cu"], t["past"], T, sq, sk, t["q"], t["k_new"], t["v_new"],
+                                  t["k_cache"], t["v_cache"], case.max_seqlen_q, case.max_seqlen_k,
+                                  out, block_table=t["block_table"], key_scale=t["key_scale"],
+                                  value_scale=t["value_scale"], scale=case.scale, sinks=t["sinks"],
+                                  workspace=ws, status=status)
+            if ev is not None:
+                ev[1].record()
+            return
         # metadata and the cache append of this step's rows: one launch
         sta.prepare_and_append(t["cu"], t["past"], T, sq, sk, t["k_new"], t["v_new"], t["k_cache"],
                                t["v_cache"], t["block_table"], key_scale=t["key_scale"],
@@ -540,15 +556,17 @@ def main():
 
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib)
-    case, ms_step, attn_ms, st = bench_decode(args.steps, args.warmup)
+    case, ms_step, attn_ms, st = bench_decode(args.steps, args.warmup, fused=True)
     kv = _kv_bytes(case)
     gbs = kv / (ms_step * 1e-3) / 1e9
     attn_med = attn_ms[len(attn_ms) // 2]
     attn_avg = sum(attn_ms) / len(attn_ms)
-    # algorithmic bytes of one attention call: K/V of visible keys, Q, out, block-table entries
+    # algorithmic bytes of one step call: K/V of visible keys, Q, out, block-table entries,
+    # and the new K/V rows read once and written once into the cache
     q_bytes = case.T * case.H_q * case.D * 2
     bt_bytes = sum((int(s) + 1 + 15) // 16 for s in case.seqlens_k if s >= 0) * 4
-    alg = kv + 2 * q_bytes + bt_bytes
+    new_bytes = 2 * (2 * case.T * case.H_kv * case.D * 2)
+    alg = kv + 2 * q_bytes + bt_bytes + new_bytes
     achieved = alg / (attn_avg * 1e-3) / 1e9
     digest = kernel_sources_sha1()
     traffic = (MEASURED_TRAFFIC["bytes_per_call"]
@@ -564,12 +582,21 @@ def main():
                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "status": st},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "paged_attention_fwd decode call: split-K kernel + merge kernel",
+                     "kernel": "paged_decode_step call: split-K kernel (with the metadata and "
+                               "the append of the new rows) + merge kernel",
                      "kernel_sources_sha1": digest,
                      "avg_us": round(attn_avg * 1e3, 2), "median_us": round(attn_med * 1e3, 2),
                      "p10_p90_us": _p10_p90(attn_ms),
                      "algorithmic_bytes": alg},
     }
+    _, ms2, attn2, st2 = bench_decode(args.steps, args.warmup)
+    attn2_avg = sum(attn2) / len(attn2)
+    line["decode_two_calls"] = {
+        "workload": "the same step as prepare_and_append, then paged_attention_fwd",
+        "us_per_step": round(ms2 * 1e3, 2), "gbs": round(kv / (ms2 * 1e-3) / 1e9, 1),
+        "attention_call_avg_us": round(attn2_avg * 1e3, 2),
+        "attention_call_gbs": round((alg - new_bytes) / (attn2_avg * 1e-3) / 1e9, 1),
+        "attention_p10_p90_us": _p10_p90(attn2), "status": st2}
     if not args.no_prefill:
         line["prefill"] = bench_prefill(128, 50, 5)
         line["prefill_no_window"] = bench_prefill(-1, 30, 3)

@@ -280,6 +280,40 @@ SPATTN_API int paged_attention_fwd(const void* q, int dtype, const void* k_cache
                         size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
+ * paged_decode_step - prepare_seqlens, kv_cache_append and paged_attention_fwd of one
+ * decode step in one launch of the split-K kernel (plus its merge when the key range is
+ * split); the same citations as those three calls ([PA] Description: lengths derived on
+ * the device, no readback; [SPA] file summaries: scatter of the step's K/V through the
+ * block table; [PA] Description and Changes: paged attention with window and sink).
+ *
+ *   Arguments: those of prepare_seqlens (no token_req / token_pos), then q, k_new, v_new
+ *   (all of dtype) and the cache, bounds, head, scale, window, sink, output and workspace
+ *   arguments of paged_attention_fwd (is_causal is 1; workspace sized by
+ *   attention_workspace_bytes(SPATTN_KIND_PAGED, ...) with the same arguments).
+ *   Well-formed metadata (cu[0] = 0, non-decreasing, cu[B] = T, past >= 0): seqlens_q,
+ *   seqlens_k, the cache, out and the status bits equal those of
+ *   prepare_and_append(..., token_req = token_pos = committed_length = NULL) followed by
+ *   paged_attention_fwd(..., seqlens_k, is_causal = 1), bit for bit.  Each workgroup
+ *   writes the new keys of its own key range before reading them, so a slot this step
+ *   writes must not be read by another request as one of its past keys (shared prefix
+ *   blocks hold past keys only).  Malformed metadata: SPATTN_STATUS_BAD_CU, seqlens_q /
+ *   seqlens_k as prepare_seqlens writes them, nothing appended, every out row zero.
+ *   Supported: dtype F16 / BF16 with a cache of the same dtype, INT8 or FP8; B <= 255;
+ *   max_seqlen_q <= 8 (the split-K path; longer query blocks take the prefill kernel).
+ *   Other arguments that the separate calls accept return SPATTN_ERR_UNSUPPORTED and
+ *   enqueue nothing.  T = 0 writes the metadata only.
+ */
+SPATTN_API int paged_decode_step(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B,
+                      int T, int32_t* seqlens_q, int32_t* seqlens_k, const void* q,
+                      const void* k_new, const void* v_new, int dtype, void* k_cache,
+                      void* v_cache, int cache_dtype, const int32_t* block_table,
+                      int max_blocks_per_seq, int block_size, int num_blocks,
+                      const float* key_scale, const float* value_scale, int max_seqlen_q,
+                      int max_seqlen_k, int H_q, int H_kv, int D, float scale, int local_window,
+                      const float* sinks, void* out, void* workspace, size_t workspace_bytes,
+                      int32_t* status, void* stream);
+
+/*
  * sparse_attention_fwd - attention over selected cache rows ([DSA] Description: selected
  * main-cache mode and local-plus-auxiliary mode, guarded int32 indices, joint FP32 stable
  * softmax with optional sink, shared auxiliary K/V storage; [DSA] review: the selection

@@ -37,6 +37,11 @@ _SIGNATURES = {
                                     c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_int,
                                     c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
                                     c_void_p]),
+    "paged_decode_step": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p,
+                                  c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_int, c_int,
+                                  c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_void_p,
+                                  c_size_t, c_void_p, c_void_p]),
     "sparse_attention_fwd": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
                                      c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_int,

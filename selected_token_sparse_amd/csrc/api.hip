@@ -238,6 +238,54 @@ int paged_attention_fwd(const void* q, int dtype, const void* k_cache, const voi
   return launch_split_attention(a, plan, st);
 }
 
+int paged_decode_step(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B, int T,
+                      int32_t* seqlens_q, int32_t* seqlens_k, const void* q, const void* k_new,
+                      const void* v_new, int dtype, void* k_cache, void* v_cache, int cache_dtype,
+                      const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                      int num_blocks, const float* key_scale, const float* value_scale,
+                      int max_seqlen_q, int max_seqlen_k, int H_q, int H_kv, int D, float scale,
+                      int local_window, const float* sinks, void* out, void* workspace,
+                      size_t workspace_bytes, int32_t* status, void* stream) {
+  if (dtype != SPATTN_F16 && dtype != SPATTN_BF16) return float_dtype(dtype) ? SPATTN_ERR_UNSUPPORTED : SPATTN_ERR_DTYPE;
+  int rc = check_heads(H_q, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+  if (B < 0 || T < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return SPATTN_ERR_SHAPE;
+  if (B > kStepMaxB) return SPATTN_ERR_UNSUPPORTED;
+  if (use_prefill_path(SPATTN_KIND_PAGED, dtype, max_seqlen_q)) return SPATTN_ERR_UNSUPPORTED;
+  if (cu_seqlens_q == nullptr || past_seqlens == nullptr || seqlens_q == nullptr || seqlens_k == nullptr)
+    return SPATTN_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  // no rows: the metadata is all there is to do
+  if (T == 0) return launch_prepare_seqlens(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k,
+                                            nullptr, nullptr, status, st);
+  if (B == 0) return SPATTN_ERR_SHAPE;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr) return SPATTN_ERR_NULL;
+  if (misaligned(q) || misaligned(k_new) || misaligned(v_new) || misaligned(out)) return SPATTN_ERR_SHAPE;
+  rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
+                   block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+
+  AttnArgs a{};
+  a.kind = SPATTN_KIND_PAGED;
+  a.q = q; a.dtype = dtype; a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+  a.block_table = block_table; a.max_blocks = max_blocks_per_seq; a.block_size = block_size;
+  a.num_blocks = num_blocks; a.key_scale = key_scale; a.value_scale = value_scale;
+  a.cu = cu_seqlens_q; a.seqlens_k = nullptr; a.B = B; a.T = T;
+  a.max_q = max_seqlen_q; a.max_k = max_seqlen_k;
+  a.window = local_window > 0 ? local_window : 0;
+  a.H_q = H_q; a.H_kv = H_kv; a.D = D;
+  a.scale = resolve_scale(scale, D);
+  a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
+  a.past = past_seqlens; a.k_new = k_new; a.v_new = v_new;
+  a.seqlens_q_out = seqlens_q; a.seqlens_k_out = seqlens_k;
+  const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, max_seqlen_k, 0,
+                                         a.window, H_q, H_kv, D);
+  if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
+  if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
+    return SPATTN_ERR_WORKSPACE;
+  return launch_split_attention(a, plan, st);
+}
+
 int sparse_attention_fwd(const void* q, int dtype, int mode, const void* k_cache,
                          const void* v_cache, int cache_dtype, const int32_t* block_table,
                          int max_blocks_per_seq, int block_size, int num_blocks,

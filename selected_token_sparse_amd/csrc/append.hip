@@ -17,27 +17,6 @@ namespace spattn {
 constexpr int kAppendThreads = 256;
 constexpr int kFusedMaxB = kAppendThreads - 1;   // boundaries staged one per thread
 
-__device__ __forceinline__ int8_t quantize_one(float x, float s) {
-  float r = __builtin_rintf(x / s);  // IEEE float32 division, ties to even
-  if (r != r) return 0;              // NaN quotient
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int8_t)(int)r;
-}
-
-// Eight consecutive elements of one KV head (D is a multiple of 8) into eight codes:
-// INT8 (kFp8 = false) or FP8 E4M3 (kFp8 = true).
-template <bool kFp8, typename NewT>
-__device__ __forceinline__ void quantize8(const NewT* __restrict__ src, const float* __restrict__ scale,
-                                          int8_t* __restrict__ dst) {
-  union { int8_t c[8]; int2 v; } u;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if constexpr (kFp8) u.c[e] = (int8_t)quantize_fp8(to_f32(src[e]), scale[e]);
-    else u.c[e] = quantize_one(to_f32(src[e]), scale[e]);
-  }
-  *reinterpret_cast<int2*>(dst) = u.v;
-}
-
 // Row r of k_new / v_new into the cache row `dst` (element offset of KV head 0's slot).
 // kQuant: 0 = float cache (rows stored as they are), 1 = INT8 codes, 2 = FP8 E4M3 codes.
 template <typename NewT, int kQuant>

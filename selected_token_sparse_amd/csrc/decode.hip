@@ -30,6 +30,7 @@
 // is applied to the accumulator before it leaves the workgroup.
 #include <type_traits>
 
+#include "append.h"
 #include "common.h"
 #include "launch.h"
 
@@ -48,6 +49,7 @@ constexpr int kMaxSplits = 256;    // splits per item (LDS merge coefficients)
 constexpr int kTargetWorkgroupsPaged = 4096;
 constexpr int kTargetWorkgroupsSparse = 2048;
 constexpr int kMetaLdsMax = 512;   // cu entries staged in LDS (more: binary search in memory)
+static_assert(kStepMaxB + 1 <= kThreads, "a fused step stages one boundary per thread");
 
 enum Src { SRC_RANGE = 0, SRC_SELECT = 1, SRC_AUX = 2 };
 
@@ -94,6 +96,14 @@ struct SplitParams {
   int chunk, n_main, n_splits;
   int meta_lds;             // 1: cu / seqlens_k staged in LDS
   float scale_log2;         // scale * log2(e)
+  // Fused decode step (past != nullptr, paged kind, B + 1 <= kThreads): seqlens_k is
+  // derived here from cu and past as prepare_seqlens derives it, and every workgroup first
+  // writes the step's new K/V rows that fall in its own key range (see step_write_keys).
+  const int32_t* past;
+  const void* k_new;        // [T, H_kv, D] of the query dtype
+  const void* v_new;
+  int32_t* seqlens_q_out;   // [B], written by workgroup 0
+  int32_t* seqlens_k_out;
 };
 
 // OR of the per-lane status flags across the wave (uniform result).
@@ -419,6 +429,75 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
   return -1;
 }
 
+// Fused decode step, workgroup 0: seqlens_q / seqlens_k exactly as prepare_seqlens writes
+// them.  Malformed metadata takes its sanitised boundaries: the running maximum of cu
+// clamped to [0, T] (one per thread, B + 1 <= kThreads) and negative past read as 0.
+__device__ __forceinline__ void step_lengths(const SplitParams& P, bool bad, int* wave_max) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (!bad) {
+    if (tid < P.B) {
+      const int q = P.cu[tid + 1] - P.cu[tid];
+      P.seqlens_q_out[tid] = q;
+      P.seqlens_k_out[tid] = P.past[tid] + q - 1;
+    }
+    return;
+  }
+  const int n = P.B + 1;
+  int v = tid < n ? P.cu[tid] : INT32_MIN;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v = max(v, y);
+  }
+  if (lane == 63) wave_max[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) v = max(v, wave_max[w]);
+  const int bound = min(max(v, 0), P.T);
+  // bound of the next boundary: from the next lane, or from the next wave's first lane
+  const int up = __shfl_down(bound, 1, 64);
+  __shared__ int first_bound[kWaves];
+  if (lane == 0) first_bound[wave] = bound;
+  __syncthreads();
+  const int next = lane < 63 ? up : (wave + 1 < kWaves ? first_bound[wave + 1] : 0);
+  if (tid < P.B) {
+    const int q = next - bound;
+    P.seqlens_q_out[tid] = q;
+    P.seqlens_k_out[tid] = max(P.past[tid], 0) + q - 1;
+  }
+  __syncthreads();                                     // wave_max is reused by the caller
+}
+
+// Fused decode step: new keys j0 .. j1 - 1 (positions >= first_new) of request b, KV head c.
+// Key j is row c0 + (j - first_new) of k_new / v_new and goes to its cache slot exactly as
+// kv_cache_append stores it (16-bit rows copied, 8-bit rows quantised by the same code
+// writers).  Each workgroup writes the new keys its own split reads before it reads them;
+// workgroups that share a key write identical bytes.  Threads take 16-byte pieces.
+template <typename QT, typename KT, int D>
+__device__ __forceinline__ void step_write_keys(const SplitParams& P, int b, int c, int j0, int j1,
+                                                int first_new, int c0, int& flags) {
+  constexpr int kPieces = D / 8;                 // 8-element pieces per row
+  const int n = max(0, j1 - j0) * 2 * kPieces;   // K and V
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int key = i / (2 * kPieces), rest = i - key * 2 * kPieces;
+    const bool is_v = rest >= kPieces;
+    const int d = (is_v ? rest - kPieces : rest) * 8;
+    const int j = j0 + key;
+    const int row = cache_row_index(P.cd, b, j, c, flags);
+    if (row < 0) continue;
+    const QT* src = reinterpret_cast<const QT*>(is_v ? P.v_new : P.k_new) +
+                    ((int64_t)(c0 + j - first_new) * P.H_kv + c) * D + d;
+    // the cache arguments are read-only everywhere else in this kernel
+    void* cache = const_cast<void*>(is_v ? P.v_cache : P.k_cache);
+    if constexpr (sizeof(KT) == 1) {
+      quantize8<std::is_same<KT, uint8_t>::value>(
+          src, (is_v ? P.value_scale : P.key_scale) + c * D + d,
+          reinterpret_cast<int8_t*>(cache) + (int64_t)row * D + d);
+    } else {
+      store16(reinterpret_cast<KT*>(cache) + (int64_t)row * D + d, load16(src));
+    }
+  }
+}
+
 // Occupancy hint for D = 64, where each wave keeps two tiles in flight: 5 waves per SIMD
 // for 16-bit caches (that register budget holds both tiles' K operands without spilling);
 // one fewer when the kernel also carries the second (window) source; 4 for INT8 caches,
@@ -432,7 +511,7 @@ constexpr int split_waves_per_eu() {
   return std::is_same<KT, uint8_t>::value ? 3 : sizeof(KT) == 1 ? 4 : 5;
 }
 
-template <int KIND, typename QT, typename KT, typename AT, int D>
+template <int KIND, typename QT, typename KT, typename AT, int D, bool kStep>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<KIND, KT, D>(), 8)))
 void split_attn_kernel(SplitParams P) {
@@ -474,7 +553,24 @@ void split_attn_kernel(SplitParams P) {
   // ---- 1. the row's request and position ----
   const int32_t* cu = P.cu;
   const int32_t* skl = P.seqlens_k;
-  if (P.meta_lds) {
+  __shared__ int wave_flags[kWaves];
+  bool step_bad = false;                               // fused step, malformed metadata
+  if constexpr (kStep) {
+    // Fused step, one load round and one barrier: meta[0..B] = cu, meta[B+1+b] =
+    // past[b] + q_len_b - 1 (seqlens_k; well-formed metadata), and whether the metadata is
+    // well formed.  Workgroup 0 also writes seqlens_q / seqlens_k as prepare_seqlens does.
+    const int n = P.B + 1;                             // <= kThreads
+    const int cv = tid < n ? P.cu[tid] : 0;
+    const int cn = tid < P.B ? P.cu[tid + 1] : 0;
+    const int pb = tid < P.B ? P.past[tid] : 0;
+    const bool bad = (tid < P.B && (cn < cv || pb < 0)) ||
+                     (tid == 0 && (cv != 0 || P.cu[P.B] != P.T));
+    if (tid < n) meta[tid] = cv;
+    if (tid < P.B) meta[n + tid] = pb + (cn - cv) - 1;
+    step_bad = __syncthreads_or(bad) != 0;
+    cu = meta;
+    skl = meta + n;
+  } else if (P.meta_lds) {
     for (int i = tid; i <= P.B; i += kThreads) {
       meta[i] = P.cu[i];
       if (i < P.B) meta[P.B + 1 + i] = P.seqlens_k[i];
@@ -484,20 +580,41 @@ void split_attn_kernel(SplitParams P) {
     skl = meta + P.B + 1;
   }
   int flags = 0;
-  const RowInfo ri = resolve_row(cu, skl, P.B, r, P.max_q, P.max_k, flags);
+  RowInfo ri;
+  if (step_bad) {
+    // malformed metadata in a fused step: every row is zero and nothing is appended
+    ri.b = -1; ri.q_len = 0; ri.kv_len = 0; ri.p = -1;
+    if (blockIdx.x == 0) flags |= SPATTN_STATUS_BAD_CU;
+  } else {
+    ri = resolve_row(cu, skl, P.B, r, P.max_q, P.max_k, flags);
+  }
+  if (kStep && !step_bad && ri.b < 0 && ri.q_len > 0 &&
+      split == 0 && ht == 0) {
+    // a fused step's row beyond the host bounds reads nothing, but its key is still appended
+    const int b = find_request(cu, P.B, r);
+    const int first_new = ri.kv_len - ri.q_len, j = first_new + (r - cu[b]);
+    if (j < 0) flags |= SPATTN_STATUS_SHORT_KV;
+    else step_write_keys<QT, KT, D>(P, b, c, j, j + 1, first_new, cu[b], flags);
+  }
 
   // ---- 2. the split's keys -> cache-row indices ----
   const SplitRange sr = split_range<KIND>(P, ri, r, c, split, flags);
   if (sr.n_keys == 0 && P.n_splits > 1) {
     // nothing in this split: (m, l) = (-inf, 0) tells the merge to skip it; no accumulator
     // (the flags raised so far are the same in every wave)
+    if (kStep && blockIdx.x == 0) step_lengths(P, step_bad, wave_flags);
     if (tid == 0) raise_status(P.status, flags);
     if (tid < nh)
       P.ws_ml[(int64_t)split * P.T * P.H_q + (int64_t)r * P.H_q + h0 + tid] = make_float2(kNegInf, 0.f);
     return;
   }
   for (int v = tid; v < sr.n_keys; v += kThreads) rows[v] = split_key_row(P, sr, ri, c, v, flags);
-  __shared__ int wave_flags[kWaves];
+  if (kStep && ri.b >= 0) {
+    // fused step: the new keys of this split's range, written before the barrier below
+    const int first_new = ri.kv_len - ri.q_len, k0 = sr.lo + sr.v0;
+    step_write_keys<QT, KT, D>(P, ri.b, c, max(k0, first_new), k0 + sr.n_keys, first_new,
+                               cu[ri.b], flags);
+  }
   {
     const int wf = wave_or_flags(flags);
     if (lane == 0) wave_flags[wave] = wf;
@@ -622,6 +739,8 @@ void split_attn_kernel(SplitParams P) {
       if (d == 0) P.ws_ml[so + (int64_t)r * P.H_q + head] = make_float2(M, L);
     }
   }
+  // fused step: the lengths, written last so that nothing of it is live in the key loop
+  if (kStep && blockIdx.x == 0) step_lengths(P, step_bad, wave_flags);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -870,7 +989,14 @@ template <int KIND, typename QT, typename KT, typename AT, int D>
 static void launch_split_typed(const SplitParams& P, hipStream_t stream) {
   const int blocks = P.n_splits * P.T * P.H_kv * P.head_tiles;
   const size_t lds = split_lds_bytes<D>(P.chunk, P.meta_lds ? 2 * (P.B + 1) : 0);
-  hipLaunchKernelGGL((split_attn_kernel<KIND, QT, KT, AT, D>), dim3(blocks), dim3(kThreads), lds, stream, P);
+  // the fused decode step is its own instantiation, so the other kernels carry none of it
+  if constexpr (KIND == SPATTN_KIND_PAGED) {
+    if (P.past != nullptr) {
+      hipLaunchKernelGGL((split_attn_kernel<KIND, QT, KT, AT, D, true>), dim3(blocks), dim3(kThreads), lds, stream, P);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((split_attn_kernel<KIND, QT, KT, AT, D, false>), dim3(blocks), dim3(kThreads), lds, stream, P);
 }
 
 template <int KIND, typename KT, typename AT, int D>
@@ -934,6 +1060,8 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   P.chunk = plan.chunk; P.n_main = plan.n_main; P.n_splits = plan.n_splits;
   P.meta_lds = a.B + 1 <= kMetaLdsMax ? 1 : 0;
   P.scale_log2 = a.scale * kLog2e;
+  P.past = a.past; P.k_new = a.k_new; P.v_new = a.v_new;
+  P.seqlens_q_out = a.seqlens_q_out; P.seqlens_k_out = a.seqlens_k_out;
   const bool direct = plan.n_splits == 1;
   P.ws_acc = nullptr; P.ws_ml = nullptr;
   if (!direct) {

@@ -50,7 +50,16 @@ struct AttnArgs {
   void* out;
   void* workspace;
   int32_t* status;
+  // fused decode step only (paged kind, 16-bit q, split path, B < 256); nullptr otherwise
+  const int32_t* past;
+  const void* k_new;
+  const void* v_new;
+  int32_t* seqlens_q_out;
+  int32_t* seqlens_k_out;
 };
+
+// Largest B of the fused decode step (its boundaries are staged one per thread).
+constexpr int kStepMaxB = 255;
 
 // Work plan of the split-K (per-row) path: how the key range of one (row, KV head) is cut.
 struct SplitPlan {

@@ -21,7 +21,7 @@ def test_header_declares_the_abi():
     names = _declared()
     assert set(names) == {"prepare_seqlens", "kv_cache_append", "prepare_and_append",
                           "qkv_prologue", "topk_select",
-                          "paged_attention_fwd", "sparse_attention_fwd",
+                          "paged_attention_fwd", "paged_decode_step", "sparse_attention_fwd",
                           "attention_workspace_bytes"}
 
 
@@ -176,6 +176,37 @@ def test_prepare_and_append_argument_errors(lib):
     assert call(a16=0) == -2           # block size
     assert call(a2=0) == -2            # rows but no request
     assert call(a8=None) == -1
+
+
+def test_decode_step_argument_errors(lib):
+    f = lib.paged_decode_step
+    # cu, past, B, T, sq, sk, q, k_new, v_new, dtype, kc, vc, cache_dt, bt, mbps, bs, nb, ks,
+    # vs, max_q, max_k, H_q, H_kv, D, scale, win, sinks, out, ws, ws_bytes, status, stream
+    base = [FAKE, FAKE, 2, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, FAKE, 4, 16, 8,
+            None, None, 1, 64, 4, 2, 64, 0.0, -1, None, FAKE, None, 0, None, None]
+    def call(**kv):
+        a = list(base)
+        for i, v in kv.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a9=0) == -4            # float32 activations: the separate calls
+    assert call(a9=3) == -3            # not an activation dtype
+    assert call(a2=256) == -4          # more requests than one boundary per thread
+    assert call(a19=64) == -4          # a query block for the prefill kernel
+    assert call(a0=None) == -1
+    assert call(a1=None) == -1
+    assert call(a4=None) == -1
+    assert call(a7=None) == -1
+    assert call(a27=None) == -1
+    assert call(a12=2) == -3           # cache dtype differs from the activations
+    assert call(a12=3) == -1           # INT8 cache without scales
+    assert call(a23=96) == -4          # head dim
+    assert call(a21=3) == -4           # H_q not a multiple of H_kv
+    assert call(a2=0) == -2            # rows but no request
+    assert call(a15=0) == -2           # block size
+    for i in (6, 7, 8, 27):            # q, k_new, v_new, out off a 16-byte boundary
+        assert call(**{f"a{i}": MIS}) == -2
+    assert call(a10=MIS) == -2
 
 
 def test_topk_argument_errors(lib):
