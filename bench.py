@@ -41,8 +41,8 @@ METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged
 # WRITE_SIZE counter passes scaled by the same counters' reading on a plain device copy of
 # known size (profiles/decode_gqa_paged_f16_traffic.md).  Valid only for the kernel sources
 # whose digest is recorded with it; any other source reports traffic = null.
-MEASURED_TRAFFIC = {"sources_sha1": "764a1376d2913a03aa6f5b7ffa8e0dd81ee2b3f5",
-                    "bytes_per_call": 286087958}
+MEASURED_TRAFFIC = {"sources_sha1": "d161122587663ea19625d0334680ff1c633a3e11",
+                    "bytes_per_call": 286274110}
 KERNEL_SOURCES = ("selected_token_sparse_amd/csrc/decode.hip", "selected_token_sparse_amd/csrc/common.h",
                   "selected_token_sparse_amd/csrc/launch.h", "selected_token_sparse_amd/csrc/append.h")
 
@@ -191,10 +191,10 @@ def bench_decode(steps, warmup, copies=3, cache_dtype=None, fused=False):
 
 
 def bench_decode_graph(layers=24, steps=20, warmup=3, copies=3):
-    """A decode step of a `layers`-layer model (one metadata pass, then per layer the cache
-    append and the attention) on the GQA paged decode workload, eager and replayed from one
-    HIP graph.  Layer i uses the i % 3 copy of the KV pool, so consecutive layers read
-    different 655 MB pools as a real model's layers would."""
+    """A decode step of a `layers`-layer model (per layer one paged_decode_step: the
+    metadata, the cache append and the attention) on the GQA paged decode workload, eager
+    and replayed from one HIP graph.  Layer i uses the i % 3 copy of the KV pool, so
+    consecutive layers read different 655 MB pools as a real model's layers would."""
     import torch
 
     import selected_token_sparse_amd as sta
@@ -215,15 +215,12 @@ def bench_decode_graph(layers=24, steps=20, warmup=3, copies=3):
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step():
-        sta.prepare_seqlens(base["cu"], base["past"], T, sq, sk)
         for layer in range(layers):
             t = sets[layer % copies]
-            sta.kv_cache_append(t["k_new"], t["v_new"], t["cu"], sk, t["k_cache"], t["v_cache"],
-                                t["block_table"])
-            sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], sk,
-                                    case.max_seqlen_q, case.max_seqlen_k, out,
-                                    block_table=t["block_table"], scale=case.scale,
-                                    sinks=t["sinks"], workspace=ws)
+            sta.paged_decode_step(t["cu"], t["past"], T, sq, sk, t["q"], t["k_new"], t["v_new"],
+                                  t["k_cache"], t["v_cache"], case.max_seqlen_q,
+                                  case.max_seqlen_k, out, block_table=t["block_table"],
+                                  scale=case.scale, sinks=t["sinks"], workspace=ws)
 
     def timed(fn):
         for _ in range(warmup):
