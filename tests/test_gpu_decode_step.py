@@ -103,6 +103,18 @@ def test_multi_row_window_contiguous_bf16():
     _against_oracle(case, got, "step_multi_row")
 
 
+@pytest.mark.parametrize("cache_dtype", [synth.I8, synth.FP8])
+def test_bf16_quantised_cache_d128_window(cache_dtype):
+    """bf16 activations over an INT8 / FP8 cache at D 128 with a 256-key window and two new
+    rows per request: the codes the step writes and the rows it returns."""
+    print("decode step bf16 quantised d128", cache_dtype, flush=True)
+    case = synth.paged_case(310, kv_lens=[1500, 300, 2, 700], q_lens=[2, 2, 2, 1], H_q=16,
+                            H_kv=2, D=128, dtype=synth.BF16, cache_dtype=cache_dtype, sinks=True,
+                            local_window=256, poison=True, max_seqlen_q=2)
+    got = _step_vs_calls(case)
+    _against_oracle(case, got, f"step_bf16_d128_{cache_dtype}")
+
+
 def test_head_tiles_and_one_split():
     """Group 20 (two head tiles write the same new keys) and a key range short enough for
     one split, whose workgroup writes the output directly."""
