@@ -41,8 +41,8 @@ METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged
 # WRITE_SIZE counter passes scaled by the same counters' reading on a plain device copy of
 # known size (profiles/decode_gqa_paged_f16_traffic.md).  Valid only for the kernel sources
 # whose digest is recorded with it; any other source reports traffic = null.
-MEASURED_TRAFFIC = {"sources_sha1": "d161122587663ea19625d0334680ff1c633a3e11",
-                    "bytes_per_call": 286274110}
+MEASURED_TRAFFIC = {"sources_sha1": "084ea0b6165bc4a2a0c84c7150e807397362775a",
+                    "bytes_per_call": 286273113}
 KERNEL_SOURCES = ("selected_token_sparse_amd/csrc/decode.hip", "selected_token_sparse_amd/csrc/common.h",
                   "selected_token_sparse_amd/csrc/launch.h", "selected_token_sparse_amd/csrc/append.h")
 

@@ -28,6 +28,11 @@
 //
 // INT8 and FP8 E4M3 caches: key_scale is folded into the query operand (f16), value_scale
 // is applied to the accumulator before it leaves the workgroup.
+//
+// Fused decode step (paged_decode_step, the kStep instantiation): step 1 derives seqlens_k
+// from cu and past in the same load round, and before the barrier that ends step 2 the
+// workgroup writes the step's new K/V rows that fall in its own key split (quantised as
+// the cache append quantises them); workgroup 0 writes seqlens_q / seqlens_k last.
 #include <type_traits>
 
 #include "append.h"
