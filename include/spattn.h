@@ -160,6 +160,8 @@ SPATTN_API int kv_cache_append(const void* k_new, const void* v_new, int new_dty
  * those of the two calls made in order (same citations): seqlens_q, seqlens_k, token_req /
  * token_pos (may be NULL), the appended rows, and the status bits of both.  For a decode
  * step it removes one kernel launch; no device metadata is read back either way.
+ *   paged_decode_step goes further for decode steps: it makes this call's work part of
+ *   the attention launch.
  *   Arguments: those of prepare_seqlens, then those of kv_cache_append after its
  *   seqlens_k (which is this call's output).  Limits: 0 <= B <= 8192.
  */
