@@ -106,10 +106,14 @@ def round_to(x, dtype: str):
     if dtype == "f16":
         return x.astype(np.float16)
     if dtype == "bf16":
-        # 8 significant bits: scale the significand to an integer, round, scale back
-        m, e = np.frexp(x)
-        r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
-        return r.astype(np.float32)
+        # bf16: 8 significant bits over float32's exponent range.  A value of magnitude in
+        # [2^(e-1), 2^e) is rounded to a multiple of 2^(e-8); below 2^-126 the spacing stays
+        # that of the smallest subnormal, 2^-133.  np.rint rounds ties to even.
+        _, e = np.frexp(x)
+        q = np.maximum(e - 8, -133)
+        with np.errstate(over="ignore"):
+            r = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+            return r.astype(np.float32)
     raise ValueError(dtype)
 
 

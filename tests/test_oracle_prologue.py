@@ -7,6 +7,7 @@ property of rotated dot products, and the equivalences the prologue's readings s
 fused = prologue followed by the cache append).
 """
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -94,6 +95,28 @@ def test_round_to_bf16_matches_float32_then_bf16_away_from_ties():
     assert np.all(bits & 0xFFFF == 0)
     step = np.ldexp(1.0, np.frexp(np.abs(x))[1] - 8)
     assert np.all(np.abs(got - x) <= step / 2)
+
+
+def test_round_to_bf16_ties_and_subnormals_match_torch():
+    """Pins round_to(.., "bf16") where a plausible mistake shows: exact ties (the low 16 bits
+    of a float32 equal to 0x8000, which must go to the even bf16 neighbour, not away from
+    zero and not by truncation), their neighbours 0x7FFF / 0x8001, and the subnormal range
+    (spacing 2^-133 below 2^-126), against torch's float32 -> bfloat16 conversion, which
+    rounds to nearest with ties to even."""
+    rng = np.random.default_rng(17)
+    hi = rng.integers(0, 1 << 16, size=40000).astype(np.uint32)
+    hi = hi[((hi >> 7) & 0xFF) != 0xFF]                   # no inf / NaN exponents
+    hi = np.concatenate([hi, np.arange(0, 1 << 8, dtype=np.uint32),            # subnormals
+                         np.arange(1 << 15, (1 << 15) + (1 << 8), dtype=np.uint32)])
+    for low in (0x8000, 0x7FFF, 0x8001, 0x0000, 0x3000, 0xC000):
+        x = ((hi << 16) | np.uint32(low)).view(np.float32)
+        got = pro.round_to(x.astype(np.float64), "bf16")
+        want = torch.from_numpy(x.copy()).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), hex(low)
+    # hand-worked ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 (even: 1);
+    # 1 + 3 * 2^-8 halfway between 1 + 2^-7 and 1 + 2^-6 (even: 1 + 2^-6); same negated
+    t = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), -(1 + 3 * 2.0 ** -8)])
+    assert pro.round_to(t, "bf16").tolist() == [1.0, 1 + 2.0 ** -6, -1.0, -(1 + 2.0 ** -6)]
 
 
 def _case(**kw):
