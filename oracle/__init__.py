@@ -36,5 +36,5 @@ from .status import (  # noqa: F401
 from .metadata import prepare_seqlens  # noqa: F401
 from .append import quantize_int8, quantize_fp8_e4m3, decode_fp8_e4m3, kv_cache_append  # noqa: F401
 from .attention import attend, paged_attention, sparse_attention  # noqa: F401
-from .prologue import qkv_prologue  # noqa: F401
+from .prologue import qkv_prologue, round_to  # noqa: F401
 from .topk import topk_select  # noqa: F401

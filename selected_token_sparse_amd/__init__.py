@@ -7,7 +7,6 @@ library is missing the calls raise, there is no CPU path.
 """
 from __future__ import annotations
 
-import math
 from typing import Optional
 
 import torch
@@ -327,7 +326,3 @@ def sparse_attention_fwd(q: torch.Tensor, mode: int, k_cache: torch.Tensor, v_ca
         _ptr(aux_k, "aux_k"), _ptr(aux_v, "aux_v"), aux_dt, aux_len, aux_batch_stride, H_q, H_kv,
         D, float(scale), _ptr(sinks, "sinks"), _ptr(out, "out"), _ptr(ws, "workspace"), ws_bytes,
         _i32(status, "status"), _stream(q)))
-
-
-def default_scale(D: int) -> float:
-    return 1.0 / math.sqrt(D)

@@ -299,8 +299,12 @@ __device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t v
   }
   // a head with no visible key so far keeps l = 0, acc = 0 (its scores are all -inf)
   const float m_use = m_run == kNegInf ? 0.f : m_run;
+  // bf16 operands keep 8 significant bits: the weights are carried as hi + lo (hi = p
+  // rounded, lo = its rounding error rounded) and PV takes one product with each, so the
+  // weights keep about 16 bits, as f16 operands keep 11
+  constexpr bool kSplitP = std::is_same<OpT, bf16>::value;
   float psum = 0.f;
-  V8 pop;
+  V8 pop, plo;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -308,6 +312,7 @@ __device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t v
       const float p = exp2_safe(s[st][i] - m_use);
       psum += p;
       pop[st * 4 + i] = (OpT)p;
+      if constexpr (kSplitP) plo[st * 4 + i] = (OpT)(p - (float)pop[st * 4 + i]);
     }
   psum = xor_sum(psum, 16);
   psum = xor_sum(psum, 32);
@@ -327,6 +332,7 @@ __device__ __forceinline__ void consume_tile(TileRegs<OpT, KT, D>& t, uint32_t v
     typename OpVec<OpT>::v4 h1 = __builtin_bit_cast(typename OpVec<OpT>::v4, r1);
     V8 aop = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
     acc[m] = mfma16(aop, pop, acc[m]);
+    if constexpr (kSplitP) acc[m] = mfma16(aop, plo, acc[m]);
   }
 }
 

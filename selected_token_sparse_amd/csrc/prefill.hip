@@ -501,14 +501,25 @@ void prefill_kernel(PrefillParams P) {
       }
       // p = exp2(c * (s - m)) <= 2^8; a row with no visible key yet keeps p = 0
       const float nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
+      // bf16 operands keep 8 significant bits: the weights are carried as hi + lo (hi = p
+      // rounded, lo = its rounding error rounded) and PV takes one product with each, so
+      // the weights keep about 16 bits, as f16 operands keep 11
+      constexpr bool kSplitP = std::is_same<OpT, bf16>::value;
       V8 pop[2];
+      V8 plo[kSplitP ? 2 : 1];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pop[i >> 3][i & 7] = (OpT)exp2_safe(__builtin_fmaf(s[i], c_scale, nm));
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_safe(__builtin_fmaf(s[i], c_scale, nm));
+        pop[i >> 3][i & 7] = (OpT)p;
+        if constexpr (kSplitP) plo[i >> 3][i & 7] = (OpT)(p - (float)pop[i >> 3][i & 7]);
+      }
       // this lane's part of the row sum, over the rounded weights the PV product uses, two
       // per instruction (products with 1 are exact; the sum is fp32)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) l_run = dot2_ones(pop[i >> 3][i & 7], pop[i >> 3][(i & 7) + 1], l_run);
+      for (int i = 0; i < 16; i += 2) {
+        l_run = dot2_ones(pop[i >> 3][i & 7], pop[i >> 3][(i & 7) + 1], l_run);
+        if constexpr (kSplitP) l_run = dot2_ones(plo[i >> 3][i & 7], plo[i >> 3][(i & 7) + 1], l_run);
+      }
       {
         const int grp = lane >> 4, lam = lane & 15;
 #pragma unroll
@@ -529,6 +540,7 @@ void prefill_kernel(PrefillParams P) {
             V4 x1 = __builtin_bit_cast(V4, r1);
             V8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
             acc[m] = mfma32(av, pop[ks], acc[m]);
+            if constexpr (kSplitP) acc[m] = mfma32(av, plo[ks], acc[m]);
           }
       }
     }

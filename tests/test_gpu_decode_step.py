@@ -75,8 +75,8 @@ def _step_vs_calls(case, cu=None, past=None):
 
 
 def _against_oracle(case, got, what):
-    ref, ost, mag = oracle_paged_step(case)
-    assert_close(got["out"], ref, case.dtype, what, mag)
+    ref, ost = oracle_paged_step(case)
+    assert_close(got["out"], ref, case.dtype, what)
     assert got["st"] == ost, (got["st"], ost)
 
 
@@ -241,12 +241,11 @@ def test_step_in_a_graph_replays_bit_exactly():
         del junk
 
 
-def test_full_size_decode_step_sampled_rows():
-    """The GQA decode workload at full size (B=32, up to 8192 keys, a 20000-block pool):
-    bit-identical to the two calls, and sampled rows against the oracle."""
+def test_full_size_decode_step_every_row():
+    """The GQA decode workload at full size (B=32, up to 8192 keys, a 20000-block pool, NaN
+    in every unreferenced slot): bit-identical to the two calls, and every row against the
+    oracle."""
     print("decode step full size", flush=True)
     case = synth.config_gqa_paged_decode(poison=True)
     got = _step_vs_calls(case)
-    rows = np.array([r for r in range(case.T) if r % 5 == 0], dtype=np.int64)
-    ref, _, mag = oracle_paged_step(case, rows=rows)
-    assert_close(got["out"][rows], ref, case.dtype, "step_full_size", mag)
+    _against_oracle(case, got, "step_full_size")

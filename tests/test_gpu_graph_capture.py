@@ -71,11 +71,11 @@ def test_decode_prefill_sparse_step_in_one_graph():
     torch.cuda.synchronize()
     eager = [o.clone() for o in (out_d, out_p, out_s)]
     st_eager = int(st.item())
-    ref_d, dst, _ = oracle_paged_step(dec)
+    ref_d, dst = oracle_paged_step(dec)
     assert_close(eager[0], ref_d, dec.dtype, "graph eager decode")
-    ref_p, pst, _ = oracle_paged_step(pre)       # the oracle appends the prompt rows itself
+    ref_p, pst = oracle_paged_step(pre)       # the oracle appends the prompt rows itself
     assert_close(eager[1], ref_p, pre.dtype, "graph eager prefill")
-    ref_s, sst, _ = oracle_sparse(sel)
+    ref_s, sst = oracle_sparse(sel)
     assert_close(eager[2], ref_s, sel.dtype, "graph eager selected")
     assert st_eager == dst | pst | sst, (st_eager, dst, pst, sst)
 
@@ -143,7 +143,7 @@ def test_multi_layer_decode_step_in_one_graph():
     eager = [o.clone() for o in outs]
     assert int(st.item()) == 0
     for c, e in zip(cases, eager):
-        ref, ost, _ = oracle_paged_step(c)
+        ref, ost = oracle_paged_step(c)
         assert ost == 0
         assert_close(e, ref, c.dtype, "multi-layer eager")
     g = torch.cuda.CUDAGraph()

@@ -341,3 +341,21 @@ def test_host_bounds_zero_rows():
     out, st = _run_paged(case, max_seqlen_q=8, max_seqlen_k=64)
     r1, r2 = int(case.cu_seqlens_q[1]), int(case.cu_seqlens_q[2])
     assert st & oracle.STATUS_K_BOUND and np.all(out[r1:r2] == 0) and np.all(out[:r1] != 0)
+
+
+def test_pool_rows_equal_the_single_call():
+    """oracle.pool deals rows out to worker processes and puts them back: the result must be
+    the single call's, bit for bit, status included."""
+    from oracle import pool
+    case = synth.paged_case(71, kv_lens=[300, 40, 129, 1], q_lens=[60, 40, 1, 1], H_q=8, H_kv=2,
+                            D=64, dtype=synth.F16, sinks=True, local_window=50)
+    args = (case.q, case.k_cache, case.v_cache, case.cu_seqlens_q, case.seqlens_k)
+    kw = dict(H_kv=2, block_table=case.block_table, block_size=case.block_size,
+              max_seqlen_q=case.max_seqlen_q, max_seqlen_k=case.max_seqlen_k, scale=case.scale,
+              local_window=case.local_window, sinks=case.sinks)
+    want, wst = oracle.paged_attention(*args, **kw)
+    got, gst = pool.map_rows("paged_attention", args, kw, range(case.T), workers=3, chunk=7)
+    assert np.array_equal(got, want) and gst == wst
+    sub = [0, 5, 59, 60, 100, 101]
+    got, _ = pool.map_rows("paged_attention", args, kw, sub, workers=2, chunk=2)
+    assert np.array_equal(got, want[sub])
