@@ -316,6 +316,33 @@ SPATTN_API int paged_decode_step(const int32_t* cu_seqlens_q, const int32_t* pas
                       int32_t* status, void* stream);
 
 /*
+ * paged_decode_step_noalloc - paged_decode_step for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without workspace / workspace_bytes, the same results
+ * bit for bit.  The split-K partials go to a static device array of the library, 16 MiB
+ * per GPU (SPATTN_NOALLOC_SCRATCH_BYTES), held from the first call on a device until the
+ * process ends; the call itself allocates nothing.  A call whose partials need more
+ * (attention_workspace_bytes(SPATTN_KIND_PAGED, ...) > SPATTN_NOALLOC_SCRATCH_BYTES, e.g.
+ * more than about 60 decode rows of 64 heads x 8192 keys) returns SPATTN_ERR_WORKSPACE and
+ * enqueues nothing.  The array needs no clearing between calls (every partial a call reads
+ * was written by the same call).  All calls on one GPU share that GPU's array, which keeps
+ * the last call's contents: calls that may overlap on one GPU (different streams without
+ * ordering between them) race and must not be made.  The current device must be the
+ * device of `stream` (SPATTN_ERR_UNSUPPORTED otherwise); SPATTN_ERR_LAUNCH if the array's
+ * device address cannot be found.  Argument errors are reported as by paged_decode_step,
+ * before the array is looked up.
+ */
+#define SPATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+SPATTN_API int paged_decode_step_noalloc(const int32_t* cu_seqlens_q, const int32_t* past_seqlens,
+                      int B, int T, int32_t* seqlens_q, int32_t* seqlens_k, const void* q,
+                      const void* k_new, const void* v_new, int dtype, void* k_cache,
+                      void* v_cache, int cache_dtype, const int32_t* block_table,
+                      int max_blocks_per_seq, int block_size, int num_blocks,
+                      const float* key_scale, const float* value_scale, int max_seqlen_q,
+                      int max_seqlen_k, int H_q, int H_kv, int D, float scale, int local_window,
+                      const float* sinks, void* out, int32_t* status, void* stream);
+
+/*
  * sparse_attention_fwd - attention over selected cache rows ([DSA] Description: selected
  * main-cache mode and local-plus-auxiliary mode, guarded int32 indices, joint FP32 stable
  * softmax with optional sink, shared auxiliary K/V storage; [DSA] review: the selection

@@ -286,6 +286,32 @@ def paged_decode_step(cu_seqlens_q: torch.Tensor, past_seqlens: torch.Tensor, T:
         _stream(cu_seqlens_q)))
 
 
+def paged_decode_step_noalloc(cu_seqlens_q: torch.Tensor, past_seqlens: torch.Tensor, T: int,
+                              seqlens_q: torch.Tensor, seqlens_k: torch.Tensor, q: torch.Tensor,
+                              k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                              v_cache: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                              out: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                              key_scale: Optional[torch.Tensor] = None,
+                              value_scale: Optional[torch.Tensor] = None, scale: float = 0.0,
+                              local_window: int = -1, sinks: Optional[torch.Tensor] = None,
+                              status: Optional[torch.Tensor] = None) -> None:
+    """paged_decode_step with its split-K partials in the library's static device array
+    (no allocation by the call or by this binding)."""
+    B = int(past_seqlens.shape[0])
+    _, H_q, D = (int(x) for x in q.shape)
+    H_kv = int(k_cache.shape[1])
+    nb, bs, mbps = _cache_dims(k_cache, block_table)
+    lib = _lib.load()
+    _check("paged_decode_step_noalloc", lib.paged_decode_step_noalloc(
+        _i32(cu_seqlens_q, "cu_seqlens_q"), _i32(past_seqlens, "past_seqlens"), B, int(T),
+        _i32(seqlens_q, "seqlens_q"), _i32(seqlens_k, "seqlens_k"), _ptr(q, "q"),
+        _ptr(k_new, "k_new"), _ptr(v_new, "v_new"), _dt(q), _ptr(k_cache, "k_cache"),
+        _ptr(v_cache, "v_cache"), _dt(k_cache), _i32(block_table, "block_table"), mbps, bs, nb,
+        _ptr(key_scale, "key_scale"), _ptr(value_scale, "value_scale"), int(max_seqlen_q),
+        int(max_seqlen_k), H_q, H_kv, D, float(scale), int(local_window), _ptr(sinks, "sinks"),
+        _ptr(out, "out"), _i32(status, "status"), _stream(cu_seqlens_q)))
+
+
 def sparse_attention_fwd(q: torch.Tensor, mode: int, k_cache: torch.Tensor, v_cache: torch.Tensor,
                          cu_seqlens_q: torch.Tensor, seqlens_k: torch.Tensor, max_seqlen_q: int,
                          sel_idx: torch.Tensor, out: torch.Tensor,

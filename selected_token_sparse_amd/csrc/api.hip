@@ -2,6 +2,8 @@
 // then the launchers.  The declarations and their contracts are in include/spattn.h.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "append.h"
@@ -52,7 +54,96 @@ int check_heads(int H_q, int H_kv, int D) {
 
 float resolve_scale(float scale, int D) { return scale == 0.0f ? 1.0f / sqrtf((float)D) : scale; }
 
+
+// ---------------------------------------------------------------------------------------
+// Scratch of paged_decode_step_noalloc: the split-K partials in a static device array
+// (one copy per GPU, held until the process ends), for callers that cannot allocate.
+// Host code never passes `scratch` itself (its host-side name is not a device address):
+// the device address is looked up once per device with hipGetSymbolAddress and kept.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = SPATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on its first use).  The
+// stream must belong to the current device: each device has its own copy of the array.
+int noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPATTN_ERR_LAUNCH;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return SPATTN_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return SPATTN_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPATTN_OK;
+}
+
 }  // namespace
+
+static int decode_step_impl(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B, int T,
+                      int32_t* seqlens_q, int32_t* seqlens_k, const void* q, const void* k_new,
+                      const void* v_new, int dtype, void* k_cache, void* v_cache, int cache_dtype,
+                      const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                      int num_blocks, const float* key_scale, const float* value_scale,
+                      int max_seqlen_q, int max_seqlen_k, int H_q, int H_kv, int D, float scale,
+                      int local_window, const float* sinks, void* out, void* workspace,
+                      size_t workspace_bytes, int32_t* status, void* stream,
+                      bool static_scratch) {
+  if (dtype != SPATTN_F16 && dtype != SPATTN_BF16) return float_dtype(dtype) ? SPATTN_ERR_UNSUPPORTED : SPATTN_ERR_DTYPE;
+  int rc = check_heads(H_q, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+  if (B < 0 || T < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return SPATTN_ERR_SHAPE;
+  if (B > kStepMaxB) return SPATTN_ERR_UNSUPPORTED;
+  if (use_prefill_path(SPATTN_KIND_PAGED, dtype, max_seqlen_q)) return SPATTN_ERR_UNSUPPORTED;
+  if (cu_seqlens_q == nullptr || past_seqlens == nullptr || seqlens_q == nullptr || seqlens_k == nullptr)
+    return SPATTN_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  // no rows: the metadata is all there is to do
+  if (T == 0) return launch_prepare_seqlens(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k,
+                                            nullptr, nullptr, status, st);
+  if (B == 0) return SPATTN_ERR_SHAPE;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr) return SPATTN_ERR_NULL;
+  if (misaligned(q) || misaligned(k_new) || misaligned(v_new) || misaligned(out)) return SPATTN_ERR_SHAPE;
+  rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
+                   block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
+  if (rc != SPATTN_OK) return rc;
+
+  AttnArgs a{};
+  a.kind = SPATTN_KIND_PAGED;
+  a.q = q; a.dtype = dtype; a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+  a.block_table = block_table; a.max_blocks = max_blocks_per_seq; a.block_size = block_size;
+  a.num_blocks = num_blocks; a.key_scale = key_scale; a.value_scale = value_scale;
+  a.cu = cu_seqlens_q; a.seqlens_k = nullptr; a.B = B; a.T = T;
+  a.max_q = max_seqlen_q; a.max_k = max_seqlen_k;
+  a.window = local_window > 0 ? local_window : 0;
+  a.H_q = H_q; a.H_kv = H_kv; a.D = D;
+  a.scale = resolve_scale(scale, D);
+  a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
+  a.past = past_seqlens; a.k_new = k_new; a.v_new = v_new;
+  a.seqlens_q_out = seqlens_q; a.seqlens_k_out = seqlens_k;
+  const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, max_seqlen_k, 0,
+                                         a.window, H_q, H_kv, D);
+  if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
+  if (static_scratch && plan.ws_bytes > 0) {
+    // the partials go to the static array: checked against its size, then its address
+    if (plan.ws_bytes > kNoAllocScratchBytes) return SPATTN_ERR_WORKSPACE;
+    const int rc2 = noalloc_scratch(st, &a.workspace);
+    if (rc2 != SPATTN_OK) return rc2;
+  } else if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes)) {
+    return SPATTN_ERR_WORKSPACE;
+  }
+  return launch_split_attention(a, plan, st);
+}
 
 extern "C" {
 
@@ -246,44 +337,27 @@ int paged_decode_step(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, 
                       int max_seqlen_q, int max_seqlen_k, int H_q, int H_kv, int D, float scale,
                       int local_window, const float* sinks, void* out, void* workspace,
                       size_t workspace_bytes, int32_t* status, void* stream) {
-  if (dtype != SPATTN_F16 && dtype != SPATTN_BF16) return float_dtype(dtype) ? SPATTN_ERR_UNSUPPORTED : SPATTN_ERR_DTYPE;
-  int rc = check_heads(H_q, H_kv, D);
-  if (rc != SPATTN_OK) return rc;
-  if (B < 0 || T < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return SPATTN_ERR_SHAPE;
-  if (B > kStepMaxB) return SPATTN_ERR_UNSUPPORTED;
-  if (use_prefill_path(SPATTN_KIND_PAGED, dtype, max_seqlen_q)) return SPATTN_ERR_UNSUPPORTED;
-  if (cu_seqlens_q == nullptr || past_seqlens == nullptr || seqlens_q == nullptr || seqlens_k == nullptr)
-    return SPATTN_ERR_NULL;
-  hipStream_t st = (hipStream_t)stream;
-  // no rows: the metadata is all there is to do
-  if (T == 0) return launch_prepare_seqlens(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k,
-                                            nullptr, nullptr, status, st);
-  if (B == 0) return SPATTN_ERR_SHAPE;
-  if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr) return SPATTN_ERR_NULL;
-  if (misaligned(q) || misaligned(k_new) || misaligned(v_new) || misaligned(out)) return SPATTN_ERR_SHAPE;
-  rc = check_cache(k_cache, v_cache, dtype, cache_dtype, block_table, max_blocks_per_seq,
-                   block_size, num_blocks, key_scale, value_scale, B, H_kv, D);
-  if (rc != SPATTN_OK) return rc;
+  return decode_step_impl(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k, q, k_new, v_new,
+                          dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq,
+                          block_size, num_blocks, key_scale, value_scale, max_seqlen_q,
+                          max_seqlen_k, H_q, H_kv, D, scale, local_window, sinks, out, workspace,
+                          workspace_bytes, status, stream, false);
+}
 
-  AttnArgs a{};
-  a.kind = SPATTN_KIND_PAGED;
-  a.q = q; a.dtype = dtype; a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
-  a.block_table = block_table; a.max_blocks = max_blocks_per_seq; a.block_size = block_size;
-  a.num_blocks = num_blocks; a.key_scale = key_scale; a.value_scale = value_scale;
-  a.cu = cu_seqlens_q; a.seqlens_k = nullptr; a.B = B; a.T = T;
-  a.max_q = max_seqlen_q; a.max_k = max_seqlen_k;
-  a.window = local_window > 0 ? local_window : 0;
-  a.H_q = H_q; a.H_kv = H_kv; a.D = D;
-  a.scale = resolve_scale(scale, D);
-  a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
-  a.past = past_seqlens; a.k_new = k_new; a.v_new = v_new;
-  a.seqlens_q_out = seqlens_q; a.seqlens_k_out = seqlens_k;
-  const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, max_seqlen_k, 0,
-                                         a.window, H_q, H_kv, D);
-  if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
-  if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
-    return SPATTN_ERR_WORKSPACE;
-  return launch_split_attention(a, plan, st);
+int paged_decode_step_noalloc(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B,
+                              int T, int32_t* seqlens_q, int32_t* seqlens_k, const void* q,
+                              const void* k_new, const void* v_new, int dtype, void* k_cache,
+                              void* v_cache, int cache_dtype, const int32_t* block_table,
+                              int max_blocks_per_seq, int block_size, int num_blocks,
+                              const float* key_scale, const float* value_scale, int max_seqlen_q,
+                              int max_seqlen_k, int H_q, int H_kv, int D, float scale,
+                              int local_window, const float* sinks, void* out, int32_t* status,
+                              void* stream) {
+  return decode_step_impl(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k, q, k_new, v_new,
+                          dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq,
+                          block_size, num_blocks, key_scale, value_scale, max_seqlen_q,
+                          max_seqlen_k, H_q, H_kv, D, scale, local_window, sinks, out, nullptr, 0,
+                          status, stream, true);
 }
 
 int sparse_attention_fwd(const void* q, int dtype, int mode, const void* k_cache,

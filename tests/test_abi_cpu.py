@@ -21,7 +21,8 @@ def test_header_declares_the_abi():
     names = _declared()
     assert set(names) == {"prepare_seqlens", "kv_cache_append", "prepare_and_append",
                           "qkv_prologue", "topk_select",
-                          "paged_attention_fwd", "paged_decode_step", "sparse_attention_fwd",
+                          "paged_attention_fwd", "paged_decode_step",
+                          "paged_decode_step_noalloc", "sparse_attention_fwd",
                           "attention_workspace_bytes"}
 
 
@@ -207,6 +208,35 @@ def test_decode_step_argument_errors(lib):
     for i in (6, 7, 8, 27):            # q, k_new, v_new, out off a 16-byte boundary
         assert call(**{f"a{i}": MIS}) == -2
     assert call(a10=MIS) == -2
+
+
+def test_noalloc_decode_step_argument_errors(lib):
+    """The allocation-free step validates like paged_decode_step, before it looks up its
+    static scratch (so no HIP call is made here), and rejects plans whose split-K partials
+    exceed the 16 MiB array."""
+    f = lib.paged_decode_step_noalloc
+    # paged_decode_step's arguments without workspace / workspace_bytes
+    base = [FAKE, FAKE, 2, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, FAKE, 4, 16, 8,
+            None, None, 1, 64, 4, 2, 64, 0.0, -1, None, FAKE, None, None]
+    def call(**kv):
+        a = list(base)
+        for i, v in kv.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a9=0) == -4            # float32 activations
+    assert call(a9=3) == -3
+    assert call(a2=256) == -4
+    assert call(a19=64) == -4          # a query block for the prefill kernel
+    assert call(a0=None) == -1
+    assert call(a27=None) == -1
+    assert call(a12=2) == -3
+    assert call(a23=96) == -4
+    assert call(a2=0) == -2
+    assert call(a6=MIS) == -2
+    # 200 rows of H 64/8 with a 65536-key bound: about 105 MB of partials
+    ws = lib.attention_workspace_bytes(0, 1, 200, 200, 1, 65536, 0, -1, 64, 8, 64)
+    assert ws > 16 << 20
+    assert call(a2=200, a3=200, a20=65536, a21=64, a22=8) == -5
 
 
 def test_topk_argument_errors(lib):
