@@ -85,6 +85,25 @@ def _prefill_flops(case):
     return pairs * case.H_q * 4 * case.D
 
 
+def _prefill_bytes(case):
+    """Algorithmic HBM bytes of a prefill call: Q and out once, and the K+V rows of every
+    key some row of the request sees, once per (request, KV head): positions
+    max(0, p_first - W + 1) .. p_last."""
+    esize = {0: 4, 1: 2, 2: 2, 3: 1, 4: 1}[case.cache_dtype]
+    qo = 2 * case.T * case.H_q * case.D * (4 if case.dtype == 0 else 2)
+    keys = 0
+    cu = case.cu_seqlens_q
+    for b in range(case.B):
+        q_len = int(cu[b + 1] - cu[b])
+        if q_len == 0:
+            continue
+        kv = int(case.seqlens_k[b]) + 1
+        p_first, p_last = kv - q_len, kv - 1
+        lo = max(0, p_first - case.local_window + 1) if case.local_window > 0 else 0
+        keys += max(0, p_last - lo + 1)
+    return qo + keys * case.H_kv * case.D * esize * 2
+
+
 def _queue_ahead():
     """A short device spin before a timed loop, so that the host has queued the loop's
     launches before the GPU reaches them and the events time the GPU, not the launches."""
@@ -288,14 +307,16 @@ def bench_prefill(window, steps, warmup, cache_dtype=None):
     ms = sorted(a.elapsed_time(b) for a, b in evs)
     med = ms[len(ms) // 2]
     flops = _prefill_flops(case)
-    qo_bytes = 2 * case.T * case.H_q * case.D * 2
+    alg = _prefill_bytes(case)
     tfl = flops / (med * 1e-3) / 1e12
+    gbs = alg / (med * 1e-3) / 1e9
     return {
         "workload": case.name, "window": window, "median_us": round(med * 1e3, 2),
         "p10_p90_us": _p10_p90(ms),
         "tflops": round(tfl, 2), "frac_mfma_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         "algorithmic_gflop": round(flops / 1e9, 3),
-        "qo_gbs": round(qo_bytes / (med * 1e-3) / 1e9, 1),
+        "algorithmic_bytes": alg, "gbs": round(gbs, 1),
+        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
     }
 
 
@@ -492,39 +513,70 @@ def copy_calibration(mib, reps=4):
     print(f"copy calibration: {reps} copies of {mib << 20} bytes", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(target_s=12.0):
-    """The oracle (numpy float64, BLAS limited to one thread) on the decode step of the same
-    workload: metadata, append and attention for the first rows, repeated until ~target_s."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(seconds=10.0):
+    """The oracle (numpy float64) on the host cores, as a process pool over rows (all cores
+    this process may use, at most 16: the machine's CPU share for one GPU), each worker on one
+    BLAS thread.  Two legs on the same workloads as the GPU lines:
+    - decode: the attention rows of the GQA paged decode step, after one oracle metadata +
+      append pass (not timed), cycled until `seconds` have passed; GB/s of the rows' KV bytes;
+    - prefill: rows of the windowed paged prefill (W=128), cycled likewise; TFLOP/s of the
+      rows' algorithmic flops (4 D per visible (row, query head, key)).
+    Must run before the GPU is initialised: the pool forks, sharing the arrays."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     import oracle
     import synth
+    from oracle import pool
 
-    case = synth.config_gqa_paged_decode()
-    cu = case.cu_seqlens_q
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        done_bytes, rows_done, passes = 0, 0, 0
+    workers = pool.default_workers()
+    legs = {}
+    for leg in ("decode", "prefill"):
+        case = synth.config_gqa_paged_decode() if leg == "decode" else synth.config_paged_prefill_window()
+        cu = case.cu_seqlens_q
         _, sk, _, _, _ = oracle.prepare_seqlens(cu, case.past_seqlens, case.T)
         kc, vc, _ = oracle.kv_cache_append(case.k_new, case.v_new, cu, sk, case.k_cache,
                                            case.v_cache, case.block_table, case.block_size)
-        per_row = []
-        for r in range(case.T):
-            b = int(np.searchsorted(cu, r, side="right") - 1)
-            per_row.append((int(sk[b]) + 1) * case.H_kv * case.D * 2 * 2)
-        while time.perf_counter() - t0 < target_s:
-            r = rows_done % case.T
-            oracle.paged_attention(case.q, kc, vc, cu, sk, H_kv=case.H_kv,
-                                   block_table=case.block_table, block_size=case.block_size,
-                                   max_seqlen_q=case.max_seqlen_q, max_seqlen_k=case.max_seqlen_k,
-                                   scale=case.scale, sinks=case.sinks, rows=[r])
-            done_bytes += per_row[r]
-            rows_done += 1
-        dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows_done} decode rows of the GQA paged decode workload (oracle attention, "
-                      f"after one oracle metadata + append pass), {dt:.1f} s, KV bytes of those rows"}
+        # per-row work: visible keys of each row
+        req = np.searchsorted(cu, np.arange(case.T), side="right") - 1
+        q_len = (cu[req + 1] - cu[req]).astype(np.int64)
+        p = (sk[req].astype(np.int64) + 1) - q_len + (np.arange(case.T) - cu[req])
+        lo = np.maximum(0, p - case.local_window + 1) if case.local_window > 0 else 0
+        keys = np.maximum(0, p - lo + 1)
+        args = (case.q, kc, vc, cu, sk)
+        kw = dict(H_kv=case.H_kv, block_table=case.block_table, block_size=case.block_size,
+                  max_seqlen_q=case.max_seqlen_q, max_seqlen_k=case.max_seqlen_k, scale=case.scale,
+                  local_window=case.local_window, sinks=case.sinks)
+        chunk = 1 if leg == "decode" else 16
+        done, dt = pool.run_for("paged_attention", args, kw, range(case.T), workers, seconds,
+                                chunk=chunk, method="fork")
+        k = keys[np.asarray(done, dtype=np.int64)]
+        if leg == "decode":
+            kv_bytes = int(k.sum()) * case.H_kv * case.D * 2 * 2
+            legs[leg] = {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s",
+                         "sample": f"{len(done)} row evaluations (the 31 rows cycled) of the GQA "
+                                   f"paged decode workload, {dt:.1f} s wall, KV bytes of those rows"}
+        else:
+            flops = int(k.sum()) * case.H_q * 4 * case.D
+            legs[leg] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                         "sample": f"{len(done)} row evaluations (rows cycled in order) of the "
+                                   f"windowed paged prefill workload, {dt:.1f} s wall, "
+                                   f"algorithmic flops of those rows"}
+        del case, kc, vc
+    out = dict(legs["decode"])
+    out.update({"cores": workers, "kind": "oracle", "host_cpus": os.cpu_count(),
+                "cpu_model": _cpu_model(), "prefill": legs["prefill"]})
+    return out
 
 
 def main():
@@ -548,6 +600,9 @@ def main():
               "GPUs needs one all-gather of split partials before the merge)",
               file=sys.stderr)
         sys.exit(2)
+    # the oracle's CPU baseline first: its process pool forks, which must happen before
+    # anything initialises the GPU in this process
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
@@ -623,8 +678,8 @@ def main():
         line["prologue_prefill"] = bench_prologue("prefill", 50, 5)
     if not args.no_topk:
         line["topk"] = bench_topk(30, 3)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -4,14 +4,17 @@ TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``: used by ``tests/`` and b
 ``cpu_baseline`` leg of ``bench.py``.  It adds no arithmetic: every output row is the one
 ``paged_attention`` / ``sparse_attention`` compute for it (their ``rows`` argument), the
 rows are only dealt out to processes and put back in order, and the status words are
-OR-ed.  Workers are started with the "spawn" method (they import numpy and this package
-only, never the GPU library) and each runs its BLAS on one thread.
+OR-ed.  Workers import numpy and this package only (never the GPU library), and each runs
+its BLAS on one thread.  ``map_rows`` starts them with the "spawn" method, which is safe in
+a process that already uses the GPU; ``run_for`` (the timed CPU baseline) may "fork"
+them, sharing the parent's arrays without copies, when the GPU has not been initialised.
 """
 from __future__ import annotations
 
 import multiprocessing as mp
 import os
-from concurrent.futures import ProcessPoolExecutor
+import time
+from concurrent.futures import FIRST_COMPLETED, ProcessPoolExecutor, wait
 
 import numpy as np
 
@@ -59,3 +62,45 @@ def map_rows(fn_name: str, args: tuple, kwargs: dict, rows, workers: int, chunk:
     for _, st in parts:
         status |= st
     return np.concatenate([o for o, _ in parts], axis=0), status
+
+
+def run_for(fn_name: str, args: tuple, kwargs: dict, rows, workers: int, seconds: float,
+            chunk: int = 8, method: str = "spawn"):
+    """Evaluate ``oracle.<fn_name>`` on chunks of ``rows`` (cycling through them) on
+    ``workers`` processes, keeping every worker busy, until ``seconds`` of wall time have
+    passed.  Returns ``(rows_done, elapsed_s)``: the row ids of every completed chunk (with
+    repeats) and the time from the first submission to the last completion, worker start-up
+    excluded."""
+    rows = [int(r) for r in rows]
+    chunks = [rows[i:i + chunk] for i in range(0, len(rows), chunk)]
+    ctx = mp.get_context(method)
+    done = []
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx, initializer=_init,
+                             initargs=(fn_name, args, kwargs)) as ex:
+        # start every worker (imports, initializer) before the clock starts
+        list(ex.map(_ready, range(4 * workers)))
+        nxt = 0
+        pending = set()
+        t0 = time.perf_counter()
+        for _ in range(2 * workers):
+            pending.add(ex.submit(_tagged, chunks[nxt % len(chunks)]))
+            nxt += 1
+        t_end = t0
+        while pending:
+            fin, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for f in fin:
+                done.extend(f.result())
+                t_end = time.perf_counter()
+                if t_end - t0 < seconds:
+                    pending.add(ex.submit(_tagged, chunks[nxt % len(chunks)]))
+                    nxt += 1
+    return done, t_end - t0
+
+
+def _ready(_):
+    return os.getpid()
+
+
+def _tagged(rows):
+    _run(rows)
+    return rows

@@ -78,3 +78,15 @@ def test_percentiles_of_sorted_call_times():
     ms = [0.001 * (i + 1) for i in range(100)]        # 1 .. 100 us
     assert bench._p10_p90(ms) == (11.0, 91.0)
     assert bench._p10_p90([0.005]) == (5.0, 5.0)
+
+
+def test_prefill_bytes_are_q_out_and_each_visible_key_once():
+    # fresh prompts: Q and out 5120 rows x 64 heads x 64 dims x 2 bytes each; every key of
+    # a prompt is seen by some row, so K + V once per KV head: 5120 x 8 x 64 x 2 x 2
+    for w in (128, -1):
+        case = synth.config_paged_prefill_window(window=w)
+        assert bench._prefill_bytes(case) == 2 * 5120 * 64 * 64 * 2 + 5120 * 8 * 64 * 4
+    # a chunk of 40 rows after 160 past keys with a 50-key window sees positions 111..199
+    case = synth.paged_case(3, kv_lens=[200], q_lens=[40], H_q=8, H_kv=2, D=64,
+                            dtype=synth.F16, local_window=50)
+    assert bench._prefill_bytes(case) == 2 * 40 * 8 * 64 * 2 + 89 * 2 * 64 * 2 * 2
