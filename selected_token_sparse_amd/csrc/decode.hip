@@ -344,12 +344,12 @@ __device__ __forceinline__ uint32_t tile_valid(int row0, int row1) {
 
 // The key loop of one wave over one source, two tiles deep: the next tile's loads are in
 // flight while the current tile is computed (V tiles alternate between two LDS buffers).
-// `rows` holds the cache-row index (row of D elements counted from kbase / vbase) of each
-// key of the split, or -1; `dk` is any in-bounds row and `dv` an in-bounds row of finite
-// values, read for masked keys.
-template <typename OpT, typename KT, int D>
+// `row_at(k)` gives the cache-row index (row of D elements counted from kbase / vbase) of
+// key k < n_keys of the split, or -1; `dk` is any in-bounds row and `dv` an in-bounds row
+// of finite values, read for masked keys.
+template <typename OpT, typename KT, int D, typename RowAt>
 __device__ __forceinline__ void wave_keys(const KT* __restrict__ kbase, const KT* __restrict__ vbase,
-                                          const KT* dk, const KT* dv, const int32_t* rows, int n_keys,
+                                          const KT* dk, const KT* dv, RowAt row_at, int n_keys,
                                           const typename OpVec<OpT>::v8 (&qop)[2][D / 32],
                                           float scale_log2, unsigned char* vbuf2, float& m_run,
                                           float& l_run, f32x4 (&acc)[D / 16]) {
@@ -363,7 +363,7 @@ __device__ __forceinline__ void wave_keys(const KT* __restrict__ kbase, const KT
   const int n_tiles = (n_keys + kTile - 1) / kTile;
   auto row_of = [&](int tile, int k) {
     const int key = tile * kTile + k;
-    return key < n_keys ? rows[key] : -1;
+    return key < n_keys ? row_at(key) : -1;
   };
   TileRegs<OpT, KT, D> ta, tb;
   int tile = wave;
@@ -440,6 +440,44 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
   return -1;
 }
 
+// Per-request metadata of a workgroup, staged in LDS (`meta`, 2 B + 1 ints) when `to_lds`.
+// Fused decode step (kStep), one load round and one barrier: meta[0..B] = cu,
+// meta[B+1+b] = past[b] + q_len_b - 1 (seqlens_k, as prepare_seqlens derives it for
+// well-formed metadata); returns whether the metadata is malformed (B + 1 <= kThreads).
+// Otherwise cu / seqlens_k are copied, or read from global memory when !to_lds.
+template <bool kStep>
+__device__ __forceinline__ bool stage_metadata(const SplitParams& P, int32_t* meta, bool to_lds,
+                                               const int32_t*& cu, const int32_t*& skl) {
+  const int tid = threadIdx.x;
+  cu = P.cu;
+  skl = P.seqlens_k;
+  if constexpr (kStep) {
+    const int n = P.B + 1;
+    const int cv = tid < n ? P.cu[tid] : 0;
+    const int cn = tid < P.B ? P.cu[tid + 1] : 0;
+    const int pb = tid < P.B ? P.past[tid] : 0;
+    const bool bad = (tid < P.B && (cn < cv || pb < 0)) ||
+                     (tid == 0 && (cv != 0 || P.cu[P.B] != P.T));
+    if (tid < n) meta[tid] = cv;
+    if (tid < P.B) meta[n + tid] = pb + (cn - cv) - 1;
+    const bool step_bad = __syncthreads_or(bad) != 0;
+    cu = meta;
+    skl = meta + n;
+    return step_bad;
+  } else {
+    if (to_lds) {
+      for (int i = tid; i <= P.B; i += kThreads) {
+        meta[i] = P.cu[i];
+        if (i < P.B) meta[P.B + 1 + i] = P.seqlens_k[i];
+      }
+      __syncthreads();
+      cu = meta;
+      skl = meta + P.B + 1;
+    }
+    return false;
+  }
+}
+
 // Fused decode step, workgroup 0: seqlens_q / seqlens_k exactly as prepare_seqlens writes
 // them.  Malformed metadata takes its sanitised boundaries: the running maximum of cu
 // clamped to [0, T] (one per thread, B + 1 <= kThreads) and negative past read as 0.
@@ -509,6 +547,123 @@ __device__ __forceinline__ void step_write_keys(const SplitParams& P, int b, int
   }
 }
 
+// One wave's key loop over main-cache rows.  Quantised caches fold the per-channel key
+// scale into the query.  The folded value x = q * s is carried as hi + lo, two 16-bit
+// operands (hi = x rounded, lo = the rounding error rounded), and S takes one product with
+// each, so the scores keep about 22 bits of x instead of 11: a single 16-bit operand would
+// put a relative error of 2^-11 on every term q_d k_d, i.e. score errors up to
+// 2^-11 sum_d |q_d k_d|.  `qraw` holds this lane's query dims as loaded (16-bit caches);
+// lanes with hv false carry a zero query.
+template <typename QT, typename KT, int D, typename RowAt>
+__device__ __forceinline__ void main_cache_keys(const SplitParams& P, const QT* qrow,
+                                                const QT* q0row, bool hv,
+                                                const i32x4 (&qraw)[D / 32], int c, RowAt row_at,
+                                                int n_keys, unsigned char* vbuf2, float& m_run,
+                                                float& l_run, f32x4 (&acc)[D / 16]) {
+  typedef typename std::conditional<sizeof(KT) == 1, f16, KT>::type OpM;
+  constexpr float kUnit = std::is_same<KT, uint8_t>::value ? kFp8Unit : 1.0f;
+  const int grp = (threadIdx.x & 63) >> 4;
+  typename OpVec<OpM>::v8 qop[2][D / 32];
+#pragma unroll
+  for (int kc = 0; kc < D / 32; ++kc) {
+    const int col = qk_col<KT>(kc, grp);
+    if constexpr (sizeof(KT) == 1) {
+      // the query dims of this step's K operand (not those of qraw's layout)
+      const typename OpVec<QT>::v8 qv = __builtin_bit_cast(
+          typename OpVec<QT>::v8, hv ? load16(qrow + col) : i32x4{0, 0, 0, 0});
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = hv ? to_f32((QT)qv[e]) * (P.key_scale[c * D + col + e] * kUnit) : 0.f;
+        const OpM hi = (OpM)x;
+        qop[0][kc][e] = hi;
+        qop[1][kc][e] = (OpM)(x - (float)hi);
+      }
+    } else {
+      qop[0][kc] = __builtin_bit_cast(typename OpVec<OpM>::v8, qraw[kc]);
+      qop[1][kc] = typename OpVec<OpM>::v8{};
+    }
+  }
+  // masked keys read row 0 of the cache for K and, with 16-bit caches, the query row of
+  // the tile's first head for V (in bounds for every lane, and finite); 8-bit V of masked
+  // keys is replaced by zeros
+  const KT* dv = sizeof(KT) == 2 ? reinterpret_cast<const KT*>(q0row)
+                                 : reinterpret_cast<const KT*>(P.k_cache);
+  wave_keys<OpM, KT, D>(reinterpret_cast<const KT*>(P.k_cache),
+                        reinterpret_cast<const KT*>(P.v_cache),
+                        reinterpret_cast<const KT*>(P.k_cache), dv, row_at, n_keys, qop,
+                        P.scale_log2, vbuf2, m_run, l_run, acc);
+}
+
+// End of a workgroup's part of one (row, KV head, head tile): the four wave states (head
+// lam, dims 16m + 4grp + i) are merged in LDS and stored.  Rows of the accumulator area are
+// padded by 4 floats so the 16-byte stores of the 16 heads of a lane group fall in
+// different banks; the merge factors of each (wave, head) are computed once, by 16
+// threads.  `direct`: the workgroup saw every key of the row, so it writes the normalised
+// output (the sink folded into the normaliser); otherwise the partial (m, l, acc) of head
+// h goes to acc_dst[h * D ..] and ml_dst[h] for the merge kernel.  8-bit caches apply
+// value_scale here.  The caller has synchronised after the key loop; `area` is free
+// again when this returns.
+template <typename QT, int D>
+__device__ __forceinline__ void combine_and_store(const SplitParams& P, unsigned char* area,
+                                                  float m_run, float l_run,
+                                                  const f32x4 (&acc)[D / 16], int nh, int r,
+                                                  int c, int h0, bool use_scale, float unit,
+                                                  bool direct, float* acc_dst, float2* ml_dst) {
+  constexpr int CR = SplitLds<D>::kCombineRow;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lam = lane & 15, grp = lane >> 4;
+  float* cm = reinterpret_cast<float*>(area);              // [wave][16] m
+  float* cl = cm + kWaves * 16;                           // [wave][16] l
+  float* cf = cl + kWaves * 16;                           // [wave][16] merge factor
+  float* cML = cf + kWaves * 16;                          // [16] (M, L)
+  float* ca = cML + kWaves * 16;                          // [wave][16][CR] acc
+  if (grp == 0) { cm[wave * 16 + lam] = m_run; cl[wave * 16 + lam] = l_run; }
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m)
+    *reinterpret_cast<f32x4*>(ca + (wave * 16 + lam) * CR + 16 * m + 4 * grp) = acc[m];
+  __syncthreads();
+  if (tid < 16) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + tid]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = M != kNegInf ? exp2_safe(cm[w * 16 + tid] - M) : 0.f;
+      cf[w * 16 + tid] = f;
+      L += cl[w * 16 + tid] * f;
+    }
+    cML[2 * tid] = M;
+    cML[2 * tid + 1] = L;
+  }
+  __syncthreads();
+  for (int e = tid; e < 16 * D; e += kThreads) {
+    const int h = e / D, d = e - h * D;
+    if (h >= nh) continue;
+    const float M = cML[2 * h], L = cML[2 * h + 1];
+    float A = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) A += ca[(w * 16 + h) * CR + d] * cf[w * 16 + h];
+      if (use_scale) A *= P.value_scale[c * D + d] * unit;
+    }
+    const int head = h0 + h;
+    if (direct) {
+      float res = 0.f;
+      if (M != kNegInf) {
+        const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
+        const float M2 = fmaxf(M, sg);
+        const float f = exp2_safe(M - M2);
+        res = A * f / (L * f + exp2_safe(sg - M2));
+      }
+      reinterpret_cast<QT*>(P.out)[((int64_t)r * P.H_q + head) * D + d] = from_f32<QT>(res);
+    } else {
+      acc_dst[h * D + d] = A;
+      if (d == 0) ml_dst[h] = make_float2(M, L);
+    }
+  }
+  __syncthreads();
+}
+
 // Occupancy hint for D = 64, where each wave keeps two tiles in flight: 5 waves per SIMD
 // for 16-bit caches (that register budget holds both tiles' K operands without spilling);
 // one fewer when the kernel also carries the second (window) source; 4 for INT8 caches,
@@ -565,31 +720,8 @@ void split_attn_kernel(SplitParams P) {
   const int32_t* cu = P.cu;
   const int32_t* skl = P.seqlens_k;
   __shared__ int wave_flags[kWaves];
-  bool step_bad = false;                               // fused step, malformed metadata
-  if constexpr (kStep) {
-    // Fused step, one load round and one barrier: meta[0..B] = cu, meta[B+1+b] =
-    // past[b] + q_len_b - 1 (seqlens_k; well-formed metadata), and whether the metadata is
-    // well formed.  Workgroup 0 also writes seqlens_q / seqlens_k as prepare_seqlens does.
-    const int n = P.B + 1;                             // <= kThreads
-    const int cv = tid < n ? P.cu[tid] : 0;
-    const int cn = tid < P.B ? P.cu[tid + 1] : 0;
-    const int pb = tid < P.B ? P.past[tid] : 0;
-    const bool bad = (tid < P.B && (cn < cv || pb < 0)) ||
-                     (tid == 0 && (cv != 0 || P.cu[P.B] != P.T));
-    if (tid < n) meta[tid] = cv;
-    if (tid < P.B) meta[n + tid] = pb + (cn - cv) - 1;
-    step_bad = __syncthreads_or(bad) != 0;
-    cu = meta;
-    skl = meta + n;
-  } else if (P.meta_lds) {
-    for (int i = tid; i <= P.B; i += kThreads) {
-      meta[i] = P.cu[i];
-      if (i < P.B) meta[P.B + 1 + i] = P.seqlens_k[i];
-    }
-    __syncthreads();
-    cu = meta;
-    skl = meta + P.B + 1;
-  }
+  // fused step: malformed metadata
+  const bool step_bad = stage_metadata<kStep>(P, meta, P.meta_lds != 0, cu, skl);
   int flags = 0;
   RowInfo ri;
   if (step_bad) {
@@ -639,42 +771,11 @@ void split_attn_kernel(SplitParams P) {
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool use_scale = sizeof(KT) == 1 && sr.src != SRC_AUX;
+  auto row_at = [&](int k) { return rows[k]; };
   if (sr.n_keys > 0) {
     if (KIND != SPATTN_KIND_LOCAL_AUX || sr.src != SRC_AUX) {
-      // Quantised caches fold the per-channel key scale into the query.  The folded value
-      // x = q * s is carried as hi + lo, two 16-bit operands (hi = x rounded, lo = the
-      // rounding error rounded), and S takes one product with each, so the scores keep
-      // about 22 bits of x instead of 11: a single 16-bit operand would put a relative
-      // error of 2^-11 on every term q_d k_d, i.e. score errors up to 2^-11 sum_d |q_d k_d|.
-      typename OpVec<OpM>::v8 qop[2][D / 32];
-#pragma unroll
-      for (int kc = 0; kc < D / 32; ++kc) {
-        const int col = qk_col<KT>(kc, grp);
-        if constexpr (sizeof(KT) == 1) {
-          // the query dims of this step's K operand (not those of qraw's layout)
-          const typename OpVec<QT>::v8 qv = __builtin_bit_cast(
-              typename OpVec<QT>::v8, hv ? load16(qrow + col) : i32x4{0, 0, 0, 0});
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = hv ? to_f32((QT)qv[e]) * (P.key_scale[c * D + col + e] * kUnit) : 0.f;
-            const OpM hi = (OpM)x;
-            qop[0][kc][e] = hi;
-            qop[1][kc][e] = (OpM)(x - (float)hi);
-          }
-        } else {
-          qop[0][kc] = __builtin_bit_cast(typename OpVec<OpM>::v8, qraw[kc]);
-          qop[1][kc] = typename OpVec<OpM>::v8{};
-        }
-      }
-      // masked keys read row 0 of the cache for K and, with 16-bit caches, the query row of
-      // the tile's first head for V (in bounds for every lane, and finite); INT8 V of masked
-      // keys is replaced by zeros
-      const KT* dv = sizeof(KT) == 2 ? reinterpret_cast<const KT*>(q0row)
-                                     : reinterpret_cast<const KT*>(P.k_cache);
-      wave_keys<OpM, KT, D>(reinterpret_cast<const KT*>(P.k_cache),
-                            reinterpret_cast<const KT*>(P.v_cache),
-                            reinterpret_cast<const KT*>(P.k_cache), dv, rows, sr.n_keys, qop,
-                            P.scale_log2, area + wave * SplitLds<D>::kVTileBytes, m_run, l_run, acc);
+      main_cache_keys<QT, KT, D>(P, qrow, q0row, hv, qraw, c, row_at, sr.n_keys,
+                                 area + wave * SplitLds<D>::kVTileBytes, m_run, l_run, acc);
     } else if constexpr (sizeof(AT) == 2) {
       typename OpVec<OpA>::v8 qop[2][D / 32];
 #pragma unroll
@@ -685,71 +786,17 @@ void split_attn_kernel(SplitParams P) {
       wave_keys<OpA, AT, D>(reinterpret_cast<const AT*>(P.aux_k),
                             reinterpret_cast<const AT*>(P.aux_v),
                             reinterpret_cast<const AT*>(q0row), reinterpret_cast<const AT*>(q0row),
-                            rows, sr.n_keys, qop,
+                            row_at, sr.n_keys, qop,
                             P.scale_log2, area + wave * SplitLds<D>::kVTileBytes, m_run, l_run, acc);
     }
   }
   __syncthreads();
 
-  // ---- 4. merge the four wave states (head lam, dims 16m + 4grp + i) ----
-  // Rows of the accumulator area are padded by 4 floats so the 16-byte stores of the 16
-  // heads of a lane group fall in different banks; the merge factors of each (wave, head)
-  // are computed once, by 16 threads.
-  constexpr int CR = SplitLds<D>::kCombineRow;
-  float* cm = reinterpret_cast<float*>(area);              // [wave][16] m
-  float* cl = cm + kWaves * 16;                           // [wave][16] l
-  float* cf = cl + kWaves * 16;                           // [wave][16] merge factor
-  float* cML = cf + kWaves * 16;                          // [16] (M, L)
-  float* ca = cML + kWaves * 16;                          // [wave][16][CR] acc
-  if (grp == 0) { cm[wave * 16 + lam] = m_run; cl[wave * 16 + lam] = l_run; }
-#pragma unroll
-  for (int m = 0; m < D / 16; ++m)
-    *reinterpret_cast<f32x4*>(ca + (wave * 16 + lam) * CR + 16 * m + 4 * grp) = acc[m];
-  __syncthreads();
-  if (tid < 16) {
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + tid]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = M != kNegInf ? exp2_safe(cm[w * 16 + tid] - M) : 0.f;
-      cf[w * 16 + tid] = f;
-      L += cl[w * 16 + tid] * f;
-    }
-    cML[2 * tid] = M;
-    cML[2 * tid + 1] = L;
-  }
-  __syncthreads();
-
+  // ---- 4. merge the four wave states and store ----
   const bool single = P.n_splits == 1;
-  const int64_t so = (int64_t)split * P.T * P.H_q;
-  for (int e = tid; e < 16 * D; e += kThreads) {
-    const int h = e / D, d = e - h * D;
-    if (h >= nh) continue;
-    const float M = cML[2 * h], L = cML[2 * h + 1];
-    float A = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) A += ca[(w * 16 + h) * CR + d] * cf[w * 16 + h];
-      if (use_scale) A *= P.value_scale[c * D + d] * kUnit;
-    }
-    const int head = h0 + h;
-    const int64_t o = ((int64_t)r * P.H_q + head) * D + d;
-    if (single) {
-      float res = 0.f;
-      if (M != kNegInf) {
-        const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
-        const float M2 = fmaxf(M, sg);
-        const float f = exp2_safe(M - M2);
-        res = A * f / (L * f + exp2_safe(sg - M2));
-      }
-      reinterpret_cast<QT*>(P.out)[o] = from_f32<QT>(res);
-    } else {
-      P.ws_acc[so * D + o] = A;
-      if (d == 0) P.ws_ml[so + (int64_t)r * P.H_q + head] = make_float2(M, L);
-    }
-  }
+  const int64_t so = (int64_t)split * P.T * P.H_q + (int64_t)r * P.H_q + h0;
+  combine_and_store<QT, D>(P, area, m_run, l_run, acc, nh, r, c, h0, use_scale, kUnit, single,
+                           single ? nullptr : P.ws_acc + so * D, single ? nullptr : P.ws_ml + so);
   // fused step: the lengths, written last so that nothing of it is live in the key loop
   if (kStep && blockIdx.x == 0) step_lengths(P, step_bad, wave_flags);
 }

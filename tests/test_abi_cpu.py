@@ -233,10 +233,10 @@ def test_noalloc_decode_step_argument_errors(lib):
     assert call(a23=96) == -4
     assert call(a2=0) == -2
     assert call(a6=MIS) == -2
-    # 200 rows of H 64/8 with a 65536-key bound: about 105 MB of partials
-    ws = lib.attention_workspace_bytes(0, 1, 200, 200, 1, 65536, 0, -1, 64, 8, 64)
+    # 255 requests of 8 rows of H 64/8 with a 65536-key bound: about 1 GB of partials
+    ws = lib.attention_workspace_bytes(0, 1, 255, 2040, 8, 65536, 0, -1, 64, 8, 64)
     assert ws > 16 << 20
-    assert call(a2=200, a3=200, a20=65536, a21=64, a22=8) == -5
+    assert call(a2=255, a3=2040, a19=8, a20=65536, a21=64, a22=8) == -5
 
 
 def test_topk_argument_errors(lib):

@@ -66,9 +66,9 @@ def test_noalloc_step_matches_the_workspace_step_twice():
 
 
 def test_noalloc_rejects_partials_beyond_the_array():
-    # 200 decode rows of 64 heads with a key bound of 65536 plan 32 splits: about 105 MB of
-    # partials (the check is on the host bounds, before any launch)
-    case = synth.paged_case(903, kv_lens=[10] * 200, q_lens=[1] * 200, H_q=64, H_kv=8, D=64,
+    # 255 requests of 8 rows of 64 heads with a key bound of 65536: about 1 GB of partials
+    # (the check is on the host bounds, before any launch)
+    case = synth.paged_case(903, kv_lens=[10] * 255, q_lens=[8] * 255, H_q=64, H_kv=8, D=64,
                             dtype=synth.F16, sinks=True, max_seqlen_k=65536)
     need = sta.attention_workspace_bytes(sta.KIND_PAGED, case.dtype, case.B, case.T,
                                          case.max_seqlen_q, case.max_seqlen_k, 0, -1, case.H_q,
