@@ -300,6 +300,14 @@ SPATTN_API int paged_attention_fwd(const void* q, int dtype, const void* k_cache
  *   writes must not be read by another request as one of its past keys (shared prefix
  *   blocks hold past keys only).  Malformed metadata: SPATTN_STATUS_BAD_CU, seqlens_q /
  *   seqlens_k as prepare_seqlens writes them, nothing appended, every out row zero.
+ *   committed_length [B] (optional, may be NULL): the caller's cursor, as for
+ *   kv_cache_append ([I8] Key Changes: optional committed_length; review: a cursor
+ *   mismatch must not be followed by a cache update).  A request with rows whose
+ *   committed_length[b] differs from past_seqlens[b] raises SPATTN_STATUS_CURSOR and none
+ *   of its keys is written; its rows are still attended over the unchanged cache.  With it
+ *   the step equals prepare_and_append(..., committed_length) followed by
+ *   paged_attention_fwd, bit for bit, so a graph replayed with stale lengths cannot
+ *   overwrite live slots when the caller passes its cursor.
  *   Supported: dtype F16 / BF16 with a cache of the same dtype, INT8 or FP8; B <= 255;
  *   max_seqlen_q <= 8 (the split-K path; longer query blocks take the prefill kernel).
  *   Other arguments that the separate calls accept return SPATTN_ERR_UNSUPPORTED and
@@ -313,7 +321,7 @@ SPATTN_API int paged_decode_step(const int32_t* cu_seqlens_q, const int32_t* pas
                       const float* key_scale, const float* value_scale, int max_seqlen_q,
                       int max_seqlen_k, int H_q, int H_kv, int D, float scale, int local_window,
                       const float* sinks, void* out, void* workspace, size_t workspace_bytes,
-                      int32_t* status, void* stream);
+                      const int32_t* committed_length, int32_t* status, void* stream);
 
 /*
  * paged_decode_step_noalloc - paged_decode_step for callers that cannot allocate device
@@ -340,7 +348,8 @@ SPATTN_API int paged_decode_step_noalloc(const int32_t* cu_seqlens_q, const int3
                       int max_blocks_per_seq, int block_size, int num_blocks,
                       const float* key_scale, const float* value_scale, int max_seqlen_q,
                       int max_seqlen_k, int H_q, int H_kv, int D, float scale, int local_window,
-                      const float* sinks, void* out, int32_t* status, void* stream);
+                      const float* sinks, void* out, const int32_t* committed_length,
+                      int32_t* status, void* stream);
 
 /*
  * sparse_attention_fwd - attention over selected cache rows ([DSA] Description: selected

@@ -265,8 +265,11 @@ def paged_decode_step(cu_seqlens_q: torch.Tensor, past_seqlens: torch.Tensor, T:
                       value_scale: Optional[torch.Tensor] = None, scale: float = 0.0,
                       local_window: int = -1, sinks: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
+                      committed_length: Optional[torch.Tensor] = None,
                       status: Optional[torch.Tensor] = None) -> None:
-    """prepare_seqlens + kv_cache_append + paged_attention_fwd of a decode step in one call."""
+    """prepare_seqlens + kv_cache_append + paged_attention_fwd of a decode step in one call.
+    With `committed_length` ([B] int32), a request whose cursor disagrees with its past
+    length is flagged (STATUS_CURSOR) and appends nothing."""
     B = int(past_seqlens.shape[0])
     _, H_q, D = (int(x) for x in q.shape)
     H_kv = int(k_cache.shape[1])
@@ -282,8 +285,8 @@ def paged_decode_step(cu_seqlens_q: torch.Tensor, past_seqlens: torch.Tensor, T:
         _ptr(v_cache, "v_cache"), _dt(k_cache), _i32(block_table, "block_table"), mbps, bs, nb,
         _ptr(key_scale, "key_scale"), _ptr(value_scale, "value_scale"), int(max_seqlen_q),
         int(max_seqlen_k), H_q, H_kv, D, float(scale), int(local_window), _ptr(sinks, "sinks"),
-        _ptr(out, "out"), _ptr(ws, "workspace"), ws_bytes, _i32(status, "status"),
-        _stream(cu_seqlens_q)))
+        _ptr(out, "out"), _ptr(ws, "workspace"), ws_bytes,
+        _i32(committed_length, "committed_length"), _i32(status, "status"), _stream(cu_seqlens_q)))
 
 
 def paged_decode_step_noalloc(cu_seqlens_q: torch.Tensor, past_seqlens: torch.Tensor, T: int,
@@ -294,6 +297,7 @@ def paged_decode_step_noalloc(cu_seqlens_q: torch.Tensor, past_seqlens: torch.Te
                               key_scale: Optional[torch.Tensor] = None,
                               value_scale: Optional[torch.Tensor] = None, scale: float = 0.0,
                               local_window: int = -1, sinks: Optional[torch.Tensor] = None,
+                              committed_length: Optional[torch.Tensor] = None,
                               status: Optional[torch.Tensor] = None) -> None:
     """paged_decode_step with its split-K partials in the library's static device array
     (no allocation by the call or by this binding)."""
@@ -309,7 +313,8 @@ def paged_decode_step_noalloc(cu_seqlens_q: torch.Tensor, past_seqlens: torch.Te
         _ptr(v_cache, "v_cache"), _dt(k_cache), _i32(block_table, "block_table"), mbps, bs, nb,
         _ptr(key_scale, "key_scale"), _ptr(value_scale, "value_scale"), int(max_seqlen_q),
         int(max_seqlen_k), H_q, H_kv, D, float(scale), int(local_window), _ptr(sinks, "sinks"),
-        _ptr(out, "out"), _i32(status, "status"), _stream(cu_seqlens_q)))
+        _ptr(out, "out"), _i32(committed_length, "committed_length"), _i32(status, "status"),
+        _stream(cu_seqlens_q)))
 
 
 def sparse_attention_fwd(q: torch.Tensor, mode: int, k_cache: torch.Tensor, v_cache: torch.Tensor,

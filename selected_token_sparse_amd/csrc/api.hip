@@ -97,8 +97,8 @@ static int decode_step_impl(const int32_t* cu_seqlens_q, const int32_t* past_seq
                       int num_blocks, const float* key_scale, const float* value_scale,
                       int max_seqlen_q, int max_seqlen_k, int H_q, int H_kv, int D, float scale,
                       int local_window, const float* sinks, void* out, void* workspace,
-                      size_t workspace_bytes, int32_t* status, void* stream,
-                      bool static_scratch) {
+                      size_t workspace_bytes, const int32_t* committed_length, int32_t* status,
+                      void* stream, bool static_scratch) {
   if (dtype != SPATTN_F16 && dtype != SPATTN_BF16) return float_dtype(dtype) ? SPATTN_ERR_UNSUPPORTED : SPATTN_ERR_DTYPE;
   int rc = check_heads(H_q, H_kv, D);
   if (rc != SPATTN_OK) return rc;
@@ -131,6 +131,7 @@ static int decode_step_impl(const int32_t* cu_seqlens_q, const int32_t* past_seq
   a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
   a.past = past_seqlens; a.k_new = k_new; a.v_new = v_new;
   a.seqlens_q_out = seqlens_q; a.seqlens_k_out = seqlens_k;
+  a.committed = committed_length;
   const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, max_seqlen_k, 0,
                                          a.window, H_q, H_kv, D);
   if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
@@ -336,12 +337,13 @@ int paged_decode_step(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, 
                       int num_blocks, const float* key_scale, const float* value_scale,
                       int max_seqlen_q, int max_seqlen_k, int H_q, int H_kv, int D, float scale,
                       int local_window, const float* sinks, void* out, void* workspace,
-                      size_t workspace_bytes, int32_t* status, void* stream) {
+                      size_t workspace_bytes, const int32_t* committed_length, int32_t* status,
+                      void* stream) {
   return decode_step_impl(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k, q, k_new, v_new,
                           dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq,
                           block_size, num_blocks, key_scale, value_scale, max_seqlen_q,
                           max_seqlen_k, H_q, H_kv, D, scale, local_window, sinks, out, workspace,
-                          workspace_bytes, status, stream, false);
+                          workspace_bytes, committed_length, status, stream, false);
 }
 
 int paged_decode_step_noalloc(const int32_t* cu_seqlens_q, const int32_t* past_seqlens, int B,
@@ -351,13 +353,13 @@ int paged_decode_step_noalloc(const int32_t* cu_seqlens_q, const int32_t* past_s
                               int max_blocks_per_seq, int block_size, int num_blocks,
                               const float* key_scale, const float* value_scale, int max_seqlen_q,
                               int max_seqlen_k, int H_q, int H_kv, int D, float scale,
-                              int local_window, const float* sinks, void* out, int32_t* status,
-                              void* stream) {
+                              int local_window, const float* sinks, void* out,
+                              const int32_t* committed_length, int32_t* status, void* stream) {
   return decode_step_impl(cu_seqlens_q, past_seqlens, B, T, seqlens_q, seqlens_k, q, k_new, v_new,
                           dtype, k_cache, v_cache, cache_dtype, block_table, max_blocks_per_seq,
                           block_size, num_blocks, key_scale, value_scale, max_seqlen_q,
                           max_seqlen_k, H_q, H_kv, D, scale, local_window, sinks, out, nullptr, 0,
-                          status, stream, true);
+                          committed_length, status, stream, true);
 }
 
 int sparse_attention_fwd(const void* q, int dtype, int mode, const void* k_cache,

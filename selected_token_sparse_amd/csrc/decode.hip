@@ -109,13 +109,16 @@ struct SplitParams {
   const void* v_new;
   int32_t* seqlens_q_out;   // [B], written by workgroup 0
   int32_t* seqlens_k_out;
+  // [B] or nullptr: the caller's cursor; a request whose past length differs appends nothing
+  const int32_t* committed;
 };
 
-// OR of the per-lane status flags across the wave (uniform result).
+// OR of the per-lane status flags across the wave (uniform result; every SPATTN_STATUS_*
+// bit, 0 .. 9).
 __device__ __forceinline__ int wave_or_flags(int flags) {
   int wave_flags = 0;
 #pragma unroll
-  for (int bit = 0; bit < 8; ++bit)
+  for (int bit = 0; bit < 10; ++bit)
     if (__ballot(flags & (1 << bit))) wave_flags |= 1 << bit;
   return wave_flags;
 }
@@ -443,8 +446,9 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
 // Per-request metadata of a workgroup, staged in LDS (`meta`, 2 B + 1 ints) when `to_lds`.
 // Fused decode step (kStep), one load round and one barrier: meta[0..B] = cu,
 // meta[B+1+b] = past[b] + q_len_b - 1 (seqlens_k, as prepare_seqlens derives it for
-// well-formed metadata); returns whether the metadata is malformed (B + 1 <= kThreads).
-// Otherwise cu / seqlens_k are copied, or read from global memory when !to_lds.
+// well-formed metadata), and with a cursor, meta[2B+1+b] = 1 when committed[b] differs
+// from past[b] (3 B + 1 ints); returns whether the metadata is malformed (B + 1 <=
+// kThreads).  Otherwise cu / seqlens_k are copied, or read from global memory when !to_lds.
 template <bool kStep>
 __device__ __forceinline__ bool stage_metadata(const SplitParams& P, int32_t* meta, bool to_lds,
                                                const int32_t*& cu, const int32_t*& skl) {
@@ -456,10 +460,14 @@ __device__ __forceinline__ bool stage_metadata(const SplitParams& P, int32_t* me
     const int cv = tid < n ? P.cu[tid] : 0;
     const int cn = tid < P.B ? P.cu[tid + 1] : 0;
     const int pb = tid < P.B ? P.past[tid] : 0;
+    const int cm = tid < P.B && P.committed != nullptr ? P.committed[tid] : pb;
     const bool bad = (tid < P.B && (cn < cv || pb < 0)) ||
                      (tid == 0 && (cv != 0 || P.cu[P.B] != P.T));
     if (tid < n) meta[tid] = cv;
-    if (tid < P.B) meta[n + tid] = pb + (cn - cv) - 1;
+    if (tid < P.B) {
+      meta[n + tid] = pb + (cn - cv) - 1;
+      if (P.committed != nullptr) meta[n + P.B + tid] = cm != pb ? 1 : 0;
+    }
     const bool step_bad = __syncthreads_or(bad) != 0;
     cu = meta;
     skl = meta + n;
@@ -731,8 +739,16 @@ void split_attn_kernel(SplitParams P) {
   } else {
     ri = resolve_row(cu, skl, P.B, r, P.max_q, P.max_k, flags);
   }
+  // fused step with a cursor: requests whose cursor disagrees append nothing (their rows
+  // are still attended over the unchanged cache); workgroup 0 flags them
+  auto cursor_bad = [&](int b) { return kStep && P.committed != nullptr && meta[2 * P.B + 1 + b] != 0; };
+  if (kStep && !step_bad && P.committed != nullptr && blockIdx.x == 0) {
+    // (a uniform branch: every thread of workgroup 0 holds the flag)
+    if (__syncthreads_or(tid < P.B && cu[tid + 1] > cu[tid] && cursor_bad(tid)))
+      flags |= SPATTN_STATUS_CURSOR;
+  }
   if (kStep && !step_bad && ri.b < 0 && ri.q_len > 0 &&
-      split == 0 && ht == 0) {
+      split == 0 && ht == 0 && !cursor_bad(find_request(cu, P.B, r))) {
     // a fused step's row beyond the host bounds reads nothing, but its key is still appended
     const int b = find_request(cu, P.B, r);
     const int first_new = ri.kv_len - ri.q_len, j = first_new + (r - cu[b]);
@@ -752,7 +768,7 @@ void split_attn_kernel(SplitParams P) {
     return;
   }
   for (int v = tid; v < sr.n_keys; v += kThreads) rows[v] = split_key_row(P, sr, ri, c, v, flags);
-  if (kStep && ri.b >= 0) {
+  if (kStep && ri.b >= 0 && !cursor_bad(ri.b)) {
     // fused step: the new keys of this split's range, written before the barrier below
     const int first_new = ri.kv_len - ri.q_len, k0 = sr.lo + sr.v0;
     step_write_keys<QT, KT, D>(P, ri.b, c, max(k0, first_new), k0 + sr.n_keys, first_new,
@@ -1046,7 +1062,7 @@ SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_
 template <int KIND, typename QT, typename KT, typename AT, int D>
 static void launch_split_typed(const SplitParams& P, hipStream_t stream) {
   const int blocks = P.n_splits * P.T * P.H_kv * P.head_tiles;
-  const size_t lds = split_lds_bytes<D>(P.chunk, P.meta_lds ? 2 * (P.B + 1) : 0);
+  const size_t lds = split_lds_bytes<D>(P.chunk, P.meta_lds || P.past != nullptr ? 3 * P.B + 1 : 0);
   // the fused decode step is its own instantiation, so the other kernels carry none of it
   if constexpr (KIND == SPATTN_KIND_PAGED) {
     if (P.past != nullptr) {
@@ -1118,7 +1134,7 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   P.chunk = plan.chunk; P.n_main = plan.n_main; P.n_splits = plan.n_splits;
   P.meta_lds = a.B + 1 <= kMetaLdsMax ? 1 : 0;
   P.scale_log2 = a.scale * kLog2e;
-  P.past = a.past; P.k_new = a.k_new; P.v_new = a.v_new;
+  P.past = a.past; P.k_new = a.k_new; P.v_new = a.v_new; P.committed = a.committed;
   P.seqlens_q_out = a.seqlens_q_out; P.seqlens_k_out = a.seqlens_k_out;
   const bool direct = plan.n_splits == 1;
   P.ws_acc = nullptr; P.ws_ml = nullptr;

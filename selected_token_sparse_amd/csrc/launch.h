@@ -56,6 +56,7 @@ struct AttnArgs {
   const void* v_new;
   int32_t* seqlens_q_out;
   int32_t* seqlens_k_out;
+  const int32_t* committed;   // fused decode step only: the caller's cursor [B] or nullptr
 };
 
 // Largest B of the fused decode step (its boundaries are staged one per thread).

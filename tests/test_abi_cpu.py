@@ -182,9 +182,10 @@ def test_prepare_and_append_argument_errors(lib):
 def test_decode_step_argument_errors(lib):
     f = lib.paged_decode_step
     # cu, past, B, T, sq, sk, q, k_new, v_new, dtype, kc, vc, cache_dt, bt, mbps, bs, nb, ks,
-    # vs, max_q, max_k, H_q, H_kv, D, scale, win, sinks, out, ws, ws_bytes, status, stream
+    # vs, max_q, max_k, H_q, H_kv, D, scale, win, sinks, out, ws, ws_bytes, committed, status,
+    # stream
     base = [FAKE, FAKE, 2, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, FAKE, 4, 16, 8,
-            None, None, 1, 64, 4, 2, 64, 0.0, -1, None, FAKE, None, 0, None, None]
+            None, None, 1, 64, 4, 2, 64, 0.0, -1, None, FAKE, None, 0, None, None, None]
     def call(**kv):
         a = list(base)
         for i, v in kv.items():
@@ -217,7 +218,7 @@ def test_noalloc_decode_step_argument_errors(lib):
     f = lib.paged_decode_step_noalloc
     # paged_decode_step's arguments without workspace / workspace_bytes
     base = [FAKE, FAKE, 2, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, FAKE, 4, 16, 8,
-            None, None, 1, 64, 4, 2, 64, 0.0, -1, None, FAKE, None, None]
+            None, None, 1, 64, 4, 2, 64, 0.0, -1, None, FAKE, None, None, None]
     def call(**kv):
         a = list(base)
         for i, v in kv.items():

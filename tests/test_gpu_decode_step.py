@@ -33,7 +33,7 @@ def _ws(case, T=None):
     return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
 
 
-def _run(case, t, mode, cu_t, past_t, ws):
+def _run(case, t, mode, cu_t, past_t, ws, committed=None):
     """One step on fresh copies of the caches; returns every output as host tensors."""
     B, T = int(past_t.shape[0]), case.T
     kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
@@ -47,11 +47,13 @@ def _run(case, t, mode, cu_t, past_t, ws):
               sinks=t["sinks"], workspace=ws, status=st)
     if mode == "step":
         sta.paged_decode_step(cu_t, past_t, T, sq, sk, t["q"], t["k_new"], t["v_new"], kc, vc,
-                              case.max_seqlen_q, case.max_seqlen_k, out, **kw)
+                              case.max_seqlen_q, case.max_seqlen_k, out,
+                              committed_length=committed, **kw)
     else:
         sta.prepare_and_append(cu_t, past_t, T, sq, sk, t["k_new"], t["v_new"], kc, vc,
                                t["block_table"], key_scale=t["key_scale"],
-                               value_scale=t["value_scale"], status=st)
+                               value_scale=t["value_scale"], committed_length=committed,
+                               status=st)
         sta.paged_attention_fwd(t["q"], kc, vc, cu_t, sk, case.max_seqlen_q, case.max_seqlen_k,
                                 out, **kw)
     torch.cuda.synchronize()
@@ -59,14 +61,15 @@ def _run(case, t, mode, cu_t, past_t, ws):
                 st=int(st.item()))
 
 
-def _step_vs_calls(case, cu=None, past=None):
+def _step_vs_calls(case, cu=None, past=None, committed=None):
     """The step and the two calls on the same inputs: identical bit for bit."""
     t = case_tensors(case)
     cu_t = tensor(np.asarray(case.cu_seqlens_q if cu is None else cu, dtype=np.int32))
     past_t = tensor(np.asarray(case.past_seqlens if past is None else past, dtype=np.int32))
+    cm_t = None if committed is None else tensor(np.asarray(committed, dtype=np.int32))
     ws = _ws(case)
-    a = _run(case, t, "step", cu_t, past_t, ws)
-    b = _run(case, t, "calls", cu_t, past_t, ws)
+    a = _run(case, t, "step", cu_t, past_t, ws, cm_t)
+    b = _run(case, t, "calls", cu_t, past_t, ws, cm_t)
     for name in ("sq", "sk", "k", "v"):
         assert torch.equal(a[name], b[name]), name
     assert torch.equal(_bits(a["out"]).cpu(), _bits(b["out"]).cpu()), "out"
@@ -137,6 +140,40 @@ def test_rows_beyond_the_bounds_still_append():
     got = _step_vs_calls(case)
     assert got["st"] & sta.STATUS_Q_BOUND and got["st"] & sta.STATUS_K_BOUND
     _against_oracle(case, got, "step_bounds")
+
+
+@pytest.mark.parametrize("cache_dtype", [synth.F16, synth.I8])
+def test_cursor_mismatch_appends_nothing(cache_dtype):
+    """committed_length on the fused step: requests whose cursor disagrees with their past
+    length (including one beyond the key bound) flag STATUS_CURSOR and write no key; their
+    rows are attended over the unchanged cache; the rest append normally.  Bit for bit the
+    two calls with the same cursor, and the oracle's append with the cursor, then attention."""
+    print("decode step cursor", cache_dtype, flush=True)
+    case = synth.paged_case(311, kv_lens=[700, 40, 2600, 1, 90, 0], q_lens=[1, 1, 1, 1, 2, 0],
+                            H_q=16, H_kv=2, D=64, dtype=synth.F16, cache_dtype=cache_dtype,
+                            sinks=True, poison=cache_dtype == synth.F16, max_seqlen_q=2,
+                            max_seqlen_k=2000)
+    committed = case.past_seqlens.copy()
+    committed[1] += 1            # stale cursor
+    committed[2] -= 3            # beyond the key bound as well
+    committed[4] = 0
+    committed[5] = 77            # no rows: not checked
+    got = _step_vs_calls(case, committed=committed)
+    assert got["st"] & sta.STATUS_CURSOR
+    _, sk, _, _, st0 = oracle.prepare_seqlens(case.cu_seqlens_q, case.past_seqlens, case.T)
+    kc, vc, st1 = oracle.kv_cache_append(case.k_new, case.v_new, case.cu_seqlens_q, sk,
+                                         case.k_cache, case.v_cache, case.block_table,
+                                         case.block_size, case.key_scale, case.value_scale,
+                                         committed_length=committed)
+    assert np.array_equal(got["k"].numpy().view(kc.dtype).reshape(kc.shape), kc, equal_nan=True)
+    ref, st2 = oracle.paged_attention(case.q, kc, vc, case.cu_seqlens_q, sk, H_kv=case.H_kv,
+                                      block_table=case.block_table, block_size=case.block_size,
+                                      key_scale=case.key_scale, value_scale=case.value_scale,
+                                      max_seqlen_q=case.max_seqlen_q,
+                                      max_seqlen_k=case.max_seqlen_k, scale=case.scale,
+                                      sinks=case.sinks)
+    assert_close(got["out"], ref, case.dtype, f"step_cursor_{cache_dtype}")
+    assert got["st"] == st0 | st1 | st2, (got["st"], st0 | st1 | st2)
 
 
 def test_missing_slots_flagged():
