@@ -106,6 +106,100 @@ __device__ __forceinline__ void pf_wait_vm() {
 }
 __device__ __forceinline__ void pf_wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// One wave's step over one 32-key tile staged in LDS, for its 32 query rows (lane l32 =
+// row, lane half h):
+//   S^T[32 keys x 32 rows] = K Q^T  (v_mfma_f32_32x32x16, D/16 steps; with kQlo a second
+//                                    product with the low half of a folded query)
+//   masks(s): the caller's masks on the lane's 16 scores (keys 8*(i/4) + 4*h + i%4)
+//   online softmax per row in the log2 domain with a lazy rescale (c_scale = |scale| log2 e
+//   applied in the exponent; the running maximum is on raw scores)
+//   O^T[D x 32 rows] += V^T P^T     (V^T from LDS via ds_read_b64_tr_b16)
+// kchunk(kk, c) / vchunk(kk, c): byte offset of 16-byte chunk c of key kk in the K / V tile.
+template <typename OpT, int D, bool kQlo, typename KChunk, typename VChunk, typename Masks>
+__device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsigned char* vl,
+                                             KChunk k_chunk, VChunk v_chunk,
+                                             const typename Op32<OpT>::v8 (&qop)[D / 16],
+                                             const typename Op32<OpT>::v8 (&qlo)[kQlo ? D / 16 : 1],
+                                             Masks masks, float c_scale, float& m_run,
+                                             float& l_run, f32x16 (&acc)[D / 32]) {
+  typedef typename Op32<OpT>::v8 V8;
+  typedef typename Op32<OpT>::v4 V4;
+  constexpr int KC = D / 16;
+  constexpr int MT = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  // S^T: A = K[key l32][16kc + 8h ..], B = qop
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    V8 a = *reinterpret_cast<const V8*>(kl + k_chunk(l32, 2 * kc + h));
+    s = mfma32(a, qop[kc], s);
+    if constexpr (kQlo) s = mfma32(a, qlo[kc], s);
+  }
+  masks(s);
+  float mt = s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
+  mt = half_swap_max(mt);                    // the row's other lane half
+  const float m_new = fmaxf(m_run, mt);      // raw-score maximum of the row
+  // the reference maximum moves only when some row's maximum outgrows it by more than
+  // kLazyRescaleLog2 (in the exponent); a row's first visible key always moves it
+  if (__ballot((m_new - m_run) * c_scale > kLazyRescaleLog2)) {
+    // rows whose max did not move keep alpha = 1 (including rows that have seen no key
+    // yet: -inf - -inf must not reach the exponent); a row seeing its first key gets
+    // alpha = 0 on acc = 0, l = 0
+    const float alpha = m_new == m_run ? 1.f : exp2_safe((m_run - m_new) * c_scale);
+    l_run *= alpha;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] *= alpha;
+    m_run = m_new;
+  }
+  // p = exp2(c * (s - m)) <= 2^8; a row with no visible key yet keeps p = 0
+  const float nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
+  // bf16 operands keep 8 significant bits: the weights are carried as hi + lo (hi = p
+  // rounded, lo = its rounding error rounded) and PV takes one product with each, so
+  // the weights keep about 16 bits, as f16 operands keep 11
+  constexpr bool kSplitP = std::is_same<OpT, bf16>::value;
+  V8 pop[2];
+  V8 plo[kSplitP ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p = exp2_safe(__builtin_fmaf(s[i], c_scale, nm));
+    pop[i >> 3][i & 7] = (OpT)p;
+    if constexpr (kSplitP) plo[i >> 3][i & 7] = (OpT)(p - (float)pop[i >> 3][i & 7]);
+  }
+  // this lane's part of the row sum, over the rounded weights the PV product uses, two
+  // per instruction (products with 1 are exact; the sum is fp32)
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    l_run = dot2_ones(pop[i >> 3][i & 7], pop[i >> 3][(i & 7) + 1], l_run);
+    if constexpr (kSplitP) l_run = dot2_ones(plo[i >> 3][i & 7], plo[i >> 3][(i & 7) + 1], l_run);
+  }
+  {
+    const int grp = lane >> 4, lam = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        // key vk, dims d .. d + 3 (8 bytes inside chunk d / 8), and key vk + 8
+        const int vk = 16 * ks + 4 * h + (lam >> 2);
+        const int d = 32 * m + 16 * (grp & 1) + 4 * (lam & 3);
+        const OpT* a0 = reinterpret_cast<const OpT*>(vl + v_chunk(vk, d >> 3) + (d & 7) * 2);
+        const OpT* a1 = reinterpret_cast<const OpT*>(vl + v_chunk(vk + 8, d >> 3) + (d & 7) * 2);
+        s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a0));
+        s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a1));
+        V4 x0 = __builtin_bit_cast(V4, r0);
+        V4 x1 = __builtin_bit_cast(V4, r1);
+        V8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        acc[m] = mfma32(av, pop[ks], acc[m]);
+        if constexpr (kSplitP) acc[m] = mfma32(av, plo[ks], acc[m]);
+      }
+  }
+}
+
 // 4 waves per SIMD at D = 64 (128 registers: both tile buffers, the accumulators and the
 // query operand fit), 3 at D = 64 with a quantised cache (the query's low operand needs
 // 16 more registers), 2 at D = 128.
@@ -455,94 +549,29 @@ void prefill_kernel(PrefillParams P) {
       const OpT* kl = reinterpret_cast<const OpT*>(base);
       const OpT* vl = reinterpret_cast<const OpT*>(base + L::kKBytes);
       const int32_t* vb = reinterpret_cast<const int32_t*>(base + L::kKBytes + L::kVBytes);
-      // S^T: A = K[key l32][16kc + 8h ..], B = qop
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        V8 a = *reinterpret_cast<const V8*>(reinterpret_cast<const unsigned char*>(kl) +
-                                            k_chunk(l32, 2 * kc + h));
-        s = mfma32(a, qop[kc], s);
-        if constexpr (kI8) s = mfma32(a, qlo[kc], s);
-      }
       // lane holds keys 8*(i/4) + 4*h + i%4 of row l32.  Masks only on tiles some row of the
       // wave does not fully see (the diagonal, the window edge, missing keys).
       const i32x4 wflags = *reinterpret_cast<const i32x4*>(vb + kPfTile);
       const bool tile_ok = (wflags[0] & wflags[1] & wflags[2] & wflags[3]) != 0;
       const bool full = tile_ok && kt + kPfTile - 1 <= w_p_first &&
                         (P.window <= 0 || kt >= w_p_last - P.window + 1);
-      if (!full) {
+      auto masks = [&](f32x16& s) {
+        if (!full) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int k0 = 8 * g4 + 4 * h;
-          const i32x4 ok = *reinterpret_cast<const i32x4*>(vb + k0);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int k0 = 8 * g4 + 4 * h;
+            const i32x4 ok = *reinterpret_cast<const i32x4*>(vb + k0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = kt + k0 + e;
-            if (!(ok[e] && j <= my_p && j >= my_lo)) s[4 * g4 + e] = kNegInf;
+            for (int e = 0; e < 4; ++e) {
+              const int j = kt + k0 + e;
+              if (!(ok[e] && j <= my_p && j >= my_lo)) s[4 * g4 + e] = kNegInf;
+            }
           }
         }
-      }
-      float mt = s[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
-      mt = half_swap_max(mt);                    // the row's other lane half
-      const float m_new = fmaxf(m_run, mt);      // raw-score maximum of the row
-      // the reference maximum moves only when some row's maximum outgrows it by more than
-      // kLazyRescaleLog2 (in the exponent); a row's first visible key always moves it
-      if (__ballot((m_new - m_run) * c_scale > kLazyRescaleLog2)) {
-        // rows whose max did not move keep alpha = 1 (including rows that have seen no key
-        // yet: -inf - -inf must not reach the exponent); a row seeing its first key gets
-        // alpha = 0 on acc = 0, l = 0
-        const float alpha = m_new == m_run ? 1.f : exp2_safe((m_run - m_new) * c_scale);
-        l_run *= alpha;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] *= alpha;
-        m_run = m_new;
-      }
-      // p = exp2(c * (s - m)) <= 2^8; a row with no visible key yet keeps p = 0
-      const float nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
-      // bf16 operands keep 8 significant bits: the weights are carried as hi + lo (hi = p
-      // rounded, lo = its rounding error rounded) and PV takes one product with each, so
-      // the weights keep about 16 bits, as f16 operands keep 11
-      constexpr bool kSplitP = std::is_same<OpT, bf16>::value;
-      V8 pop[2];
-      V8 plo[kSplitP ? 2 : 1];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2_safe(__builtin_fmaf(s[i], c_scale, nm));
-        pop[i >> 3][i & 7] = (OpT)p;
-        if constexpr (kSplitP) plo[i >> 3][i & 7] = (OpT)(p - (float)pop[i >> 3][i & 7]);
-      }
-      // this lane's part of the row sum, over the rounded weights the PV product uses, two
-      // per instruction (products with 1 are exact; the sum is fp32)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        l_run = dot2_ones(pop[i >> 3][i & 7], pop[i >> 3][(i & 7) + 1], l_run);
-        if constexpr (kSplitP) l_run = dot2_ones(plo[i >> 3][i & 7], plo[i >> 3][(i & 7) + 1], l_run);
-      }
-      {
-        const int grp = lane >> 4, lam = lane & 15;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            // key vk, dims d .. d + 3 (8 bytes inside chunk d / 8), and key vk + 8
-            const int vk = 16 * ks + 4 * h + (lam >> 2);
-            const int d = 32 * m + 16 * (grp & 1) + 4 * (lam & 3);
-            const unsigned char* vlb = reinterpret_cast<const unsigned char*>(vl);
-            const OpT* a0 = reinterpret_cast<const OpT*>(vlb + v_chunk(vk, d >> 3) + (d & 7) * 2);
-            const OpT* a1 = reinterpret_cast<const OpT*>(vlb + v_chunk(vk + 8, d >> 3) + (d & 7) * 2);
-            s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(a0));
-            s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(a1));
-            V4 x0 = __builtin_bit_cast(V4, r0);
-            V4 x1 = __builtin_bit_cast(V4, r1);
-            V8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            acc[m] = mfma32(av, pop[ks], acc[m]);
-            if constexpr (kSplitP) acc[m] = mfma32(av, plo[ks], acc[m]);
-          }
-      }
+      };
+      pf_tile_math<OpT, D, kI8>(reinterpret_cast<const unsigned char*>(kl),
+                                reinterpret_cast<const unsigned char*>(vl), k_chunk, v_chunk, qop,
+                                qlo, masks, c_scale, m_run, l_run, acc);
     }
   };
 
@@ -637,6 +666,218 @@ void prefill_kernel(PrefillParams P) {
   if (wave_flags && lane == 0) raise_status(P.status, wave_flags);
 }
 
+// ---------------------------------------------------------------------------------------
+// Windowed prefill over 16-bit caches ("[WebGPU] Add PagedAttention metadata and GPT-OSS
+// support": local window; review finding Q3: the keys a query block needs are one window
+// plus the block).  Workgroup = one 32-row block of one request and one KV head, with every
+// query head of its group: the block's whole key span, max(0, p_first - W + 1) .. p_last
+// (at most 31 + W keys), goes into LDS by DMA once, behind one barrier.  Then each wave
+// takes the group's heads h = wave, wave + NW, ... and runs every tile of the span for the
+// 32 rows, with no further barrier.  K and V are read once per group of heads, and the
+// per-tile barrier of the streaming kernel is gone.
+// ---------------------------------------------------------------------------------------
+constexpr int kWinRows = 32;
+constexpr int kWinMax = 128;   // largest window this kernel takes
+
+template <int D>
+struct WinLds {
+  static constexpr int kMaxTiles = (kWinRows + kWinMax - 1 + kPfTile - 1) / kPfTile;
+  static constexpr int kTileBytes = kPfTile * D * 2;      // K (or V) of one tile
+  static constexpr int kVOff = kMaxTiles * kTileBytes;
+  static constexpr int kOkOff = 2 * kMaxTiles * kTileBytes;   // one byte per span key
+  static constexpr int kTotal = kOkOff + kMaxTiles * kPfTile;
+};
+
+template <typename QT, int D, int NW>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<QT, D>(), 8)))
+void prefill_window_kernel(PrefillParams P) {
+  typedef WinLds<D> L;
+  typedef typename Op32<QT>::v8 V8;
+  constexpr int KC = D / 16;
+  constexpr int MT = D / 32;
+  constexpr int CHK = D / 8;                        // 16-byte chunks per key row
+  constexpr int IPT = kPfTile * CHK / 64;           // DMA instructions per K (or V) tile
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint8_t* key_ok = smem + L::kOkOff;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  // (request, KV head) pair p runs on XCD p % 8, its row blocks in order, so the blocks
+  // whose spans overlap share that XCD's L2
+  int b, c, rb;
+  {
+    const int i = blockIdx.x;
+    const int x = i & 7, k = i >> 3;
+    const int pair = (k / P.n_rt) * 8 + x;
+    if (pair >= P.B * P.H_kv) return;
+    rb = k - (k / P.n_rt) * P.n_rt;
+    c = pair % P.H_kv;
+    b = pair / P.H_kv;
+  }
+
+  int flags = 0;
+  const int c0 = P.cu[b];
+  int q_len = P.cu[b + 1] - c0;
+  const int kv_len = P.seqlens_k[b] + 1;
+  bool dead = false;
+  if (q_len < 0 || c0 < 0 || c0 + q_len > P.T) { flags |= SPATTN_STATUS_BAD_CU; q_len = 0; }
+  else if (q_len > P.max_q) { flags |= SPATTN_STATUS_Q_BOUND; dead = true; }
+  else if (kv_len > P.max_k) { flags |= SPATTN_STATUS_K_BOUND; dead = true; }
+  else if (kv_len < q_len) flags |= SPATTN_STATUS_SHORT_KV;
+  auto raise = [&]() {
+    int wf = 0;
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit)
+      if (__ballot(flags & (1 << bit))) wf |= 1 << bit;
+    if (wf && lane == 0) raise_status(P.status, wf);
+  };
+  if (dead) {
+    // the request's rows are zero; rows past the host bound are covered by striding
+    for (int hh = wave; hh < P.group; hh += NW)
+      for (int i = rb * kWinRows + l32; i < q_len; i += P.n_rt * kWinRows) {
+        QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + i) * P.H_q + c * P.group + hh) * D;
+        for (int d = h; d < D; d += 2) o[d] = from_f32<QT>(0.f);
+      }
+    raise();
+    return;
+  }
+  const int row_base = rb * kWinRows;
+  if (row_base >= q_len) { raise(); return; }
+  const int rows = min(kWinRows, q_len - row_base);
+  const int pos0 = kv_len - q_len;
+  const int p_first = pos0 + row_base, p_last = p_first + rows - 1;
+  const int j_lo = max(0, p_first - P.window + 1);
+  const int j_hi = min(p_last, kv_len - 1);
+  const int n_keys = max(0, j_hi - j_lo + 1);
+  const int n_tiles = (n_keys + kPfTile - 1) / kPfTile;
+
+  // ---- the span's K and V into LDS: tile t holds keys j_lo + 32 t + kk, row kk with its
+  //      16-byte chunks XOR-swizzled by kk (as the streaming kernel's stages) ----
+  const QT* kcache = reinterpret_cast<const QT*>(P.k_cache);
+  const QT* vcache = reinterpret_cast<const QT*>(P.v_cache);
+  const QT* safe = reinterpret_cast<const QT*>(P.q) + ((int64_t)(c0 + row_base) * P.H_q + c * P.group) * D;
+  const bool paged = P.cd.block_table != nullptr;
+  const int bs = P.cd.block_size;
+  const int32_t* table = paged ? P.cd.block_table + (int64_t)b * P.cd.max_blocks : nullptr;
+  // the query operands of this wave's first head load under the span's DMA
+  const int my_row = row_base + l32;
+  const bool row_ok = my_row < q_len;
+  auto load_q = [&](int hh, V8 (&qop)[KC]) {
+    const QT* qr = reinterpret_cast<const QT*>(P.q) + ((int64_t)(c0 + my_row) * P.H_q + c * P.group + hh) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qop[kc] = row_ok ? __builtin_bit_cast(V8, load16(qr + kc * 16 + h * 8)) : V8{};
+  };
+  V8 qop[KC];
+  if (wave < P.group) load_q(wave, qop);
+  bool all_ok = true;
+  for (int q = wave; q < n_tiles * IPT; q += NW) {
+    const int t = q / IPT;
+    const int pos = (q - t * IPT) * 64 + lane;
+    const int kk = pos / CHK, slot = pos - kk * CHK;
+    const int col = (slot ^ pf_swizzle<D>(kk)) * 8;
+    const int j = j_lo + t * kPfTile + kk;
+    bool ok = j <= j_hi;
+    int64_t row = 0;
+    if (ok) {
+      if (paged) {
+        const int lb = P.cd.bs_shift >= 0 ? j >> P.cd.bs_shift : j / bs;
+        const int blk = lb < P.cd.max_blocks ? table[lb] : -1;
+        if (lb >= P.cd.max_blocks) flags |= SPATTN_STATUS_CAPACITY;
+        else if (blk < 0 || blk >= P.cd.num_blocks) flags |= SPATTN_STATUS_BAD_BLOCK;
+        ok = lb < P.cd.max_blocks && blk >= 0 && blk < P.cd.num_blocks;
+        row = (((int64_t)blk * P.cd.H_kv + c) * bs + (j - lb * bs));
+      } else {
+        ok = j < bs && b < P.cd.num_blocks;
+        if (!ok) flags |= SPATTN_STATUS_CAPACITY;
+        row = ((int64_t)b * P.cd.H_kv + c) * bs + j;
+      }
+    }
+    // a missing key reads a finite row (the block's first query row); its weight is 0
+    const QT* kp = ok ? kcache + row * D + col : safe + col;
+    const QT* vp = ok ? vcache + row * D + col : safe + col;
+    pf_dma16(kp, smem + t * L::kTileBytes + (q - t * IPT) * 1024);
+    pf_dma16(vp, smem + L::kVOff + t * L::kTileBytes + (q - t * IPT) * 1024);
+    if (slot == 0) key_ok[t * kPfTile + kk] = ok ? 1 : 0;
+    all_ok = all_ok && (ok || j > j_hi);
+  }
+  pf_wait_vm<0>();
+  const bool span_ok = __syncthreads_or(!all_ok) == 0;   // every key of the span exists
+
+  // ---- every head of this wave over the span ----
+  const float c_scale = fabsf(P.scale_log2);
+  const bool q_neg = P.scale_log2 < 0.f;
+  const int my_p = pos0 + my_row;
+  const int my_lo = max(0, my_p - P.window + 1);
+  // rows of the block: the tiles every row sees whole are those inside
+  // [lo(p_last), p_first]
+  const int full_lo = max(0, p_last - P.window + 1), full_hi = p_first;
+  auto k_chunk = [&](int kk, int ch) -> int { return kk * D * 2 + ((ch ^ pf_swizzle<D>(kk)) << 4); };
+  for (int hh = wave; hh < P.group; hh += NW) {
+    const int head = c * P.group + hh;
+    const V8 qlo[1] = {V8{}};
+    if (hh != wave) load_q(hh, qop);
+    if (q_neg) {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qop[kc] = -qop[kc];
+    }
+    f32x16 acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
+    float m_run = kNegInf, l_run = 0.f;
+    for (int t = 0; t < n_tiles; ++t) {
+      const int kt = j_lo + t * kPfTile;
+      const bool full = span_ok && kt >= full_lo && kt + kPfTile - 1 <= full_hi;
+      auto masks = [&](f32x16& s) {
+        if (full) return;
+        // key kt + k is visible to this lane's row when lo(p) <= kt + k <= p (k counted
+        // from the lane half's first key, 4 h) and it exists
+        const int lo_rel = my_lo - kt - 4 * h, hi_rel = my_p - kt - 4 * h;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int k = 8 * (i >> 2) + (i & 3);
+          s[i] = (k >= lo_rel && k <= hi_rel) ? s[i] : kNegInf;
+        }
+        if (!span_ok) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (!key_ok[t * kPfTile + 8 * (i >> 2) + 4 * h + (i & 3)]) s[i] = kNegInf;
+        }
+      };
+      pf_tile_math<QT, D, false>(smem + t * L::kTileBytes, smem + L::kVOff + t * L::kTileBytes,
+                                 k_chunk, k_chunk, qop, qlo, masks, c_scale, m_run, l_run, acc);
+    }
+    // finalise: sink, normalise, store (lane: row l32, dims 32m + 8(i/4) + 4h + i%4)
+    l_run = half_swap_sum(l_run);
+    if (row_ok) {
+      QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
+      float f = 0.f, inv = 0.f;
+      if (m_run != kNegInf) {
+        const float ms = m_run * c_scale;
+        const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
+        const float M2 = fmaxf(ms, sg);
+        f = exp2_safe(ms - M2);
+        inv = f / (l_run * f + exp2_safe(sg - M2));
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * m + 8 * g4 + 4 * h;
+          typename Op32<QT>::v4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = from_f32<QT>(acc[m][4 * g4 + e] * inv);
+          *reinterpret_cast<typename Op32<QT>::v4*>(o + d0) = w;
+        }
+    }
+  }
+  raise();
+}
+
 template <typename QT, typename KT, int D>
 static void launch_prefill_typed(const PrefillParams& P, int RW, hipStream_t stream) {
   const size_t lds = PfLds<D, sizeof(KT) == 2>::kTotal;
@@ -663,6 +904,28 @@ int launch_prefill_attention(const AttnArgs& a, hipStream_t stream) {
   P.group = a.H_q / a.H_kv;
   P.max_q = a.max_q; P.max_k = a.max_k; P.window = a.window;
   P.scale_log2 = a.scale * kLog2e;
+  // a window of at most kWinMax keys over a 16-bit cache, groups of 4 or more heads: the
+  // one-span kernel (8 waves for groups of 8 or more, else 4)
+  if (a.window > 0 && a.window <= kWinMax && a.cache_dtype == a.dtype && P.group >= 4) {
+    P.n_rt = (a.max_q + kWinRows - 1) / kWinRows;
+    const long total = ((long)a.B * a.H_kv + 7) / 8 * 8 * P.n_rt;
+    if (total <= 0) return SPATTN_OK;
+    if (total > 0x7fffffffL) return SPATTN_ERR_SHAPE;
+    P.total = (int)total;
+    const bool w8 = P.group >= 8;
+#define SPATTN_WIN(QT, DD)                                                                      \
+  if (w8) hipLaunchKernelGGL((prefill_window_kernel<QT, DD, 8>), dim3(P.total), dim3(512),      \
+                             WinLds<DD>::kTotal, stream, P);                                    \
+  else hipLaunchKernelGGL((prefill_window_kernel<QT, DD, 4>), dim3(P.total), dim3(256),         \
+                          WinLds<DD>::kTotal, stream, P)
+    if (a.D == 64) {
+      if (a.dtype == SPATTN_F16) { SPATTN_WIN(f16, 64); } else { SPATTN_WIN(bf16, 64); }
+    } else {
+      if (a.dtype == SPATTN_F16) { SPATTN_WIN(f16, 128); } else { SPATTN_WIN(bf16, 128); }
+    }
+#undef SPATTN_WIN
+    return hipGetLastError() == hipSuccess ? SPATTN_OK : SPATTN_ERR_LAUNCH;
+  }
   // workgroup = RW row blocks x (4 / RW) heads: two row blocks of two heads measured fastest
   // for groups of 4 or more (more rows per K/V tile than four heads of one row block)
   const int RW = P.group == 1 ? 4 : 2;
