@@ -63,6 +63,57 @@ def test_topk_variants(v):
     _check(case, name)
 
 
+# Rows longer than 16384 candidates take the streaming path (persistent workgroups, the
+# next segment's scores copied under the current one's selection); these cases walk its
+# branches: several segments a workgroup with rows that select everything in between, one-
+# and two-word rows, ranked counts on both sides of the 32768-position word edge, no
+# ranked selection (tail >= k, k = 0), no tail, NaN / -0 scores and the shortest row
+# length that takes the path.
+STREAM_VARIANTS = [
+    # (name, kv_lens, q_lens, H_kv, L, k, tail, capacity, ties, specials)
+    ("stream_many_segments", [20000, 100, 17000, 2500], [40, 30, 20, 10], 4, 20000, 1024, 16,
+     1100, 0.2, 0.01),
+    ("stream_two_words_mixed", [65536, 30000, 32833, 40000], [8, 8, 3, 8], 4, 65536, 2048, 64,
+     2048, 0.1, 0.005),
+    ("stream_tail_covers_k", [30000, 25000], [3, 2], 2, 30000, 100, 150, 128, 0.0, 0.0),
+    ("stream_k0", [30000], [2], 2, 30000, 0, 5, 4, 0.0, 0.0),
+    ("stream_no_tail_specials", [50000, 49000], [4, 4], 2, 50000, 3000, 0, 3000, 0.3, 0.05),
+    ("stream_L16388", [16388, 16000], [4, 4], 3, 16388, 700, 8, 700, 0.3, 0.02),
+]
+
+
+@pytest.mark.parametrize("v", STREAM_VARIANTS, ids=[v[0] for v in STREAM_VARIANTS])
+def test_topk_stream_variants(v):
+    name, kv, ql, H, L, k, tail, cap, ties, spec = v
+    case = synth.topk_case(sum(map(ord, name)), kv_lens=kv, q_lens=ql, H_kv=H, L=L, k=k, tail=tail,
+                           capacity=cap, ties=ties, specials=spec, name=name)
+    _check(case, name)
+
+
+@pytest.mark.parametrize("L", [3000, 40000], ids=["L3000", "L40000"])
+def test_rows_owned_by_no_request(L):
+    """Rows past cu[B] belong to no request: count 0, every slot -1 and the BAD_CU status
+    bit; the owned rows still match the oracle."""
+    case = synth.topk_case(L, kv_lens=[L, L // 2], q_lens=[3, 2], H_kv=2, L=L, k=256, tail=8,
+                           capacity=260, ties=0.1, specials=0.01)
+    extra = 3
+    scores = np.concatenate([case.scores, np.ones((extra,) + case.scores.shape[1:], np.float32)])
+    sel = torch.full((case.T + extra, 2, 260), 777, dtype=torch.int32, device="cuda")
+    cnt = torch.full((case.T + extra, 2), 777, dtype=torch.int32, device="cuda")
+    st = status_tensor()
+    print("topk rows owned by no request", L, flush=True)
+    sta.topk_select(tensor(scores), tensor(case.cu_seqlens_q), tensor(case.seqlens_k), case.k,
+                    sel, cnt, tail=case.tail, status=st)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    assert int(st.item()) & sta.STATUS_BAD_CU
+    assert (cnt[case.T:] == 0).all() and (sel[case.T:] == -1).all()
+    want_sel, want_cnt = oracle.topk_select(case.scores, case.cu_seqlens_q, case.seqlens_k,
+                                            k=case.k, tail=case.tail, capacity=260)
+    assert np.array_equal(cnt[:case.T], want_cnt)
+    assert np.array_equal(sel[:case.T], want_sel)
+
+
 def test_all_equal_scores_take_the_lowest_positions():
     case = synth.topk_case(3, kv_lens=[40000], q_lens=[2], H_kv=2, L=40000, k=1000, tail=10)
     case.scores[:] = 0.5
