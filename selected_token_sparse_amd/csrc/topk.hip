@@ -321,8 +321,16 @@ __device__ __forceinline__ void ts_transpose_stage(uint32_t* W) {
   for (int k = 0; k < 32; ++k) {
     if (k & J) continue;
     uint32_t a = W[k], c = W[k + J];
-    const uint32_t a2 = (a & m) | ((c << J) & ~m);
-    const uint32_t c2 = (c & ~m) | ((a >> J) & m);
+    uint32_t a2, c2;
+    if (J >= 8) {
+      // whole bytes move: one byte permute per row (selector bytes 0-3 pick a's bytes,
+      // 4-7 c's)
+      a2 = __builtin_amdgcn_perm(c, a, J == 16 ? 0x05040100u : 0x06020400u);
+      c2 = __builtin_amdgcn_perm(c, a, J == 16 ? 0x07060302u : 0x07030501u);
+    } else {
+      a2 = (a & m) | ((c << J) & ~m);
+      c2 = (c & ~m) | ((a >> J) & m);
+    }
     a = a2; c = c2;
     asm volatile("" : "+v"(a), "+v"(c));   // keeps the exchanges in order (register pressure)
     W[k] = a; W[k + J] = c;
@@ -443,21 +451,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
     }
   };
   auto make_planes = [&](uint32_t* kw, int w, int m, bool copy_steps) {
-    // sign flip for the common case, then an exact pass over the word when one of its
-    // scores is a NaN or -0 (the flip is undone bit-exactly)
-    bool special = false;
+    // order-preserving keys: adding +0 turns -0 into +0 and leaves every other number
+    // (subnormals included: the kernels keep float32 denormals) unchanged, the sign flip
+    // orders the numbers, and a NaN gets key 1
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
-      const uint32_t b = kw[c];
-      special |= __builtin_amdgcn_classf(__builtin_bit_cast(float, b), 0x23);
-      kw[c] = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
-    }
-    if (special) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        const uint32_t k = kw[c];
-        kw[c] = score_key_bits((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
-      }
+      const float f = __builtin_bit_cast(float, kw[c]);
+      const uint32_t b = __builtin_bit_cast(uint32_t, f + 0.0f);
+      const uint32_t k = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+      kw[c] = __builtin_isnan(f) ? 1u : k;
     }
     if (copy_steps) dma_step();
     ts_transpose(kw);
@@ -499,17 +501,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
     if (wb < m) load_word(key, 0, m);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();   // the stage is free
-    if (NW == 1 && next < S) dma_begin(next, 0, n_next - min(min(P.tail, P.k), n_next));
-    if (wb < m) make_planes(key, 0, m, NW == 1);
-    if (NW > 1) {
-      // word 1 through the stage; a wave issues its copy once its word 0 is in planes (a
-      // wave that issues a burst of memory instructions stalls until the memory system
-      // takes them)
+    if (NW == 1) {
+      if (next < S) dma_begin(next, 0, n_next - min(min(P.tail, P.k), n_next));
+      if (wb < m) make_planes(key, 0, m, true);
+    } else {
+      // word 1 through the stage: a wave issues its share of the copy once its word 0 is
+      // in planes (a wave that issues a burst of memory instructions stalls until the
+      // memory system takes them; copies issued by only a few waves ran slower)
+      if (wb < m) make_planes(key, 0, m, false);
       if (words > 1) {
         dma_begin(seg, 1, m);
         for (int i = 0; i < 8; ++i) dma_step();
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
+      if (words > 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();   // word 1 is in the stage
       if (kTsWord + wb < m) load_word(key + 32, 1, m);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
