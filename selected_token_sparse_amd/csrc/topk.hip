@@ -421,14 +421,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
   // bytes a lane) to stage byte 1024 q; wave v issues q = v + 16 i as slice i (i < 8).
   // Lanes past m re-read the word's first unit.
   const float* dma_row = nullptr;
-  int dma_len = 0, dma_slice = 8, dma_limit = 8;
+  int dma_len = 0, dma_slice = 8;
   auto dma_begin = [&](int s, int w, int m) {
     dma_row = P.scores + (int64_t)s * P.L + w * kTsWord;
     dma_len = min(kTsWord, m - w * kTsWord);
     dma_slice = 0;
   };
   auto dma_step = [&]() {
-    if (dma_slice < dma_limit) {
+    if (dma_slice < 8) {
       const int q = wave + kTkWaves * dma_slice;
       if (256 * q < dma_len) {
         int u = 64 * q + lane;
@@ -522,19 +522,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
       if (next < S) dma_begin(next, 0, n_next - min(min(P.tail, P.k), n_next));
     }
 
-    // Two words: word 1's planes 0..15 wait in the upper half of the stage until the search
-    // reaches them (step 8), which keeps the register count of the search within budget;
-    // the next segment's copy fills the lower half meanwhile (slices 0..3) and the upper
-    // half once every wave has taken its planes back.
-    uint32_t* park = stage + kTsWord / 2 + 4 * tid;
-    if (NW > 1) {
-      dma_limit = 4;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<u32x4*>(park + 4096 * q) =
-            u32x4{key[32 + 4 * q], key[33 + 4 * q], key[34 + 4 * q], key[35 + 4 * q]};
-    }
-
     // select the need-th largest key, two bits a step: gt = keys above the prefix so far,
     // eq = keys equal to it.  A step counts the keys of eq whose next two bits are 11, 1x and
     // non-zero, takes the largest digit d whose keys at or above it reach need, and stops
@@ -545,18 +532,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
     int gt_total = 0, ge_total = -1;   // counts of keys above / at or above the prefix
 #pragma unroll
     for (int b = 31; b >= 1; b -= 2) {
-      if (NW > 1 && b == 15) {   // (also after an early stop: the old values are then dead)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(park + 4096 * q);
-          key[32 + 4 * q] = v[0]; key[33 + 4 * q] = v[1]; key[34 + 4 * q] = v[2]; key[35 + 4 * q] = v[3];
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      }
-      if (NW > 1 && b == 13) dma_limit = 8;   // after step 8's barrier: the upper half is free
       if (ge_total != need) {
         dma_step();
-        if (NW > 1 && b < 15) dma_step();
         uint32_t c3 = 0, c2 = 0, c1 = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -612,26 +589,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
         }
       }
     }
-    if (NW > 1 && dma_limit < 8) {
-      __syncthreads();   // the search stopped before step 8: nobody reads the parked planes
-      dma_limit = 8;
-    }
     const int remaining = need - gt_total;   // taken from eq, lowest positions first
 
     // emit in position order: word 0 of every thread, then word 1; one scan per word counts
-    // the selected keys (above the selected one, or in the tail) and the tied ones together
-    int pe = 32 * tid, me = m, ne = n;
-    asm volatile("" : "+v"(pe), "+s"(me), "+s"(ne));   // (none of this computed early)
+    // the selected keys above the selected one and the tied ones together.  The tail
+    // (positions m .. n-1, after every ranked one) fills the last nt entries.
+    int pe = 32 * tid;
+    asm volatile("" : "+v"(pe));   // (none of this computed early)
     uint32_t Gp[NW], Ep[NW], sc[NW], incl[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const int pw = w * kTsWord + pe;
       Gp[w] = __builtin_rotateleft32(gt[w], rot);
       Ep[w] = __builtin_rotateleft32(eq[w], rot);
-      const int lo = min(max(me - pw, 0), 32), hi = min(max(ne - pw, 0), 32);
-      const uint32_t below_hi = hi ? (0xFFFFFFFFu >> (32 - hi)) : 0u;
-      const uint32_t below_lo = lo ? (0xFFFFFFFFu >> (32 - lo)) : 0u;
-      Gp[w] |= below_hi & ~below_lo;   // the tail (disjoint from gt: unranked keys are 0)
       sc[w] = (uint32_t)__builtin_popcount(Gp[w]) | ((uint32_t)__builtin_popcount(Ep[w]) << 16);
       incl[w] = ts_wave_scan(sc[w]);   // per-word block totals <= 32768 in each half
       if (lane == 63) wtot[wave][w] = incl[w];
@@ -671,6 +640,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
       base_a += (int)(total & 0xFFFFu);
       base_e += (int)(total >> 16);
     }
+    for (int j = tid; j < nt; j += kTkThreads) out[need + j] = m + j;
     for (int j = P.k + tid; j < P.capacity; j += kTkThreads) out[j] = -1;
     if (tid == 0) P.sel_count[seg] = P.k;
     // the rest of the next segment's copy after the stores (queued behind the copy, the
