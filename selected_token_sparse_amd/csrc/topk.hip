@@ -312,7 +312,8 @@ __device__ __forceinline__ int ts_candidates(const TopkParams& P, int seg) {
 }
 
 // One stage of the 32 x 32 bit transpose: rows k and k + J (k without bit J) exchange the
-// upper J-bit halves of row k's 2J-bit groups with the lower halves of row k + J's.
+// upper J-bit halves of row k's 2J-bit groups with the lower halves of row k + J's.  The
+// stages J = 16, 8, 4, 2, 1 in turn leave W[b] bit c = bit b of the word that was W[c].
 template <int J>
 __device__ __forceinline__ void ts_transpose_stage(uint32_t* W) {
   constexpr uint32_t m = J == 16 ? 0x0000FFFFu : J == 8 ? 0x00FF00FFu : J == 4 ? 0x0F0F0F0Fu
@@ -337,14 +338,6 @@ __device__ __forceinline__ void ts_transpose_stage(uint32_t* W) {
   }
 }
 
-// In place: afterwards W[b] bit c = bit b of the word that was W[c].
-__device__ __forceinline__ void ts_transpose(uint32_t* W) {
-  ts_transpose_stage<16>(W);
-  ts_transpose_stage<8>(W);
-  ts_transpose_stage<4>(W);
-  ts_transpose_stage<2>(W);
-  ts_transpose_stage<1>(W);
-}
 
 // Sum over the wave (every lane gets it, as a scalar).
 __device__ __forceinline__ uint32_t ts_wave_sum(uint32_t v) {
@@ -450,7 +443,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
       kw[4 * j] = v[0]; kw[4 * j + 1] = v[1]; kw[4 * j + 2] = v[2]; kw[4 * j + 3] = v[3];
     }
   };
+  // (copy_steps: one DMA slice of the copy in flight between each pair of phases, eight
+  // in all, so that no wave stalls on a burst of them)
   auto make_planes = [&](uint32_t* kw, int w, int m, bool copy_steps) {
+    if (copy_steps) dma_step();
     // order-preserving keys: adding +0 turns -0 into +0 and leaves every other number
     // (subnormals included: the kernels keep float32 denormals) unchanged, the sign flip
     // orders the numbers, and a NaN gets key 1
@@ -460,9 +456,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
       const uint32_t b = __builtin_bit_cast(uint32_t, f + 0.0f);
       const uint32_t k = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
       kw[c] = __builtin_isnan(f) ? 1u : k;
+      if (copy_steps && c == 15) dma_step();
     }
     if (copy_steps) dma_step();
-    ts_transpose(kw);
+    ts_transpose_stage<16>(kw);
+    if (copy_steps) dma_step();
+    ts_transpose_stage<8>(kw);
+    if (copy_steps) dma_step();
+    ts_transpose_stage<4>(kw);
+    if (copy_steps) dma_step();
+    ts_transpose_stage<2>(kw);
+    if (copy_steps) dma_step();
+    ts_transpose_stage<1>(kw);
     if (copy_steps) dma_step();
     const int valid = min(max(m - w * kTsWord - 32 * tid, 0), 32);
     if (valid < 32) {
@@ -505,14 +510,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_stream_kernel(TopkParams P) {
       if (next < S) dma_begin(next, 0, n_next - min(min(P.tail, P.k), n_next));
       if (wb < m) make_planes(key, 0, m, true);
     } else {
-      // word 1 through the stage: a wave issues its share of the copy once its word 0 is
-      // in planes (a wave that issues a burst of memory instructions stalls until the
-      // memory system takes them; copies issued by only a few waves ran slower)
-      if (wb < m) make_planes(key, 0, m, false);
-      if (words > 1) {
-        dma_begin(seg, 1, m);
-        for (int i = 0; i < 8; ++i) dma_step();
-      }
+      // word 1 through the stage, its copy spread through word 0's conversion (a wave that
+      // issues a burst of memory instructions stalls until the memory system takes them;
+      // copies issued by only a few waves ran slower)
+      if (words > 1) dma_begin(seg, 1, m);
+      if (wb < m) make_planes(key, 0, m, words > 1);
+      while (dma_slice < 8) dma_step();
       if (words > 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();   // word 1 is in the stage
       if (kTsWord + wb < m) load_word(key + 32, 1, m);
