@@ -822,86 +822,73 @@ void split_attn_kernel(SplitParams P) {
 // SparsePagedAttention", finalize stage; one wave per (row, query head), merge
 // coefficients shared across the head's output channels).
 // ---------------------------------------------------------------------------------------
-template <typename QT, int D>
+template <typename QT, int D, int kBatch>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws_acc,
                                                     const float2* __restrict__ ws_ml,
                                                     const float* __restrict__ sinks,
                                                     void* __restrict__ out, int T, int H_q,
                                                     int n_splits) {
-  // Splits without a visible key wrote m = -inf and no accumulator: only live splits are
-  // read.  Their (m, l) pairs come in one parallel round (lane s holds split s + 64 g); the
-  // accumulators of live splits are then loaded eight at a time with every load in flight
-  // before the first is used.
-  constexpr int kGroups = kMaxSplits / 64;
+  // Splits without a visible key wrote m = -inf and no accumulator (their accumulator
+  // memory is stale).  Every split's (m, l) and accumulator load of a batch of kBatch
+  // (n_splits rounded up to a power of two, at most 16) is issued before any is used: one
+  // memory round for up to 16 splits.  A dead split's accumulator is dropped by a select,
+  // never multiplied in.
+  constexpr int PER = D / 64;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (pair >= T * H_q) return;
   const int head = pair % H_q;
   const int64_t stride = (int64_t)T * H_q;
-  float2 ml[kGroups];
+  float M = kNegInf, L = 0.f;   // running reference maximum and normaliser
+  float A[PER];
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    const int sp = lane + 64 * g;
-    ml[g] = sp < n_splits ? ws_ml[sp * stride + pair] : make_float2(kNegInf, 0.f);
+  for (int e = 0; e < PER; ++e) A[e] = 0.f;
+  for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+    float2 ml[kBatch];
+    float a[kBatch][PER];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int sp = min(s0 + k, n_splits - 1);   // (in range; repeats are dropped below)
+      ml[k] = ws_ml[sp * stride + pair];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) a[k][e] = ws_acc[(sp * stride + pair) * D + lane + 64 * e];
+    }
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (s0 + k < n_splits) Mb = fmaxf(Mb, ml[k].x);
+    if (Mb == kNegInf) continue;                  // nothing visible yet
+    const float r = M == kNegInf ? 0.f : exp2_safe(M - Mb);
+    L *= r;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) A[e] *= r;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const bool live = s0 + k < n_splits && ml[k].x != kNegInf;
+      const float f = live ? exp2_safe(ml[k].x - Mb) : 0.f;
+      L += live ? ml[k].y * f : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) A[e] += live ? a[k][e] * f : 0.f;
+    }
+    M = Mb;
   }
-  float M = kNegInf;
+  // the sink joins the maximum and the normaliser only (read last, so that its load is in
+  // flight with the others); no visible key (A = 0): zeros
+  const float sg = sinks != nullptr ? sinks[head] * kLog2e : kNegInf;
+  const float Mf = fmaxf(M, sg);
+  float Lt = 0.f;
+  if (Mf != kNegInf) {
+    const float r = M == kNegInf ? 0.f : exp2_safe(M - Mf);
+    Lt = L * r + (sg == kNegInf ? 0.f : exp2_safe(sg - Mf));
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) M = fmaxf(M, ml[g].x);
-  M = xor_max(M, 32); M = xor_max(M, 16); M = xor_max(M, 8);
-  M = xor_max(M, 4); M = xor_max(M, 2); M = xor_max(M, 1);
-  constexpr int PER = D / 64;
+    for (int e = 0; e < PER; ++e) A[e] *= r;
+  }
   float res[PER];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) res[k] = 0.f;
-  if (M != kNegInf) {
-    const float sg = sinks != nullptr ? sinks[head] * kLog2e : kNegInf;
-    const float M2 = fmaxf(M, sg);
-    float f[kGroups];
-    float Lp = 0.f;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      f[g] = ml[g].x != kNegInf ? exp2_safe(ml[g].x - M2) : 0.f;
-      Lp += ml[g].y * f[g];
-    }
-    Lp = xor_sum(Lp, 32); Lp = xor_sum(Lp, 16); Lp = xor_sum(Lp, 8);
-    Lp = xor_sum(Lp, 4); Lp = xor_sum(Lp, 2); Lp = xor_sum(Lp, 1);
-    const float L = Lp + exp2_safe(sg - M2);
-    float A[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) A[k] = 0.f;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      if (64 * g >= n_splits) break;
-      uint64_t live = __ballot(ml[g].x != kNegInf);
-      while (live) {
-        // the next (up to) eight live splits; missing ones repeat the first with weight 0
-        int idx[8];
-        float cf[8];
-        const int first = __builtin_ctzll(live);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int bit = live ? __builtin_ctzll(live) : first;
-          cf[k] = live ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f[g]), bit)) : 0.f;
-          idx[k] = 64 * g + bit;
-          live &= live - 1;
-        }
-        float a[8][PER];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-#pragma unroll
-          for (int e = 0; e < PER; ++e) a[k][e] = ws_acc[(idx[k] * stride + pair) * D + lane + 64 * e];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-#pragma unroll
-          for (int e = 0; e < PER; ++e) A[e] += a[k][e] * cf[k];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) res[k] = A[k] / L;
-  }
+  for (int e = 0; e < PER; ++e) res[e] = Lt > 0.f ? A[e] / Lt : 0.f;
   QT* o = reinterpret_cast<QT*>(out) + (int64_t)pair * D;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) o[lane + 64 * k] = from_f32<QT>(res[k]);
+  for (int e = 0; e < PER; ++e) o[lane + 64 * e] = from_f32<QT>(res[e]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1154,9 +1141,16 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   if (!direct) {
     const int pairs = a.T * a.H_q;
     dim3 grid((pairs + 3) / 4);
+#define SPATTN_MERGE_B(QT, DD, NB)                                                           \
+  hipLaunchKernelGGL((merge_kernel<QT, DD, NB>), grid, dim3(256), 0, stream, P.ws_acc,       \
+                     P.ws_ml, a.sinks, a.out, a.T, a.H_q, plan.n_splits)
 #define SPATTN_MERGE(QT, DD)                                                                 \
-  hipLaunchKernelGGL((merge_kernel<QT, DD>), grid, dim3(256), 0, stream, P.ws_acc, P.ws_ml,  \
-                     a.sinks, a.out, a.T, a.H_q, plan.n_splits)
+  do {                                                                                       \
+    if (plan.n_splits <= 2) SPATTN_MERGE_B(QT, DD, 2);                                       \
+    else if (plan.n_splits <= 4) SPATTN_MERGE_B(QT, DD, 4);                                  \
+    else if (plan.n_splits <= 8) SPATTN_MERGE_B(QT, DD, 8);                                  \
+    else SPATTN_MERGE_B(QT, DD, 16);                                                         \
+  } while (0)
     if (a.D == 64) {
       if (a.dtype == SPATTN_F32) SPATTN_MERGE(float, 64);
       else if (a.dtype == SPATTN_F16) SPATTN_MERGE(f16, 64);
@@ -1167,6 +1161,7 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
       else SPATTN_MERGE(bf16, 128);
     }
 #undef SPATTN_MERGE
+#undef SPATTN_MERGE_B
     if (hipGetLastError() != hipSuccess) return SPATTN_ERR_LAUNCH;
   }
   return SPATTN_OK;
