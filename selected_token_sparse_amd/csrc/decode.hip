@@ -829,10 +829,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
                                                     void* __restrict__ out, int T, int H_q,
                                                     int n_splits) {
   // Splits without a visible key wrote m = -inf and no accumulator (their accumulator
-  // memory is stale).  Every split's (m, l) and accumulator load of a batch of kBatch
-  // (n_splits rounded up to a power of two, at most 16) is issued before any is used: one
-  // memory round for up to 16 splits.  A dead split's accumulator is dropped by a select,
-  // never multiplied in.
+  // memory is stale and is not read).  Per batch of kBatch splits (n_splits rounded up to
+  // a power of two, at most 16): the (m, l) pairs in one round, then the accumulators of
+  // the live splits, every load issued before any is used.
   constexpr int PER = D / 64;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -850,8 +849,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
     for (int k = 0; k < kBatch; ++k) {
       const int sp = min(s0 + k, n_splits - 1);   // (in range; repeats are dropped below)
       ml[k] = ws_ml[sp * stride + pair];
+    }
 #pragma unroll
-      for (int e = 0; e < PER; ++e) a[k][e] = ws_acc[(sp * stride + pair) * D + lane + 64 * e];
+    for (int k = 0; k < kBatch; ++k) {
+      const int sp = min(s0 + k, n_splits - 1);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) a[k][e] = 0.f;
+      if (s0 + k < n_splits && ml[k].x != kNegInf) {   // (uniform across the wave)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) a[k][e] = ws_acc[(sp * stride + pair) * D + lane + 64 * e];
+      }
     }
     float Mb = M;
 #pragma unroll
