@@ -194,16 +194,22 @@ def bench_decode(steps, warmup, copies=3, cache_dtype=None, fused=False):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [_events() for _ in range(steps)]
+    # the timed steps, back to back with nothing recorded between them
     t0, t1 = _events()
-    torch.cuda.synchronize()
     _queue_ahead()
     t0.record()
     for i in range(steps):
-        step(i, evs[i])
+        step(i)
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    # the same steps again with events around each call: its duration distribution (the
+    # event records between calls would lengthen the steps timed above)
+    evs = [_events() for _ in range(steps)]
+    _queue_ahead()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     attn_ms = sorted(a.elapsed_time(b) for a, b in evs)
     st = int(status.item())
     return case, total_ms / steps, attn_ms, st
