@@ -48,11 +48,14 @@ constexpr int kWgStep = kWaves * kTile;
 constexpr int kMaxChunk = 2048;    // keys per split while there are enough workgroups
 constexpr int kChunkCap = 4096;    // keys per split, hard limit (LDS row-index buffer)
 constexpr int kMaxSplits = 256;    // splits per item (LDS merge coefficients)
-// Workgroups the split plan aims for: paged ranges stream 2 KB runs and gain from more,
-// shorter splits; selected rows are random 256-byte gathers where fewer, longer splits
-// (fewer partial states) measured faster.
-constexpr int kTargetWorkgroupsPaged = 4096;
-constexpr int kTargetWorkgroupsSparse = 2048;
+// Workgroups the split plan aims for (the split length doubles until the plan has at most
+// this many).  Measured on the GQA decode (248 row-head items, up to 8192 keys): 992
+// workgroups of 2048 keys match 3968 of 512 over a 16-bit cache and are 10-18% faster over
+// 8-bit caches, whose shorter byte streams leave more of the time to per-workgroup set-up
+// and partial states.  Selected and local-plus-aux rows run fastest at one workgroup per
+// item and key range: 512 workgroups of 2048 selected keys need no merge at all.
+constexpr int kTargetWorkgroupsPaged = 1024;
+constexpr int kTargetWorkgroupsSparse = 512;
 constexpr int kMetaLdsMax = 512;   // cu entries staged in LDS (more: binary search in memory)
 static_assert(kStepMaxB + 1 <= kThreads, "a fused step stages one boundary per thread");
 
