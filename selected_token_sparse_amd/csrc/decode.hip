@@ -102,6 +102,7 @@ struct SplitParams {
   int max_q, max_k, max_sel, window, aux_len;
   int64_t aux_row_stride;   // rows (of D elements) between requests in the aux store
   int chunk, n_main, n_splits;
+  int row_slots;            // LDS entries of the split's row table (see split_row_slots)
   int meta_lds;             // 1: cu / seqlens_k staged in LDS
   float scale_log2;         // scale * log2(e)
   // Fused decode step (past != nullptr, paged kind, B + 1 <= kThreads): seqlens_k is
@@ -129,7 +130,10 @@ __device__ __forceinline__ int wave_or_flags(int flags) {
 // so nothing waits for it (a read-then-OR would put a contended load on the critical path).
 
 // LDS layout (bytes): per-wave V tiles (reused as the combine / merge area after the key
-// loop), then the split's cache-row indices, then the staged metadata.
+// loop), then the split's row table, then the staged metadata.  The row table holds one
+// cache-row index per key for selected and auxiliary rows, and one base row per cache block
+// for paged ranges (a key's row is its block's base plus its offset in the block), so a
+// 2048-key paged split needs 129 entries at block size 16 instead of 2048.
 template <int D>
 struct SplitLds {
   // two tiles in flight per wave: a wave's two V tile buffers
@@ -140,8 +144,15 @@ struct SplitLds {
 };
 
 template <int D>
-static size_t split_lds_bytes(int chunk, int meta_ints) {
-  return SplitLds<D>::kAreaBytes + (size_t)chunk * 4 + (size_t)meta_ints * 4;
+static size_t split_lds_bytes(int row_slots, int meta_ints) {
+  return SplitLds<D>::kAreaBytes + (size_t)row_slots * 4 + (size_t)meta_ints * 4;
+}
+
+// Row-table entries of a split of `chunk` keys: with a block table, one per block a paged
+// range can touch (a split may start inside a block); otherwise one per key.
+static int split_row_slots(int kind, int chunk, bool paged, int block_size) {
+  if (kind != SPATTN_KIND_PAGED || !paged) return chunk;
+  return (chunk + block_size - 2) / block_size + 1;
 }
 
 // LDS-DMA of 16 bytes per lane: lane l's bytes land at lds + 16 * l (the LDS address is
@@ -675,17 +686,18 @@ __device__ __forceinline__ void combine_and_store(const SplitParams& P, unsigned
   __syncthreads();
 }
 
-// Occupancy hint for D = 64, where each wave keeps two tiles in flight: 5 waves per SIMD
-// for 16-bit caches (that register budget holds both tiles' K operands without spilling);
-// one fewer when the kernel also carries the second (window) source; 4 for INT8 caches,
-// whose tiles hold the raw K and V codes and whose query has a second (low) operand; 3
+// Occupancy hint for D = 64, where each wave keeps two tiles in flight: 4 waves per SIMD
+// for 16-bit and INT8 caches (the double-buffered V tiles take 32 KB of LDS per
+// workgroup, so a CU holds at most 4 workgroups of 4 waves whatever the registers allow;
+// INT8 tiles hold the raw K and V codes and the query has a second, low operand); one
+// fewer when the kernel also carries the second (window) source over an 8-bit cache; 3
 // for FP8 caches, whose conversion needs a few more registers (at 4 it spills inside the
-// key loop: 63.6 us against 56.6 at 3 for the FP8 decode; INT8 at 4: 53.1 us).
+// key loop: 63.6 us against 56.6 at 3 for the FP8 decode).
 template <int KIND, typename KT, int D>
 constexpr int split_waves_per_eu() {
   if (D != 64) return 1;
   if (KIND == SPATTN_KIND_LOCAL_AUX) return sizeof(KT) == 1 ? 3 : 4;
-  return std::is_same<KT, uint8_t>::value ? 3 : sizeof(KT) == 1 ? 4 : 5;
+  return std::is_same<KT, uint8_t>::value ? 3 : 4;
 }
 
 template <int KIND, typename QT, typename KT, typename AT, int D, bool kStep>
@@ -699,7 +711,7 @@ void split_attn_kernel(SplitParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* area = smem;
   int32_t* rows = reinterpret_cast<int32_t*>(smem + SplitLds<D>::kAreaBytes);
-  int32_t* meta = rows + P.chunk;
+  int32_t* meta = rows + P.row_slots;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -770,7 +782,30 @@ void split_attn_kernel(SplitParams P) {
       P.ws_ml[(int64_t)split * P.T * P.H_q + (int64_t)r * P.H_q + h0 + tid] = make_float2(kNegInf, 0.f);
     return;
   }
-  for (int v = tid; v < sr.n_keys; v += kThreads) rows[v] = split_key_row(P, sr, ri, c, v, flags);
+  // paged range through a block table: keys j0 .. j0 + n_keys - 1, the base row of block
+  // lb at rows[lb - lb0] (-1: missing); other sources: key k's row at rows[k]
+  const bool blocks = KIND == SPATTN_KIND_PAGED && P.cd.block_table != nullptr;
+  const int j0 = sr.lo + sr.v0;
+  const int bs = P.cd.block_size, bsh = P.cd.bs_shift;
+  auto block_of = [&](int j) { return bsh >= 0 ? j >> bsh : j / bs; };
+  const int lb0 = block_of(j0);
+  if (blocks) {
+    const int n_ent = sr.n_keys > 0 ? block_of(j0 + sr.n_keys - 1) - lb0 + 1 : 0;
+    for (int v = tid; v < n_ent; v += kThreads) {
+      const int lb = lb0 + v;
+      int e = -1;
+      if (lb >= P.cd.max_blocks) {
+        flags |= SPATTN_STATUS_CAPACITY;
+      } else {
+        const int blk = P.cd.block_table[(int64_t)ri.b * P.cd.max_blocks + lb];
+        if (blk < 0 || blk >= P.cd.num_blocks) flags |= SPATTN_STATUS_BAD_BLOCK;
+        else e = (blk * P.cd.H_kv + c) * bs;
+      }
+      rows[v] = e;
+    }
+  } else {
+    for (int v = tid; v < sr.n_keys; v += kThreads) rows[v] = split_key_row(P, sr, ri, c, v, flags);
+  }
   if (kStep && ri.b >= 0 && !cursor_bad(ri.b)) {
     // fused step: the new keys of this split's range, written before the barrier below
     const int first_new = ri.kv_len - ri.q_len, k0 = sr.lo + sr.v0;
@@ -790,7 +825,13 @@ void split_attn_kernel(SplitParams P) {
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool use_scale = sizeof(KT) == 1 && sr.src != SRC_AUX;
-  auto row_at = [&](int k) { return rows[k]; };
+  auto row_at = [&](int k) -> int {
+    if (!blocks) return rows[k];
+    const int j = j0 + k;
+    const int lb = block_of(j);
+    const int e = rows[lb - lb0];
+    return e < 0 ? -1 : e + (j - lb * bs);
+  };
   if (sr.n_keys > 0) {
     if (KIND != SPATTN_KIND_LOCAL_AUX || sr.src != SRC_AUX) {
       main_cache_keys<QT, KT, D>(P, qrow, q0row, hv, qraw, c, row_at, sr.n_keys,
@@ -1059,7 +1100,7 @@ SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_
 template <int KIND, typename QT, typename KT, typename AT, int D>
 static void launch_split_typed(const SplitParams& P, hipStream_t stream) {
   const int blocks = P.n_splits * P.T * P.H_kv * P.head_tiles;
-  const size_t lds = split_lds_bytes<D>(P.chunk, P.meta_lds || P.past != nullptr ? 3 * P.B + 1 : 0);
+  const size_t lds = split_lds_bytes<D>(P.row_slots, P.meta_lds || P.past != nullptr ? 3 * P.B + 1 : 0);
   // the fused decode step is its own instantiation, so the other kernels carry none of it
   if constexpr (KIND == SPATTN_KIND_PAGED) {
     if (P.past != nullptr) {
@@ -1129,6 +1170,7 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   P.aux_len = a.aux_len;
   P.aux_row_stride = a.aux_stride / a.D;
   P.chunk = plan.chunk; P.n_main = plan.n_main; P.n_splits = plan.n_splits;
+  P.row_slots = split_row_slots(a.kind, plan.chunk, a.block_table != nullptr, a.block_size);
   P.meta_lds = a.B + 1 <= kMetaLdsMax ? 1 : 0;
   P.scale_log2 = a.scale * kLog2e;
   P.past = a.past; P.k_new = a.k_new; P.v_new = a.v_new; P.committed = a.committed;
