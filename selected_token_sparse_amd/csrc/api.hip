@@ -132,8 +132,8 @@ static int decode_step_impl(const int32_t* cu_seqlens_q, const int32_t* past_seq
   a.past = past_seqlens; a.k_new = k_new; a.v_new = v_new;
   a.seqlens_q_out = seqlens_q; a.seqlens_k_out = seqlens_k;
   a.committed = committed_length;
-  const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, max_seqlen_k, 0,
-                                         a.window, H_q, H_kv, D);
+  const SplitPlan plan = make_split_plan(a.kind, dtype, cache_dtype, B, T, max_seqlen_q,
+                                         max_seqlen_k, 0, a.window, H_q, H_kv, D);
   if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
   if (static_scratch && plan.ws_bytes > 0) {
     // the partials go to the static array: checked against its size, then its address
@@ -282,7 +282,8 @@ size_t attention_workspace_bytes(int kind, int dtype, int B, int T, int max_seql
   if (check_heads(H_q, H_kv, D) != SPATTN_OK) return bad;
   if (kind == SPATTN_KIND_LOCAL_AUX && local_window <= 0) return bad;
   if (kind == SPATTN_KIND_PAGED && use_prefill_path(kind, dtype, max_seqlen_q)) return 0;
-  const SplitPlan plan = make_split_plan(kind, dtype, B, T, max_seqlen_q, max_seqlen_k,
+  // the plan of a 16-bit cache: over an 8-bit cache a call never needs more
+  const SplitPlan plan = make_split_plan(kind, dtype, dtype, B, T, max_seqlen_q, max_seqlen_k,
                                          max_selected, local_window, H_q, H_kv, D);
   return plan.n_splits < 0 ? bad : plan.ws_bytes;
 }
@@ -322,8 +323,8 @@ int paged_attention_fwd(const void* q, int dtype, const void* k_cache, const voi
   a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
   hipStream_t st = (hipStream_t)stream;
   if (use_prefill_path(a.kind, dtype, max_seqlen_q)) return launch_prefill_attention(a, st);
-  const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, max_seqlen_k, 0,
-                                         a.window, H_q, H_kv, D);
+  const SplitPlan plan = make_split_plan(a.kind, dtype, cache_dtype, B, T, max_seqlen_q,
+                                         max_seqlen_k, 0, a.window, H_q, H_kv, D);
   if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
     return SPATTN_ERR_WORKSPACE;
@@ -410,8 +411,8 @@ int sparse_attention_fwd(const void* q, int dtype, int mode, const void* k_cache
   a.H_q = H_q; a.H_kv = H_kv; a.D = D;
   a.scale = resolve_scale(scale, D);
   a.sinks = sinks; a.out = out; a.workspace = workspace; a.status = status;
-  const SplitPlan plan = make_split_plan(a.kind, dtype, B, T, max_seqlen_q, 0, max_selected,
-                                         a.window, H_q, H_kv, D);
+  const SplitPlan plan = make_split_plan(a.kind, dtype, a.cache_dtype, B, T, max_seqlen_q, 0,
+                                         max_selected, a.window, H_q, H_kv, D);
   if (plan.n_splits < 0) return SPATTN_ERR_SHAPE;
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
     return SPATTN_ERR_WORKSPACE;

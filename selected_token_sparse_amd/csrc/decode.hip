@@ -45,16 +45,19 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 32;          // keys per wave iteration
 constexpr int kWgStep = kWaves * kTile;
-constexpr int kMaxChunk = 2048;    // keys per split while there are enough workgroups
-constexpr int kChunkCap = 4096;    // keys per split, hard limit (LDS row-index buffer)
+constexpr int kMaxChunk = 2048;    // sparse kinds: keys per split while there are enough workgroups
+constexpr int kChunkCap = 4096;    // keys per split, hard limit (LDS row table)
 constexpr int kMaxSplits = 256;    // splits per item (LDS merge coefficients)
-// Workgroups the split plan aims for (the split length doubles until the plan has at most
-// this many).  Measured on the GQA decode (248 row-head items, up to 8192 keys): 992
-// workgroups of 2048 keys match 3968 of 512 over a 16-bit cache and are 10-18% faster over
-// 8-bit caches, whose shorter byte streams leave more of the time to per-workgroup set-up
-// and partial states.  Selected and local-plus-aux rows run fastest at one workgroup per
-// item and key range: 512 workgroups of 2048 selected keys need no merge at all.
+// Workgroups the split plan aims for.  Paged ranges: one round of resident workgroups, i.e.
+// 256 CUs x the workgroups a CU holds at D = 64 (4; 3 over FP8 caches, whose kernel needs
+// more registers), split evenly.  Measured on the GQA decode (248 row-head items, up to
+// 8192 keys): 992 workgroups of 2048 keys match 3968 of 512 over a 16-bit cache and are
+// 10-20% faster over 8-bit caches, whose shorter byte streams leave more of the time to
+// per-workgroup set-up and partial states.  Selected and local-plus-aux rows run fastest at
+// one workgroup per item and key range (the split length doubles until the plan has at
+// most this many): 512 workgroups of 2048 selected keys need no merge at all.
 constexpr int kTargetWorkgroupsPaged = 1024;
+constexpr int kTargetWorkgroupsPagedFp8 = 768;
 constexpr int kTargetWorkgroupsSparse = 512;
 constexpr int kMetaLdsMax = 512;   // cu entries staged in LDS (more: binary search in memory)
 static_assert(kStepMaxB + 1 <= kThreads, "a fused step stages one boundary per thread");
@@ -1056,8 +1059,8 @@ bool use_prefill_path(int kind, int dtype, int max_q) {
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_k, int max_sel,
-                          int window, int H_q, int H_kv, int D) {
+SplitPlan make_split_plan(int kind, int dtype, int cache_dtype, int B, int T, int max_q,
+                          int max_k, int max_sel, int window, int H_q, int H_kv, int D) {
   (void)B; (void)max_q;
   SplitPlan pl{};
   const int group = H_q / H_kv;
@@ -1076,12 +1079,27 @@ SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_
     long s = (n_main + ch - 1) / ch + (n_aux + ch - 1) / ch;
     return std::max(1L, s);
   };
-  const long target = kind == SPATTN_KIND_PAGED ? kTargetWorkgroupsPaged : kTargetWorkgroupsSparse;
-  while (chunk < kMaxChunk && chunk < total && items * splits_for(chunk) > target) chunk *= 2;
-  while (splits_for(chunk) > kMaxSplits && chunk < kChunkCap) chunk *= 2;
-  if (splits_for(chunk) > kMaxSplits) {  // key range too long for one call
-    pl.n_splits = -1;
-    return pl;
+  if (kind == SPATTN_KIND_PAGED && !f32) {
+    // as many equal splits per item as fill the target, each of kWgStep .. kChunkCap keys
+    // (a multiple of kWgStep)
+    const long target = cache_dtype == SPATTN_FP8 ? kTargetWorkgroupsPagedFp8 : kTargetWorkgroupsPaged;
+    long s = std::max(1L, target / std::max(1L, items));
+    s = std::min(s, std::max(1L, (n_main + kWgStep - 1) / kWgStep));
+    s = std::max(s, (n_main + kChunkCap - 1) / kChunkCap);
+    if (s > kMaxSplits) {  // key range too long for one call
+      pl.n_splits = -1;
+      return pl;
+    }
+    const long per = (n_main + s - 1) / s;
+    chunk = (int)std::max((long)kWgStep, (per + kWgStep - 1) / kWgStep * kWgStep);
+  } else {
+    const long target = kind == SPATTN_KIND_PAGED ? kTargetWorkgroupsPaged : kTargetWorkgroupsSparse;
+    while (chunk < kMaxChunk && chunk < total && items * splits_for(chunk) > target) chunk *= 2;
+    while (splits_for(chunk) > kMaxSplits && chunk < kChunkCap) chunk *= 2;
+    if (splits_for(chunk) > kMaxSplits) {  // key range too long for one call
+      pl.n_splits = -1;
+      return pl;
+    }
   }
   pl.chunk = chunk;
   pl.n_main = (int)std::max(1L, (n_main + chunk - 1) / chunk);

@@ -74,8 +74,8 @@ struct SplitPlan {
 
 // Prefill (MFMA tile) path is used when true; otherwise the split-K path.
 bool use_prefill_path(int kind, int dtype, int max_q);
-SplitPlan make_split_plan(int kind, int dtype, int B, int T, int max_q, int max_k, int max_sel,
-                          int window, int H_q, int H_kv, int D);
+SplitPlan make_split_plan(int kind, int dtype, int cache_dtype, int B, int T, int max_q,
+                          int max_k, int max_sel, int window, int H_q, int H_kv, int D);
 
 int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t stream);
 int launch_prefill_attention(const AttnArgs& a, hipStream_t stream);
