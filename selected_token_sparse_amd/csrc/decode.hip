@@ -106,6 +106,8 @@ struct SplitParams {
   int64_t aux_row_stride;   // rows (of D elements) between requests in the aux store
   int chunk, n_main, n_splits;
   int row_slots;            // LDS entries of the split's row table (see split_row_slots)
+  int cu_slots;             // > 0: paged splits dealt to CUs by size (see deal_split); the
+                            // CUs one KV head's workgroups spread over
   int meta_lds;             // 1: cu / seqlens_k staged in LDS
   float scale_log2;         // scale * log2(e)
   // Fused decode step (past != nullptr, paged kind, B + 1 <= kThreads): seqlens_k is
@@ -460,6 +462,63 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
   return -1;
 }
 
+// Paged splits dealt to CUs by size.  The workgroups of a launch that fits the GPU are
+// all resident at once, and workgroup i runs on XCD i % 8 and, within it, on CU
+// (i / 8) % 32; a CU streams its workgroups' keys at a rate of its own, so the call lasts
+// as long as the CU with the most keys.  With fixed splits the key counts of the splits
+// sharing a CU follow from the rows' lengths (four long rows' splits can meet on one CU
+// while another gets empty splits).  Instead every workgroup computes all U = n_splits * T
+// split sizes of its KV head from the metadata, ranks them (largest first, ties by
+// index) and takes the split of the rank that a serpentine deal gives its position:
+// position j = (its index among the head's workgroups) sits on CU slot j % cus, round
+// j / cus; even rounds deal ranks in slot order, odd rounds in reverse, so each CU gets one
+// split of each size class.  The partial-state layout does not change.  Needs U <=
+// kThreads and scratch for kThreads + 1 ints.
+template <int KIND>
+__device__ __forceinline__ void deal_split(const SplitParams& P, const int32_t* cu,
+                                           const int32_t* skl, bool step_bad, int* sm,
+                                           int& split, int& r) {
+  const int tid = threadIdx.x;
+  const int U = P.n_splits * P.T;
+  int* s_size = sm;                  // [kThreads]
+  int* s_pick = sm + kThreads;       // [1]
+  int sz = 0;
+  if (tid < U) {
+    const int rr = tid % P.T, ss = tid / P.T;
+    int L = 0;
+    if (!step_bad) {
+      int f = 0;   // each row's own workgroups raise its flags
+      const RowInfo x = resolve_row(cu, skl, P.B, rr, P.max_q, P.max_k, f);
+      if (x.b >= 0) {
+        const int lo = P.window > 0 ? max(0, x.p - P.window + 1) : 0;
+        L = max(0, x.p - lo + 1);
+      }
+    }
+    sz = min(max(L - ss * P.chunk, 0), P.chunk);
+  }
+  if (tid < ((U + 3) & ~3)) s_size[tid] = tid < U ? sz : -1;   // padding ranks last
+  __syncthreads();
+  const int j = blockIdx.x / P.H_kv;
+  const int cus = P.cu_slots;
+  const int R = j / cus, pos = j - R * cus;
+  const int nR = min(cus, U - R * cus);
+  const int k = R * cus + ((R & 1) ? nR - 1 - pos : pos);
+  if (tid < U) {
+    int rank = 0;
+    for (int u = 0; u < U; u += 4) {
+      const i32x4 o = *reinterpret_cast<const i32x4*>(s_size + u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rank += (o[e] > sz) || (o[e] == sz && u + e < tid);
+    }
+    if (rank == k) *s_pick = tid;
+  }
+  __syncthreads();
+  const int unit = __builtin_amdgcn_readfirstlane(*s_pick);   // (uniform: one writer)
+  split = unit / P.T;
+  r = unit - split * P.T;
+  __syncthreads();                   // the scratch is free again
+}
+
 // Per-request metadata of a workgroup, staged in LDS (`meta`, 2 B + 1 ints) when `to_lds`.
 // Fused decode step (kStep), one load round and one barrier: meta[0..B] = cu,
 // meta[B+1+b] = past[b] + q_len_b - 1 (seqlens_k, as prepare_seqlens derives it for
@@ -724,23 +783,27 @@ void split_attn_kernel(SplitParams P) {
 
   const int hkt = P.H_kv * P.head_tiles;
   const int per_split = P.T * hkt;
-  const int split = blockIdx.x / per_split;
+  int split = blockIdx.x / per_split;
   const int rem = blockIdx.x - split * per_split;
-  const int r = rem / hkt;
+  int r = rem / hkt;
   const int kvt = rem - r * hkt;
   const int c = kvt / P.head_tiles;
   const int ht = kvt - c * P.head_tiles;
   const int h0 = c * P.group + ht * 16;                 // first query head of the tile
   const int nh = min(16, P.group - ht * 16);            // heads in the tile
+  const bool dealt = KIND == SPATTN_KIND_PAGED && P.cu_slots > 0;
 
-  // the query rows depend on the grid position only: their loads overlap the prologue
+  // the query rows: without the deal they depend on the grid position only and load
+  // under the metadata round
   const bool hv = lam < nh;
-  const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0 + (hv ? lam : 0)) * D;
-  const QT* q0row = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0) * D;
   i32x4 qraw[D / 32];
+  auto load_query = [&]() {
+    const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0 + (hv ? lam : 0)) * D;
 #pragma unroll
-  for (int kc = 0; kc < D / 32; ++kc)
-    qraw[kc] = hv ? load16(qrow + kc * 32 + grp * 8) : i32x4{0, 0, 0, 0};
+    for (int kc = 0; kc < D / 32; ++kc)
+      qraw[kc] = hv ? load16(qrow + kc * 32 + grp * 8) : i32x4{0, 0, 0, 0};
+  };
+  if (!dealt) load_query();
 
   // ---- 1. the row's request and position ----
   const int32_t* cu = P.cu;
@@ -748,6 +811,12 @@ void split_attn_kernel(SplitParams P) {
   __shared__ int wave_flags[kWaves];
   // fused step: malformed metadata
   const bool step_bad = stage_metadata<kStep>(P, meta, P.meta_lds != 0, cu, skl);
+  if (dealt) {
+    deal_split<KIND>(P, cu, skl, step_bad, reinterpret_cast<int*>(area), split, r);
+    load_query();
+  }
+  const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0 + (hv ? lam : 0)) * D;
+  const QT* q0row = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0) * D;
   int flags = 0;
   RowInfo ri;
   if (step_bad) {
@@ -1189,6 +1258,15 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   P.aux_row_stride = a.aux_stride / a.D;
   P.chunk = plan.chunk; P.n_main = plan.n_main; P.n_splits = plan.n_splits;
   P.row_slots = split_row_slots(a.kind, plan.chunk, a.block_table != nullptr, a.block_size);
+  // the deal of paged splits to CUs: 16-bit caches (measured on the decode workload: f16
+  // call 71.2 -> 65.6 us; over INT8 / FP8 caches, whose streams are half as long, the
+  // deal's prologue cost more than it gained: 42.2 -> 43.6 and 42.0 -> 45.6 us), one head
+  // tile, 8 XCDs of 32 CUs shared evenly by the KV heads, every split of a head ranked by
+  // one thread
+  P.cu_slots = 0;
+  if (a.kind == SPATTN_KIND_PAGED && a.dtype != SPATTN_F32 && a.cache_dtype == a.dtype &&
+      plan.head_tiles == 1 && 8 % a.H_kv == 0 && (long)plan.n_splits * a.T <= kThreads)
+    P.cu_slots = 32 * (8 / a.H_kv);
   P.meta_lds = a.B + 1 <= kMetaLdsMax ? 1 : 0;
   P.scale_log2 = a.scale * kLog2e;
   P.past = a.past; P.k_new = a.k_new; P.v_new = a.v_new; P.committed = a.committed;
