@@ -462,13 +462,15 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
   return -1;
 }
 
-// Paged splits dealt to CUs by size.  The workgroups of a launch that fits the GPU are
+// Splits dealt to CUs by size (paged ranges and selected rows).  The workgroups of a launch
+// that fits the GPU are
 // all resident at once, and workgroup i runs on XCD i % 8 and, within it, on CU
 // (i / 8) % 32; a CU streams its workgroups' keys at a rate of its own, so the call lasts
 // as long as the CU with the most keys.  With fixed splits the key counts of the splits
 // sharing a CU follow from the rows' lengths (four long rows' splits can meet on one CU
-// while another gets empty splits).  Instead every workgroup computes all U = n_splits * T
-// split sizes of its KV head from the metadata, ranks them (largest first, ties by
+// while another gets empty splits; selected rows' counts vary the same way).  Instead
+// every workgroup computes all U = n_splits * T split sizes of its KV head (paged: from
+// the metadata; selected: from the per-row counts), ranks them (largest first, ties by
 // index) and takes the split of the rank that a serpentine deal gives its position:
 // position j = (its index among the head's workgroups) sits on CU slot j % cus, round
 // j / cus; even rounds deal ranks in slot order, odd rounds in reverse, so each CU gets one
@@ -476,7 +478,7 @@ __device__ __forceinline__ int split_key_row(const SplitParams& P, const SplitRa
 // kThreads and scratch for kThreads + 1 ints.
 template <int KIND>
 __device__ __forceinline__ void deal_split(const SplitParams& P, const int32_t* cu,
-                                           const int32_t* skl, bool step_bad, int* sm,
+                                           const int32_t* skl, bool step_bad, int c, int* sm,
                                            int& split, int& r) {
   const int tid = threadIdx.x;
   const int U = P.n_splits * P.T;
@@ -486,7 +488,12 @@ __device__ __forceinline__ void deal_split(const SplitParams& P, const int32_t* 
   if (tid < U) {
     const int rr = tid % P.T, ss = tid / P.T;
     int L = 0;
-    if (!step_bad) {
+    if constexpr (KIND == SPATTN_KIND_SELECTED) {
+      // the row's count as split_range reads it (a dead row's splits are empty, but are
+      // ranked by their count: only the deal's balance depends on it)
+      L = P.sel_count != nullptr ? min(max(P.sel_count[(int64_t)rr * P.H_kv + c], 0), P.max_sel)
+                                 : P.max_sel;
+    } else if (!step_bad) {
       int f = 0;   // each row's own workgroups raise its flags
       const RowInfo x = resolve_row(cu, skl, P.B, rr, P.max_q, P.max_k, f);
       if (x.b >= 0) {
@@ -791,7 +798,7 @@ void split_attn_kernel(SplitParams P) {
   const int ht = kvt - c * P.head_tiles;
   const int h0 = c * P.group + ht * 16;                 // first query head of the tile
   const int nh = min(16, P.group - ht * 16);            // heads in the tile
-  const bool dealt = KIND == SPATTN_KIND_PAGED && P.cu_slots > 0;
+  const bool dealt = KIND != SPATTN_KIND_LOCAL_AUX && P.cu_slots > 0;
 
   // the query rows: without the deal they depend on the grid position only and load
   // under the metadata round
@@ -812,7 +819,7 @@ void split_attn_kernel(SplitParams P) {
   // fused step: malformed metadata
   const bool step_bad = stage_metadata<kStep>(P, meta, P.meta_lds != 0, cu, skl);
   if (dealt) {
-    deal_split<KIND>(P, cu, skl, step_bad, reinterpret_cast<int*>(area), split, r);
+    deal_split<KIND>(P, cu, skl, step_bad, c, reinterpret_cast<int*>(area), split, r);
     load_query();
   }
   const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0 + (hv ? lam : 0)) * D;
@@ -1264,8 +1271,9 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   // tile, 8 XCDs of 32 CUs shared evenly by the KV heads, every split of a head ranked by
   // one thread
   P.cu_slots = 0;
-  if (a.kind == SPATTN_KIND_PAGED && a.dtype != SPATTN_F32 && a.cache_dtype == a.dtype &&
-      plan.head_tiles == 1 && 8 % a.H_kv == 0 && (long)plan.n_splits * a.T <= kThreads)
+  if ((a.kind == SPATTN_KIND_PAGED || a.kind == SPATTN_KIND_SELECTED) && a.dtype != SPATTN_F32 &&
+      a.cache_dtype == a.dtype && plan.head_tiles == 1 && 8 % a.H_kv == 0 &&
+      (long)plan.n_splits * a.T <= kThreads)
     P.cu_slots = 32 * (8 / a.H_kv);
   P.meta_lds = a.B + 1 <= kMetaLdsMax ? 1 : 0;
   P.scale_log2 = a.scale * kLog2e;
