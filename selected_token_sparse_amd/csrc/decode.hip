@@ -503,7 +503,9 @@ __device__ __forceinline__ void deal_split(const SplitParams& P, const int32_t* 
     }
     sz = min(max(L - ss * P.chunk, 0), P.chunk);
   }
-  if (tid < ((U + 3) & ~3)) s_size[tid] = tid < U ? sz : -1;   // padding ranks last
+  // one sort key per split: the size, ties by index (sizes <= kChunkCap, U <= 512)
+  const int key = sz * 512 + (511 - tid);
+  if (tid < ((U + 3) & ~3)) s_size[tid] = tid < U ? key : -1;   // padding ranks last
   __syncthreads();
   const int j = blockIdx.x / P.H_kv;
   const int cus = P.cu_slots;
@@ -511,11 +513,11 @@ __device__ __forceinline__ void deal_split(const SplitParams& P, const int32_t* 
   const int nR = min(cus, U - R * cus);
   const int k = R * cus + ((R & 1) ? nR - 1 - pos : pos);
   if (tid < U) {
-    int rank = 0;
+    int rank = 0;                    // splits with a larger key
     for (int u = 0; u < U; u += 4) {
       const i32x4 o = *reinterpret_cast<const i32x4*>(s_size + u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rank += (o[e] > sz) || (o[e] == sz && u + e < tid);
+      for (int e = 0; e < 4; ++e) rank += o[e] > key ? 1 : 0;
     }
     if (rank == k) *s_pick = tid;
   }
