@@ -1267,15 +1267,13 @@ int launch_split_attention(const AttnArgs& a, const SplitPlan& plan, hipStream_t
   P.aux_row_stride = a.aux_stride / a.D;
   P.chunk = plan.chunk; P.n_main = plan.n_main; P.n_splits = plan.n_splits;
   P.row_slots = split_row_slots(a.kind, plan.chunk, a.block_table != nullptr, a.block_size);
-  // the deal of paged splits to CUs: 16-bit caches (measured on the decode workload: f16
-  // call 71.2 -> 65.6 us; over INT8 / FP8 caches, whose streams are half as long, the
-  // deal's prologue cost more than it gained: 42.2 -> 43.6 and 42.0 -> 45.6 us), one head
-  // tile, 8 XCDs of 32 CUs shared evenly by the KV heads, every split of a head ranked by
-  // one thread
+  // the deal of splits to CUs (paged ranges and selected rows): one head tile, 8 XCDs of
+  // 32 CUs shared evenly by the KV heads, every split of a head ranked by one thread.
+  // Measured on the decode workload: f16 call 71.2 -> 62.7 us, INT8 cache 42.4 -> 40.1,
+  // FP8 unchanged; selected grouped decode 80.2 -> 63.9 us.
   P.cu_slots = 0;
   if ((a.kind == SPATTN_KIND_PAGED || a.kind == SPATTN_KIND_SELECTED) && a.dtype != SPATTN_F32 &&
-      a.cache_dtype == a.dtype && plan.head_tiles == 1 && 8 % a.H_kv == 0 &&
-      (long)plan.n_splits * a.T <= kThreads)
+      plan.head_tiles == 1 && 8 % a.H_kv == 0 && (long)plan.n_splits * a.T <= kThreads)
     P.cu_slots = 32 * (8 / a.H_kv);
   P.meta_lds = a.B + 1 <= kMetaLdsMax ? 1 : 0;
   P.scale_log2 = a.scale * kLog2e;
