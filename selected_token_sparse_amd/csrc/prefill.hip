@@ -774,37 +774,67 @@ void prefill_window_kernel(PrefillParams P) {
   };
   V8 qop[KC];
   if (wave < P.group) load_q(wave, qop);
+  // Block ids: with a power-of-two block size of at least the 64 / CHK keys one DMA
+  // instruction covers, an instruction's keys lie in at most two blocks, whose ids are read
+  // by scalar loads (the table is read-only here): the DMAs of the span then go out back to
+  // back, with no wait for a vector load between them (each such wait would also wait for
+  // the DMAs and query loads already in flight).  Other block sizes read ids per lane.
+  constexpr int kKeysPerInst = 64 / CHK;
+  const bool scalar_ids = paged && P.cd.bs_shift >= 0 && (1 << P.cd.bs_shift) >= kKeysPerInst;
+  const __attribute__((address_space(4))) int32_t* ctable =
+      (const __attribute__((address_space(4))) int32_t*)table;
   bool all_ok = true;
-  for (int q = wave; q < n_tiles * IPT; q += NW) {
-    const int t = q / IPT;
-    const int pos = (q - t * IPT) * 64 + lane;
-    const int kk = pos / CHK, slot = pos - kk * CHK;
-    const int col = (slot ^ pf_swizzle<D>(kk)) * 8;
-    const int j = j_lo + t * kPfTile + kk;
-    bool ok = j <= j_hi;
-    int64_t row = 0;
-    if (ok) {
-      if (paged) {
-        const int lb = P.cd.bs_shift >= 0 ? j >> P.cd.bs_shift : j / bs;
-        const int blk = lb < P.cd.max_blocks ? table[lb] : -1;
-        if (lb >= P.cd.max_blocks) flags |= SPATTN_STATUS_CAPACITY;
-        else if (blk < 0 || blk >= P.cd.num_blocks) flags |= SPATTN_STATUS_BAD_BLOCK;
-        ok = lb < P.cd.max_blocks && blk >= 0 && blk < P.cd.num_blocks;
-        row = (((int64_t)blk * P.cd.H_kv + c) * bs + (j - lb * bs));
-      } else {
-        ok = j < bs && b < P.cd.num_blocks;
-        if (!ok) flags |= SPATTN_STATUS_CAPACITY;
-        row = ((int64_t)b * P.cd.H_kv + c) * bs + j;
+  auto span_dma = [&](auto scalar_tag) {
+    constexpr bool kScalar = decltype(scalar_tag)::value;
+    for (int q = wave; q < n_tiles * IPT; q += NW) {
+      const int t = q / IPT;
+      const int pos = (q - t * IPT) * 64 + lane;
+      const int kk = pos / CHK, slot = pos - kk * CHK;
+      const int col = (slot ^ pf_swizzle<D>(kk)) * 8;
+      const int j = j_lo + t * kPfTile + kk;
+      bool ok = j <= j_hi;
+      int64_t row = 0;
+      int blk_a = -1, blk_b = -1, lb_a = 0;
+      if constexpr (kScalar) {
+        const int ja = j_lo + t * kPfTile + (q - t * IPT) * kKeysPerInst;   // (uniform)
+        lb_a = ja >> P.cd.bs_shift;
+        const int lb_b = (ja + kKeysPerInst - 1) >> P.cd.bs_shift;
+        blk_a = lb_a < P.cd.max_blocks ? ctable[__builtin_amdgcn_readfirstlane(lb_a)] : -1;
+        blk_b = lb_b == lb_a ? blk_a
+                             : lb_b < P.cd.max_blocks ? ctable[__builtin_amdgcn_readfirstlane(lb_b)] : -1;
       }
+      if (ok) {
+        if (paged) {
+          const int lb = P.cd.bs_shift >= 0 ? j >> P.cd.bs_shift : j / bs;
+          const int blk = kScalar ? (lb == lb_a ? blk_a : blk_b)
+                                  : lb < P.cd.max_blocks ? table[lb] : -1;
+          if (lb >= P.cd.max_blocks) flags |= SPATTN_STATUS_CAPACITY;
+          else if (blk < 0 || blk >= P.cd.num_blocks) flags |= SPATTN_STATUS_BAD_BLOCK;
+          ok = lb < P.cd.max_blocks && blk >= 0 && blk < P.cd.num_blocks;
+          row = (((int64_t)blk * P.cd.H_kv + c) * bs + (j - lb * bs));
+        } else {
+          ok = j < bs && b < P.cd.num_blocks;
+          if (!ok) flags |= SPATTN_STATUS_CAPACITY;
+          row = ((int64_t)b * P.cd.H_kv + c) * bs + j;
+        }
+      }
+      // a missing key reads a finite row (the block's first query row); its weight is 0
+      const QT* kp = ok ? kcache + row * D + col : safe + col;
+      const QT* vp = ok ? vcache + row * D + col : safe + col;
+      pf_dma16(kp, smem + t * L::kTileBytes + (q - t * IPT) * 1024);
+      pf_dma16(vp, smem + L::kVOff + t * L::kTileBytes + (q - t * IPT) * 1024);
+      if (slot == 0) key_ok[t * kPfTile + kk] = ok ? 1 : 0;
+      all_ok = all_ok && (ok || j > j_hi);
     }
-    // a missing key reads a finite row (the block's first query row); its weight is 0
-    const QT* kp = ok ? kcache + row * D + col : safe + col;
-    const QT* vp = ok ? vcache + row * D + col : safe + col;
-    pf_dma16(kp, smem + t * L::kTileBytes + (q - t * IPT) * 1024);
-    pf_dma16(vp, smem + L::kVOff + t * L::kTileBytes + (q - t * IPT) * 1024);
-    if (slot == 0) key_ok[t * kPfTile + kk] = ok ? 1 : 0;
-    all_ok = all_ok && (ok || j > j_hi);
-  }
+  };
+  if (scalar_ids) span_dma(std::true_type{});
+  else span_dma(std::false_type{});
+  // the sink of this wave's first head, by a scalar load (read-only here) issued while the
+  // span is in flight instead of at the finalisation
+  const __attribute__((address_space(4))) float* csinks =
+      (const __attribute__((address_space(4))) float*)P.sinks;
+  const float sink_first = P.sinks != nullptr && wave < P.group
+      ? csinks[__builtin_amdgcn_readfirstlane(c * P.group + wave)] : kNegInf;
   pf_wait_vm<0>();
   const bool span_ok = __syncthreads_or(!all_ok) == 0;   // every key of the span exists
 
@@ -858,7 +888,8 @@ void prefill_window_kernel(PrefillParams P) {
       float f = 0.f, inv = 0.f;
       if (m_run != kNegInf) {
         const float ms = m_run * c_scale;
-        const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
+        const float sraw = hh == wave ? sink_first : P.sinks != nullptr ? P.sinks[head] : 0.f;
+        const float sg = P.sinks != nullptr ? sraw * kLog2e : kNegInf;
         const float M2 = fmaxf(ms, sg);
         f = exp2_safe(ms - M2);
         inv = f / (l_run * f + exp2_safe(sg - M2));
