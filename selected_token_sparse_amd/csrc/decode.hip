@@ -624,18 +624,24 @@ __device__ __forceinline__ void step_write_keys(const SplitParams& P, int b, int
     const bool is_v = rest >= kPieces;
     const int d = (is_v ? rest - kPieces : rest) * 8;
     const int j = j0 + key;
-    const int row = cache_row_index(P.cd, b, j, c, flags);
-    if (row < 0) continue;
     const QT* src = reinterpret_cast<const QT*>(is_v ? P.v_new : P.k_new) +
                     ((int64_t)(c0 + j - first_new) * P.H_kv + c) * D + d;
+    // the new row's piece loads before the block-id lookup, so the two loads overlap
+    const i32x4 raw = load16(src);
+    const int row = cache_row_index(P.cd, b, j, c, flags);
+    if (row < 0) continue;
     // the cache arguments are read-only everywhere else in this kernel
     void* cache = const_cast<void*>(is_v ? P.v_cache : P.k_cache);
     if constexpr (sizeof(KT) == 1) {
+      const typename OpVec<QT>::v8 x = __builtin_bit_cast(typename OpVec<QT>::v8, raw);
+      QT piece[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) piece[e] = x[e];
       quantize8<std::is_same<KT, uint8_t>::value>(
-          src, (is_v ? P.value_scale : P.key_scale) + c * D + d,
+          piece, (is_v ? P.value_scale : P.key_scale) + c * D + d,
           reinterpret_cast<int8_t*>(cache) + (int64_t)row * D + d);
     } else {
-      store16(reinterpret_cast<KT*>(cache) + (int64_t)row * D + d, load16(src));
+      store16(reinterpret_cast<KT*>(cache) + (int64_t)row * D + d, raw);
     }
   }
 }
@@ -646,7 +652,7 @@ __device__ __forceinline__ void step_write_keys(const SplitParams& P, int b, int
 // each, so the scores keep about 22 bits of x instead of 11: a single 16-bit operand would
 // put a relative error of 2^-11 on every term q_d k_d, i.e. score errors up to
 // 2^-11 sum_d |q_d k_d|.  `qraw` holds this lane's query dims as loaded (16-bit caches);
-// lanes with hv false carry a zero query.
+// lanes with hv false loaded the tile's first head and carry a zero query.
 template <typename QT, typename KT, int D, typename RowAt>
 __device__ __forceinline__ void main_cache_keys(const SplitParams& P, const QT* qrow,
                                                 const QT* q0row, bool hv,
@@ -672,7 +678,7 @@ __device__ __forceinline__ void main_cache_keys(const SplitParams& P, const QT* 
         qop[1][kc][e] = (OpM)(x - (float)hi);
       }
     } else {
-      qop[0][kc] = __builtin_bit_cast(typename OpVec<OpM>::v8, qraw[kc]);
+      qop[0][kc] = __builtin_bit_cast(typename OpVec<OpM>::v8, hv ? qraw[kc] : i32x4{0, 0, 0, 0});
       qop[1][kc] = typename OpVec<OpM>::v8{};
     }
   }
@@ -810,7 +816,7 @@ void split_attn_kernel(SplitParams P) {
     const QT* qrow = reinterpret_cast<const QT*>(P.q) + ((int64_t)r * P.H_q + h0 + (hv ? lam : 0)) * D;
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc)
-      qraw[kc] = hv ? load16(qrow + kc * 32 + grp * 8) : i32x4{0, 0, 0, 0};
+      qraw[kc] = load16(qrow + kc * 32 + grp * 8);
   };
   if (!dealt) load_query();
 
@@ -921,7 +927,7 @@ void split_attn_kernel(SplitParams P) {
       typename OpVec<OpA>::v8 qop[2][D / 32];
 #pragma unroll
       for (int kc = 0; kc < D / 32; ++kc) {
-        qop[0][kc] = __builtin_bit_cast(typename OpVec<OpA>::v8, qraw[kc]);
+        qop[0][kc] = __builtin_bit_cast(typename OpVec<OpA>::v8, hv ? qraw[kc] : i32x4{0, 0, 0, 0});
         qop[1][kc] = typename OpVec<OpA>::v8{};
       }
       wave_keys<OpA, AT, D>(reinterpret_cast<const AT*>(P.aux_k),
