@@ -76,6 +76,26 @@ template <> __device__ __forceinline__ void load8<float>(const float* p, float (
 #pragma unroll
   for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
 }
+// the same, split into the load and the conversion, so that the loads can stay in flight
+// across the metadata lookups (a conversion right after a load waits for it)
+struct Raw8 { i32x4 a, b; };
+template <typename T> __device__ __forceinline__ Raw8 load_raw8(const T* p) {
+  Raw8 r;
+  r.a = load16(p);
+  r.b = sizeof(T) == 4 ? load16(p + 16 / sizeof(T)) : i32x4{0, 0, 0, 0};
+  return r;
+}
+template <typename T> __device__ __forceinline__ void convert8(const Raw8& r, float (&x)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    const f32x4 a = __builtin_bit_cast(f32x4, r.a), b = __builtin_bit_cast(f32x4, r.b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+  } else {
+    const T* e = reinterpret_cast<const T*>(&r.a);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = to_f32(e[i]);
+  }
+}
 template <typename T> __device__ __forceinline__ void store8(T* p, const float (&x)[8]) {
   i32x4 r;
   T* e = reinterpret_cast<T*>(&r);
@@ -111,7 +131,7 @@ __global__ __launch_bounds__(kProThreads) void qkv_prologue_kernel(PrologueParam
   __shared__ float rowbuf[kProWaves][64 * 8];   // each lane's 8 channels, row after row
   __shared__ float partial[kProWaves][64];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // (uniform: scalar)
   const int G = P.G;
   const int gi = lane / G;                      // row slot of this lane in a batch
   const int li = lane - gi * G;                 // lane within the row's group
@@ -125,7 +145,10 @@ __global__ __launch_bounds__(kProThreads) void qkv_prologue_kernel(PrologueParam
   const int base = (int)(r0 - (int64_t)t_first * NH);   // r0's head index in its token
 
   // phase 1: which rows, and their source loads (independent of any metadata)
+  // (every lane loads: an inactive lane reads the wave's first row, so no register is
+  // cleared while a load is in flight; the loaded bits are converted after the metadata)
   ProRow R[ITER];
+  Raw8 raw[ITER];
   float x[ITER][8];
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
@@ -137,16 +160,12 @@ __global__ __launch_bounds__(kProThreads) void qkv_prologue_kernel(PrologueParam
     r.active = slot_ok && r0 + k < P.n_rows;
     r.kind = r.task < P.H_q ? 0 : (r.task < P.H_q + P.H_kv ? 1 : 2);   // Q, K, V
     r.head = r.kind == 0 ? r.task : (r.kind == 1 ? r.task - P.H_q : r.task - P.H_q - P.H_kv);
-    if (r.active) {
-      const T* src;
-      if (P.qkv != nullptr) src = reinterpret_cast<const T*>(P.qkv) + (r0 + k) * D;
-      else if (r.kind == 0) src = reinterpret_cast<const T*>(P.q) + ((int64_t)r.t * P.H_q + r.head) * D;
-      else src = reinterpret_cast<const T*>(r.kind == 1 ? P.k : P.v) + ((int64_t)r.t * P.H_kv + r.head) * D;
-      load8<T>(src + d0, x[it]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[it][e] = 0.f;
-    }
+    const T* src;
+    if (!r.active) src = reinterpret_cast<const T*>(P.qkv != nullptr ? P.qkv : P.q) + (P.qkv != nullptr ? r0 * D : 0);
+    else if (P.qkv != nullptr) src = reinterpret_cast<const T*>(P.qkv) + (r0 + k) * D;
+    else if (r.kind == 0) src = reinterpret_cast<const T*>(P.q) + ((int64_t)r.t * P.H_q + r.head) * D;
+    else src = reinterpret_cast<const T*>(r.kind == 1 ? P.k : P.v) + ((int64_t)r.t * P.H_kv + r.head) * D;
+    raw[it] = load_raw8<T>(src + d0);
   }
 
   // phase 2: token metadata, lane j for the wave's token j
@@ -155,7 +174,53 @@ __global__ __launch_bounds__(kProThreads) void qkv_prologue_kernel(PrologueParam
   {
     const int last = (int)((min(r0 + (int64_t)ITER * P.rows_per_wave, P.n_rows) - 1) / NH);
     const int tj = t_first + lane;
-    if (tj <= last) {
+    // The request of the wave's first and of its last token, by a binary search with
+    // scalar loads (the metadata is read-only here, and waiting for a scalar load never
+    // waits for the row loads in flight).  When both give request b, every token between
+    // them does too: the search for each of them takes the same comparisons (whatever the
+    // order of cu), so the request's lengths, offset and cursor are read once, by scalar
+    // loads, instead of by a chain of vector loads per lane.
+    typedef const __attribute__((address_space(4))) int32_t* CI;
+    const CI ccu = (CI)P.cu;
+    auto find_uniform = [&](int r) {
+      int lo = 0, hi = P.B - 1;
+      if (P.B <= 0 || ccu[0] > r) return -1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ccu[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      return r < ccu[lo + 1] ? lo : -1;
+    };
+    const int b_first = find_uniform(t_first);
+    const bool one_request = b_first >= 0 && find_uniform(last) == b_first;
+    int ub_c0 = 0, ub_qlen = 0, ub_kvlen = 0, ub_off = 0;
+    bool ub_cursor_bad = false;
+    if (one_request) {
+      ub_c0 = ccu[b_first];
+      ub_qlen = ccu[b_first + 1] - ub_c0;
+      ub_kvlen = ((CI)P.seqlens_k)[b_first] + 1;
+      ub_off = P.rotary_offsets != nullptr ? ((CI)P.rotary_offsets)[b_first] : 0;
+      ub_cursor_bad = P.committed != nullptr && ((CI)P.committed)[b_first] != ub_kvlen - ub_qlen;
+    }
+    if (tj <= last && one_request) {
+      int flags = 0;
+      const int b = b_first;
+      const int q_len = ub_qlen;
+      const int kv_len = ub_kvlen;
+      const int p = kv_len - q_len + (tj - ub_c0);
+      bool pos_ok = true;
+      if (P.rotary_dim > 0) {
+        m_pos = (P.position_ids != nullptr ? P.position_ids[tj] : p) + ub_off;
+        if (m_pos < 0 || m_pos >= P.max_position) { pos_ok = false; flags |= SPATTN_STATUS_POSITION; }
+      }
+      if (pos_ok) m_state |= 1;
+      if (ub_cursor_bad) flags |= SPATTN_STATUS_CURSOR;
+      else if (!pos_ok) {}
+      else if (p < 0) flags |= SPATTN_STATUS_SHORT_KV;
+      else m_dst = cache_row(P.cd, b, p, 0, flags);
+      if (m_dst >= 0) m_state |= 2;
+      raise_status(P.status, flags);           // a token split over two waves reports twice
+    } else if (tj <= last) {
       int flags = 0;
       const int b = find_request(P.cu, P.B, tj);
       if (b < 0) {
@@ -193,6 +258,7 @@ __global__ __launch_bounds__(kProThreads) void qkv_prologue_kernel(PrologueParam
     r.dst = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
     r.append_ok = r.active && r.kind != 0 && (st & 2) != 0;
     r.compute = r.active && (r.kind == 0 ? (st & 1) != 0 : r.append_ok);
+    convert8<T>(raw[it], x[it]);
     if (!r.compute) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[it][e] = 0.f;   // rows of no request or position: zero queries
