@@ -167,6 +167,17 @@ __global__ __launch_bounds__(kProThreads) void qkv_prologue_kernel(PrologueParam
     else src = reinterpret_cast<const T*>(r.kind == 1 ? P.k : P.v) + ((int64_t)r.t * P.H_kv + r.head) * D;
     raw[it] = load_raw8<T>(src + d0);
   }
+  // the norm weight of each row's kind depends on no metadata: it loads with the rows
+  const float* w_any = P.q_norm_weight != nullptr ? P.q_norm_weight : P.k_norm_weight;
+  const bool pre_w = P.qk_norm && w_any != nullptr;
+  Raw8 wraw[ITER];
+  if (pre_w) {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const float* w = R[it].kind == 0 ? P.q_norm_weight : P.k_norm_weight;
+      wraw[it] = load_raw8<float>((w != nullptr ? w : w_any) + d0);
+    }
+  }
 
   // phase 2: token metadata, lane j for the wave's token j
   int m_state = 0, m_pos = 0;                   // state: 1 = queries computed, 2 = K/V appended
@@ -293,7 +304,7 @@ __global__ __launch_bounds__(kProThreads) void qkv_prologue_kernel(PrologueParam
         const float* w = r.kind == 0 ? P.q_norm_weight : P.k_norm_weight;
         if (w != nullptr) {
           float wv[8];
-          load8<float>(w + d0, wv);
+          convert8<float>(wraw[it], wv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) xv[e] = xv[e] * inv * wv[e];
         } else {
