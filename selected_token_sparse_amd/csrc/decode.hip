@@ -969,11 +969,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
   if (pair >= T * H_q) return;
   const int head = pair % H_q;
   const int64_t stride = (int64_t)T * H_q;
+  // the sink, loaded before the partial states: loads complete in order, so the waits for
+  // the states cover it (loaded after them, it cost a round trip of its own at the end).
+  // Every lane loads (a workspace word when there are no sinks, unused), so no register is
+  // cleared while the load is in flight.
+  const float sink_raw = *(sinks != nullptr ? sinks + head : reinterpret_cast<const float*>(ws_ml));
   float M = kNegInf, L = 0.f;   // running reference maximum and normaliser
   float A[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) A[e] = 0.f;
-  for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+  // one batch (the first is peeled from the loop: a call with at most kBatch splits then has
+  // no loop, whose back edge would make the compiler wait for the sink before the first
+  // batch's loads)
+  auto batch = [&](int s0) {
     float2 ml[kBatch];
     float a[kBatch][PER];
 #pragma unroll
@@ -995,7 +1003,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
       if (s0 + k < n_splits) Mb = fmaxf(Mb, ml[k].x);
-    if (Mb == kNegInf) continue;                  // nothing visible yet
+    if (Mb == kNegInf) return;                    // nothing visible yet
     const float r = M == kNegInf ? 0.f : exp2_safe(M - Mb);
     L *= r;
 #pragma unroll
@@ -1009,10 +1017,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
       for (int e = 0; e < PER; ++e) A[e] += live ? a[k][e] * f : 0.f;
     }
     M = Mb;
-  }
-  // the sink joins the maximum and the normaliser only (read last, so that its load is in
-  // flight with the others); no visible key (A = 0): zeros
-  const float sg = sinks != nullptr ? sinks[head] * kLog2e : kNegInf;
+  };
+  if (n_splits > 0) batch(0);
+  for (int s0 = kBatch; s0 < n_splits; s0 += kBatch) batch(s0);
+  // the sink joins the maximum and the normaliser only; no visible key (A = 0): zeros
+  const float sg = sinks != nullptr ? sink_raw * kLog2e : kNegInf;
   const float Mf = fmaxf(M, sg);
   float Lt = 0.f;
   if (Mf != kNegInf) {
