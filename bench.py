@@ -41,8 +41,8 @@ METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), GQA paged
 # WRITE_SIZE counter passes scaled by the same counters' reading on a plain device copy of
 # known size (profiles/decode_gqa_paged_f16_traffic.md).  Valid only for the kernel sources
 # whose digest is recorded with it; any other source reports traffic = null.
-MEASURED_TRAFFIC = {"sources_sha1": "517f1c224aeb23478edb98fc2c1fa690d097c01a",
-                    "bytes_per_call": 278377875}
+MEASURED_TRAFFIC = {"sources_sha1": "45ff4aabb1b04412e83b69e250adef8a36a0ecc9",
+                    "bytes_per_call": 278401400}
 KERNEL_SOURCES = ("selected_token_sparse_amd/csrc/decode.hip", "selected_token_sparse_amd/csrc/common.h",
                   "selected_token_sparse_amd/csrc/launch.h", "selected_token_sparse_amd/csrc/append.h")
 
