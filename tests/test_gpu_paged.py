@@ -92,6 +92,11 @@ PREFILL = [
     # contiguous per-request caches [B, H_kv, capacity, D] (no block table): fresh prompts
     # and chunked prefill (rows appended after a history), with and without a window
     ("f16_contig_w64", dict(kv_lens=[300, 97, 160], q_lens=[300, 97, 40], H_q=16, H_kv=2, D=64, dtype=synth.F16, contiguous=True, capacity=320, sinks=True, local_window=64)),
+    # the windowed span kernel's block ids: read per lane for a block size that is not a
+    # power of two of at least 8 (5, 4), by scalar loads otherwise (32, with D = 128)
+    ("f16_w96_bs5", dict(kv_lens=[150, 61, 230], q_lens=[150, 40, 100], H_q=16, H_kv=2, D=64, dtype=synth.F16, block_size=5, sinks=True, local_window=96)),
+    ("f16_w40_bs4_g4", dict(kv_lens=[130, 77], q_lens=[130, 60], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=4, local_window=40)),
+    ("bf16_w128_bs32_d128", dict(kv_lens=[300, 45], q_lens=[260, 45], H_q=16, H_kv=2, D=128, dtype=synth.BF16, block_size=32, sinks=True, local_window=128)),
     ("f16_contig_causal_chunked", dict(kv_lens=[500, 200, 33], q_lens=[120, 200, 9], H_q=8, H_kv=2, D=64, dtype=synth.F16, contiguous=True, capacity=512)),
     ("bf16_contig_d128_chunked_sink", dict(kv_lens=[260, 70], q_lens=[100, 70], H_q=8, H_kv=2, D=128, dtype=synth.BF16, contiguous=True, capacity=300, sinks=True)),
     ("f16_i8_contig", dict(kv_lens=[200, 90], q_lens=[150, 30], H_q=8, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.I8, contiguous=True, capacity=256, sinks=True)),
@@ -212,6 +217,39 @@ def test_short_kv_and_bad_blocks():
     assert_close(out, ref, synth.F16, "short_kv_bad_blocks")
     assert int(st.item()) == ost
     assert ost & oracle.STATUS_BAD_BLOCK and ost & oracle.STATUS_SHORT_KV
+
+
+@pytest.mark.parametrize("bs", [16, 5])
+def test_windowed_short_kv_bad_blocks_and_bounds(bs):
+    """The windowed span kernel (window 24, 8 query heads per KV head) over a table with a
+    block id past the pool and a negative one, a request with fewer keys than rows and one
+    over the query bound (zero rows): outputs and status bits against the oracle.  Block
+    size 16 reads the block ids by scalar loads, 5 per lane."""
+    kv, ql = [60, 160, 45, 50], [20, 60, 45, 30]
+    case = synth.paged_case(33 + bs, kv_lens=kv, q_lens=ql, H_q=16, H_kv=2, D=64,
+                            dtype=synth.F16, sinks=True, block_size=bs, local_window=24)
+    case.block_table = case.block_table.copy()
+    case.block_table[2, 1] = case.block_table.max() + 1000   # beyond the pool (keys in view)
+    case.block_table[2, 2] = -5
+    case.max_seqlen_q = 50                                     # request 2 (45) fits, 1 (60) does not
+    print("windowed short kv / bad blocks / bounds", bs, flush=True)
+    sk = case.seqlens_k.copy()
+    sk[3] = 19                                                 # request 3: 20 keys for 30 rows
+    t = case_tensors(case)
+    t["seqlens_k"] = tensor(sk, None)
+    st = status_tensor()
+    out = torch.empty((case.T, case.H_q, case.D), dtype=torch.float16, device="cuda")
+    sta.paged_attention_fwd(t["q"], t["k_cache"], t["v_cache"], t["cu"], t["seqlens_k"],
+                            case.max_seqlen_q, case.max_seqlen_k, out, block_table=t["block_table"],
+                            scale=case.scale, local_window=24, sinks=t["sinks"], status=st)
+    torch.cuda.synchronize()
+    ref, ost = oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.cu_seqlens_q, sk,
+                                      H_kv=2, block_table=case.block_table, block_size=bs,
+                                      max_seqlen_q=case.max_seqlen_q, max_seqlen_k=case.max_seqlen_k,
+                                      scale=case.scale, local_window=24, sinks=case.sinks)
+    assert_close(out, ref, synth.F16, f"windowed_short_kv_bad_blocks_bs{bs}")
+    assert int(st.item()) == ost
+    assert ost & oracle.STATUS_BAD_BLOCK and ost & oracle.STATUS_SHORT_KV and ost & oracle.STATUS_Q_BOUND
 
 
 def test_argument_errors_enqueue_nothing():
