@@ -214,6 +214,8 @@ def test_out_of_range_positions_and_cursor():
     cur = np.array([10, 0, 0], dtype=np.int32)   # request 1 disagrees; 0 and 2 agree
     _check(case, "cursor", committed_length=cur)
     _check(case, "both", position_ids=pos, committed_length=cur)
+    # the 40-row request disagrees (its waves resolve their request by the scalar path)
+    _check(case, "cursor, long request", committed_length=np.array([0, 6, 5], dtype=np.int32))
 
 
 def test_full_size_decode_step_shape():
