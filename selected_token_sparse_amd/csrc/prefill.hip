@@ -455,6 +455,25 @@ void prefill_kernel(PrefillParams P) {
   const uint32_t blk_bytes = (uint32_t)P.cd.H_kv * (uint32_t)bs * (uint32_t)(D * sizeof(KT));
   const char* kbytes = reinterpret_cast<const char*>(kcache + head_off);
   const char* vbytes = reinterpret_cast<const char*>(vcache + head_off);
+  // One DMA instruction covers kKeysPerInst consecutive keys.  With a power-of-two block
+  // size of at least that many keys, they lie in one block; when they are all in the key
+  // range and the block's id (read by a scalar load: the table is read-only here) is valid,
+  // the instruction's address is  block base (uniform) + a per-lane offset that is the same
+  // for every tile, so the tile's DMAs need no per-lane block lookup, bounds checks or
+  // address arithmetic.  Other instructions (range edges, missing blocks) go per lane.
+  constexpr int kKeysPerInst = 64 / CHK;
+  const bool uniform_dma = dma_fast && (1 << P.cd.bs_shift) >= kKeysPerInst;
+  const __attribute__((address_space(4))) int32_t* ctable =
+      (const __attribute__((address_space(4))) int32_t*)(paged ? P.cd.block_table + (int64_t)b * P.cd.max_blocks
+                                                               : nullptr);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t lane_off[kDmaPerWave];      // bytes from the instruction's first key row
+#pragma unroll
+  for (int n = 0; n < kDmaPerWave; ++n) {
+    const int p = (wave * kDmaPerWave + n) * 64 + lane;
+    const int key = p / CHK, slot = p % CHK;
+    lane_off[n] = (uint32_t)(((key % kKeysPerInst) * D + (slot ^ pf_swizzle<D>(key)) * 8) * sizeof(KT));
+  }
   auto issue_dma = [&](int kt, int stage) {
     unsigned char* base = smem + stage * L::kStage;
     int32_t* vb = reinterpret_cast<int32_t*>(base + L::kKBytes + L::kVBytes);
@@ -468,7 +487,20 @@ void prefill_kernel(PrefillParams P) {
       bool ok;
       const KT* kp;
       const KT* vp;
-      if (dma_fast) {
+      // the uniform case: first key of the instruction, its block and that block's id
+      const int ja = kt + (wave_u * kDmaPerWave + n) * kKeysPerInst;
+      int blk_u = -1;
+      if (uniform_dma && ja >= j_lo && ja + kKeysPerInst - 1 <= j_hi) {
+        const int lb = ja >> P.cd.bs_shift;
+        if (lb < P.cd.max_blocks) blk_u = ctable[lb];
+      }
+      if ((unsigned)blk_u < (unsigned)P.cd.num_blocks) {
+        ok = true;
+        const uint64_t boff = (uint64_t)(uint32_t)blk_u * blk_bytes +
+                              (uint32_t)(ja & (bs - 1)) * (uint32_t)(D * sizeof(KT));   // (uniform)
+        kp = reinterpret_cast<const KT*>(kbytes + boff + lane_off[n]);
+        vp = reinterpret_cast<const KT*>(vbytes + boff + lane_off[n]);
+      } else if (dma_fast) {
         const int j = kt + key;
         const int lb = j >> P.cd.bs_shift;
         const int blk = bt_lds[min(max(lb - win_lb, 0), L::kBtCap - 1)];
@@ -487,8 +519,10 @@ void prefill_kernel(PrefillParams P) {
         kp = ok ? kcache + off : safe_k + col;
         vp = ok ? vcache + off : safe_v + col;
       }
-      pf_dma16(kp, base + q * 1024);
-      pf_dma16(vp, base + L::kKBytes + q * 1024);
+      // (the LDS destination is uniform: wave_u keeps it in scalar registers)
+      const int q_u = wave_u * kDmaPerWave + n;
+      pf_dma16(kp, base + q_u * 1024);
+      pf_dma16(vp, base + L::kKBytes + q_u * 1024);
       if (slot == 0) vb[key] = ok ? 1 : 0;
       all_ok = all_ok && ok;
     }

@@ -97,6 +97,11 @@ PREFILL = [
     ("f16_w96_bs5", dict(kv_lens=[150, 61, 230], q_lens=[150, 40, 100], H_q=16, H_kv=2, D=64, dtype=synth.F16, block_size=5, sinks=True, local_window=96)),
     ("f16_w40_bs4_g4", dict(kv_lens=[130, 77], q_lens=[130, 60], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=4, local_window=40)),
     ("bf16_w128_bs32_d128", dict(kv_lens=[300, 45], q_lens=[260, 45], H_q=16, H_kv=2, D=128, dtype=synth.BF16, block_size=32, sinks=True, local_window=128)),
+    # the causal kernel's DMA: one uniform block per instruction (block sizes of at least
+    # 8 keys at D = 64, 4 at D = 128), per lane at range edges
+    ("f16_causal_bs8", dict(kv_lens=[200, 77], q_lens=[200, 50], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=8, sinks=True)),
+    ("f16_chunk_bs64_w70", dict(kv_lens=[300, 150], q_lens=[260, 150], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=64, local_window=70)),
+    ("bf16_causal_bs128_d128", dict(kv_lens=[400, 130], q_lens=[300, 130], H_q=8, H_kv=2, D=128, dtype=synth.BF16, block_size=128, sinks=True)),
     ("f16_contig_causal_chunked", dict(kv_lens=[500, 200, 33], q_lens=[120, 200, 9], H_q=8, H_kv=2, D=64, dtype=synth.F16, contiguous=True, capacity=512)),
     ("bf16_contig_d128_chunked_sink", dict(kv_lens=[260, 70], q_lens=[100, 70], H_q=8, H_kv=2, D=128, dtype=synth.BF16, contiguous=True, capacity=300, sinks=True)),
     ("f16_i8_contig", dict(kv_lens=[200, 90], q_lens=[150, 30], H_q=8, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.I8, contiguous=True, capacity=256, sinks=True)),
