@@ -120,7 +120,7 @@ __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsi
                                              KChunk k_chunk, VChunk v_chunk,
                                              const typename Op32<OpT>::v8 (&qop)[D / 16],
                                              const typename Op32<OpT>::v8 (&qlo)[kQlo ? D / 16 : 1],
-                                             Masks masks, float c_scale, float& m_run,
+                                             Masks masks, float c_scale, float lazy_raw, float& m_run,
                                              float& l_run, f32x16 (&acc)[D / 32]) {
   typedef typename Op32<OpT>::v8 V8;
   typedef typename Op32<OpT>::v4 V4;
@@ -138,14 +138,17 @@ __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsi
     if constexpr (kQlo) s = mfma32(a, qlo[kc], s);
   }
   masks(s);
-  float mt = s[0];
+  // the lane's maximum by a tree of three-input maxima (depth 3 instead of a chain of 8)
+  float m5[5];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
+  for (int k = 0; k < 5; ++k) m5[k] = fmaxf(fmaxf(s[3 * k], s[3 * k + 1]), s[3 * k + 2]);
+  float mt = fmaxf(fmaxf(fmaxf(m5[0], m5[1]), m5[2]), fmaxf(fmaxf(m5[3], m5[4]), s[15]));
   mt = half_swap_max(mt);                    // the row's other lane half
   const float m_new = fmaxf(m_run, mt);      // raw-score maximum of the row
   // the reference maximum moves only when some row's maximum outgrows it by more than
-  // kLazyRescaleLog2 (in the exponent); a row's first visible key always moves it
-  if (__ballot((m_new - m_run) * c_scale > kLazyRescaleLog2)) {
+  // kLazyRescaleLog2 in the exponent, i.e. by lazy_raw = kLazyRescaleLog2 / c_scale in raw
+  // scores; a row's first visible key always moves it (-inf + lazy_raw = -inf)
+  if (__ballot(m_new > m_run + lazy_raw)) {
     // rows whose max did not move keep alpha = 1 (including rows that have seen no key
     // yet: -inf - -inf must not reach the exponent); a row seeing its first key gets
     // alpha = 0 on acc = 0, l = 0
@@ -311,6 +314,7 @@ void prefill_kernel(PrefillParams P) {
   // is kept on raw scores q.k and the positive factor c = |scale| * log2(e) is applied inside
   // the exponent, so a negative scale is folded into the query's sign.
   const float c_scale = fabsf(P.scale_log2);
+  const float lazy_raw = kLazyRescaleLog2 / c_scale;   // the rescale threshold in raw scores
   const bool q_neg = P.scale_log2 < 0.f;
   // Quantised caches fold the per-channel key scale into the query and carry the folded
   // value x = q * s as hi + lo (hi = x rounded to the operand type, lo = its rounding error
@@ -585,12 +589,14 @@ void prefill_kernel(PrefillParams P) {
       const int32_t* vb = reinterpret_cast<const int32_t*>(base + L::kKBytes + L::kVBytes);
       // lane holds keys 8*(i/4) + 4*h + i%4 of row l32.  Masks only on tiles some row of the
       // wave does not fully see (the diagonal, the window edge, missing keys).
-      const i32x4 wflags = *reinterpret_cast<const i32x4*>(vb + kPfTile);
-      const bool tile_ok = (wflags[0] & wflags[1] & wflags[2] & wflags[3]) != 0;
-      const bool full = tile_ok && kt + kPfTile - 1 <= w_p_first &&
-                        (P.window <= 0 || kt >= w_p_last - P.window + 1);
+      // (the loaders' flags are read here, after the K operand reads are issued, so the two
+      // LDS round trips overlap)
+      const bool full_rows = kt + kPfTile - 1 <= w_p_first &&
+                             (P.window <= 0 || kt >= w_p_last - P.window + 1);
       auto masks = [&](f32x16& s) {
-        if (!full) {
+        const i32x4 wflags = *reinterpret_cast<const i32x4*>(vb + kPfTile);
+        const bool tile_ok = (wflags[0] & wflags[1] & wflags[2] & wflags[3]) != 0;
+        if (!(tile_ok && full_rows)) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int k0 = 8 * g4 + 4 * h;
@@ -605,7 +611,7 @@ void prefill_kernel(PrefillParams P) {
       };
       pf_tile_math<OpT, D, kI8>(reinterpret_cast<const unsigned char*>(kl),
                                 reinterpret_cast<const unsigned char*>(vl), k_chunk, v_chunk, qop,
-                                qlo, masks, c_scale, m_run, l_run, acc);
+                                qlo, masks, c_scale, lazy_raw, m_run, l_run, acc);
     }
   };
 
@@ -874,6 +880,7 @@ void prefill_window_kernel(PrefillParams P) {
 
   // ---- every head of this wave over the span ----
   const float c_scale = fabsf(P.scale_log2);
+  const float lazy_raw = kLazyRescaleLog2 / c_scale;   // the rescale threshold in raw scores
   const bool q_neg = P.scale_log2 < 0.f;
   const int my_p = pos0 + my_row;
   const int my_lo = max(0, my_p - P.window + 1);
@@ -913,7 +920,7 @@ void prefill_window_kernel(PrefillParams P) {
         }
       };
       pf_tile_math<QT, D, false>(smem + t * L::kTileBytes, smem + L::kVOff + t * L::kTileBytes,
-                                 k_chunk, k_chunk, qop, qlo, masks, c_scale, m_run, l_run, acc);
+                                 k_chunk, k_chunk, qop, qlo, masks, c_scale, lazy_raw, m_run, l_run, acc);
     }
     // finalise: sink, normalise, store (lane: row l32, dims 32m + 8(i/4) + 4h + i%4)
     l_run = half_swap_sum(l_run);
