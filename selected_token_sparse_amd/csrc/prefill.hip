@@ -129,6 +129,9 @@ __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsi
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int l32 = lane & 31;
+  // p = exp2(c * (s - m)) <= 2^8 with nm = -c m; a row with no visible key yet keeps p = 0.
+  // nm is formed here, off the tile's dependent chain, and again only when m moves.
+  float nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
   // S^T: A = K[key l32][16kc + 8h ..], B = qop
   f32x16 s = f32x16{};
 #pragma unroll
@@ -157,9 +160,8 @@ __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsi
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] *= alpha;
     m_run = m_new;
+    nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
   }
-  // p = exp2(c * (s - m)) <= 2^8; a row with no visible key yet keeps p = 0
-  const float nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
   // bf16 operands keep 8 significant bits: the weights are carried as hi + lo (hi = p
   // rounded, lo = its rounding error rounded) and PV takes one product with each, so
   // the weights keep about 16 bits, as f16 operands keep 11
