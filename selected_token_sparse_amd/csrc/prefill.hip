@@ -115,13 +115,24 @@ __device__ __forceinline__ void pf_wait_lgkm0() { asm volatile("s_waitcnt lgkmcn
 //   applied in the exponent; the running maximum is on raw scores)
 //   O^T[D x 32 rows] += V^T P^T     (V^T from LDS via ds_read_b64_tr_b16)
 // kchunk(kk, c) / vchunk(kk, c): byte offset of 16-byte chunk c of key kk in the K / V tile.
-template <typename OpT, int D, bool kQlo, typename KChunk, typename VChunk, typename Masks>
+//
+// kPair: two tiles in one softmax pass, for a full 32-row block of a window W that is a
+// multiple of 32: the first tile of its key span (keys j_lo + k, visible to row r when
+// k >= r) and the last (keys j_lo + W + k, visible when k < r) cover complementary
+// triangles, so each row sees exactly 32 of their 64 keys.  Both QK products are taken;
+// element i holds the key of the first tile when that key is at or after the row, else the
+// one of the second; the softmax runs once over the merged 16 elements, and the weights go
+// to the PV product of their own tile (0 in the other).  kl1 / vl1: the second tile.
+template <typename OpT, int D, bool kQlo, bool kPair = false, typename KChunk, typename VChunk,
+          typename Masks>
 __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsigned char* vl,
                                              KChunk k_chunk, VChunk v_chunk,
                                              const typename Op32<OpT>::v8 (&qop)[D / 16],
                                              const typename Op32<OpT>::v8 (&qlo)[kQlo ? D / 16 : 1],
                                              Masks masks, float c_scale, float lazy_raw, float& m_run,
-                                             float& l_run, f32x16 (&acc)[D / 32]) {
+                                             float& l_run, f32x16 (&acc)[D / 32],
+                                             const unsigned char* kl1 = nullptr,
+                                             const unsigned char* vl1 = nullptr) {
   typedef typename Op32<OpT>::v8 V8;
   typedef typename Op32<OpT>::v4 V4;
   constexpr int KC = D / 16;
@@ -134,13 +145,29 @@ __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsi
   float nm = m_run == kNegInf ? 0.f : -m_run * c_scale;
   // S^T: A = K[key l32][16kc + 8h ..], B = qop
   f32x16 s = f32x16{};
+  f32x16 s1 = f32x16{};
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
     V8 a = *reinterpret_cast<const V8*>(kl + k_chunk(l32, 2 * kc + h));
     s = mfma32(a, qop[kc], s);
     if constexpr (kQlo) s = mfma32(a, qlo[kc], s);
+    if constexpr (kPair) {
+      V8 a1 = *reinterpret_cast<const V8*>(kl1 + k_chunk(l32, 2 * kc + h));
+      s1 = mfma32(a1, qop[kc], s1);
+    }
   }
-  masks(s);
+  // (pair) first[i]: element i's key, 8 (i / 4) + 4 h + i % 4 of the tile, is at or after
+  // the lane's row, so it comes from the first tile
+  bool first[16];
+  if constexpr (kPair) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      first[i] = 8 * (i >> 2) + 4 * h + (i & 3) >= l32;
+      s[i] = first[i] ? s[i] : s1[i];
+    }
+  } else {
+    masks(s);
+  }
   // the lane's maximum by a tree of three-input maxima (depth 3 instead of a chain of 8)
   float m5[5];
 #pragma unroll
@@ -168,11 +195,23 @@ __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsi
   constexpr bool kSplitP = std::is_same<OpT, bf16>::value;
   V8 pop[2];
   V8 plo[kSplitP ? 2 : 1];
+  V8 pop1[kPair ? 2 : 1];
+  V8 plo1[kPair && kSplitP ? 2 : 1];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float p = exp2_safe(__builtin_fmaf(s[i], c_scale, nm));
-    pop[i >> 3][i & 7] = (OpT)p;
-    if constexpr (kSplitP) plo[i >> 3][i & 7] = (OpT)(p - (float)pop[i >> 3][i & 7]);
+    if constexpr (kPair) {
+      const float p0 = first[i] ? p : 0.f, p1 = first[i] ? 0.f : p;
+      pop[i >> 3][i & 7] = (OpT)p0;
+      pop1[i >> 3][i & 7] = (OpT)p1;
+      if constexpr (kSplitP) {
+        plo[i >> 3][i & 7] = (OpT)(p0 - (float)pop[i >> 3][i & 7]);
+        plo1[i >> 3][i & 7] = (OpT)(p1 - (float)pop1[i >> 3][i & 7]);
+      }
+    } else {
+      pop[i >> 3][i & 7] = (OpT)p;
+      if constexpr (kSplitP) plo[i >> 3][i & 7] = (OpT)(p - (float)pop[i >> 3][i & 7]);
+    }
   }
   // this lane's part of the row sum, over the rounded weights the PV product uses, two
   // per instruction (products with 1 are exact; the sum is fp32)
@@ -180,6 +219,10 @@ __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsi
   for (int i = 0; i < 16; i += 2) {
     l_run = dot2_ones(pop[i >> 3][i & 7], pop[i >> 3][(i & 7) + 1], l_run);
     if constexpr (kSplitP) l_run = dot2_ones(plo[i >> 3][i & 7], plo[i >> 3][(i & 7) + 1], l_run);
+    if constexpr (kPair) {
+      l_run = dot2_ones(pop1[i >> 3][i & 7], pop1[i >> 3][(i & 7) + 1], l_run);
+      if constexpr (kSplitP) l_run = dot2_ones(plo1[i >> 3][i & 7], plo1[i >> 3][(i & 7) + 1], l_run);
+    }
   }
   {
     const int grp = lane >> 4, lam = lane & 15;
@@ -201,6 +244,27 @@ __device__ __forceinline__ void pf_tile_math(const unsigned char* kl, const unsi
         V8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         acc[m] = mfma32(av, pop[ks], acc[m]);
         if constexpr (kSplitP) acc[m] = mfma32(av, plo[ks], acc[m]);
+      }
+  }
+  if constexpr (kPair) {   // the same product over the pair's second V tile
+    const int grp = lane >> 4, lam = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int vk = 16 * ks + 4 * h + (lam >> 2);
+        const int d = 32 * m + 16 * (grp & 1) + 4 * (lam & 3);
+        const OpT* a0 = reinterpret_cast<const OpT*>(vl1 + v_chunk(vk, d >> 3) + (d & 7) * 2);
+        const OpT* a1 = reinterpret_cast<const OpT*>(vl1 + v_chunk(vk + 8, d >> 3) + (d & 7) * 2);
+        s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a0));
+        s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a1));
+        V4 x0 = __builtin_bit_cast(V4, r0);
+        V4 x1 = __builtin_bit_cast(V4, r1);
+        V8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        acc[m] = mfma32(av, pop1[ks], acc[m]);
+        if constexpr (kSplitP) acc[m] = mfma32(av, plo1[ks], acc[m]);
       }
   }
 }
@@ -889,6 +953,9 @@ void prefill_window_kernel(PrefillParams P) {
   // rows of the block: the tiles every row sees whole are those inside
   // [lo(p_last), p_first]
   const int full_lo = max(0, p_last - P.window + 1), full_hi = p_first;
+  constexpr bool kPairEnds = !std::is_same<QT, bf16>::value;
+  const bool pair_ends = span_ok && rows == kWinRows && p_first - P.window + 1 >= 0 &&
+                         (P.window & (kPfTile - 1)) == 0 && n_tiles == P.window / kPfTile + 1;
   auto k_chunk = [&](int kk, int ch) -> int { return kk * D * 2 + ((ch ^ pf_swizzle<D>(kk)) << 4); };
   for (int hh = wave; hh < P.group; hh += NW) {
     const int head = c * P.group + hh;
@@ -902,7 +969,19 @@ void prefill_window_kernel(PrefillParams P) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
     float m_run = kNegInf, l_run = 0.f;
-    for (int t = 0; t < n_tiles; ++t) {
+    // a full block of a window that is a multiple of 32 (span W + 31 keys, W / 32 + 1 tiles)
+    // takes its first and last tiles in one pass; the tiles between are seen whole
+    // (fp16 only: bf16 carries the weights as hi + lo, and two tiles' of them spill)
+    int t_begin = 0, t_end = n_tiles;
+    if (kPairEnds && pair_ends) {
+      pf_tile_math<QT, D, false, kPairEnds>(smem, smem + L::kVOff, k_chunk, k_chunk, qop, qlo,
+                                       [](f32x16&) {}, c_scale, lazy_raw, m_run, l_run, acc,
+                                       smem + (n_tiles - 1) * L::kTileBytes,
+                                       smem + L::kVOff + (n_tiles - 1) * L::kTileBytes);
+      t_begin = 1;
+      t_end = n_tiles - 1;
+    }
+    for (int t = t_begin; t < t_end; ++t) {
       const int kt = j_lo + t * kPfTile;
       const bool full = span_ok && kt >= full_lo && kt + kPfTile - 1 <= full_hi;
       auto masks = [&](f32x16& s) {

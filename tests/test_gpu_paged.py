@@ -102,6 +102,12 @@ PREFILL = [
     ("f16_causal_bs8", dict(kv_lens=[200, 77], q_lens=[200, 50], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=8, sinks=True)),
     ("f16_chunk_bs64_w70", dict(kv_lens=[300, 150], q_lens=[260, 150], H_q=8, H_kv=2, D=64, dtype=synth.F16, block_size=64, local_window=70)),
     ("bf16_causal_bs128_d128", dict(kv_lens=[400, 130], q_lens=[300, 130], H_q=8, H_kv=2, D=128, dtype=synth.BF16, block_size=128, sinks=True)),
+    # the windowed kernel's first and last span tiles in one pass (fp16, a window that is a
+    # multiple of 32, full row blocks past the sequence start): W = 32 (the pair alone),
+    # W = 64 at D = 128, W = 96 in a chunk after a history
+    ("f16_w32_pair", dict(kv_lens=[130, 70], q_lens=[130, 70], H_q=8, H_kv=2, D=64, dtype=synth.F16, sinks=True, local_window=32)),
+    ("f16_w64_d128_pair", dict(kv_lens=[200, 90], q_lens=[200, 70], H_q=8, H_kv=2, D=128, dtype=synth.F16, sinks=True, local_window=64)),
+    ("f16_w96_chunk_pair", dict(kv_lens=[400, 160], q_lens=[100, 160], H_q=16, H_kv=2, D=64, dtype=synth.F16, local_window=96)),
     ("f16_contig_causal_chunked", dict(kv_lens=[500, 200, 33], q_lens=[120, 200, 9], H_q=8, H_kv=2, D=64, dtype=synth.F16, contiguous=True, capacity=512)),
     ("bf16_contig_d128_chunked_sink", dict(kv_lens=[260, 70], q_lens=[100, 70], H_q=8, H_kv=2, D=128, dtype=synth.BF16, contiguous=True, capacity=300, sinks=True)),
     ("f16_i8_contig", dict(kv_lens=[200, 90], q_lens=[150, 30], H_q=8, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.I8, contiguous=True, capacity=256, sinks=True)),
