@@ -108,6 +108,10 @@ PREFILL = [
     ("f16_w32_pair", dict(kv_lens=[130, 70], q_lens=[130, 70], H_q=8, H_kv=2, D=64, dtype=synth.F16, sinks=True, local_window=32)),
     ("f16_w64_d128_pair", dict(kv_lens=[200, 90], q_lens=[200, 70], H_q=8, H_kv=2, D=128, dtype=synth.F16, sinks=True, local_window=64)),
     ("f16_w96_chunk_pair", dict(kv_lens=[400, 160], q_lens=[100, 160], H_q=16, H_kv=2, D=64, dtype=synth.F16, local_window=96)),
+    # 8-bit caches: a wave's tile load in one block by a scalar table read (block size 8
+    # at D = 64, 4 keys a load at D = 128), per lane at range edges and for block size 4
+    ("f16_i8_bs8_chunk", dict(kv_lens=[300, 120], q_lens=[200, 120], H_q=8, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.I8, block_size=8, sinks=True)),
+    ("bf16_fp8_bs4_d128", dict(kv_lens=[150, 60], q_lens=[150, 40], H_q=8, H_kv=2, D=128, dtype=synth.BF16, cache_dtype=synth.FP8, block_size=4)),
     ("f16_contig_causal_chunked", dict(kv_lens=[500, 200, 33], q_lens=[120, 200, 9], H_q=8, H_kv=2, D=64, dtype=synth.F16, contiguous=True, capacity=512)),
     ("bf16_contig_d128_chunked_sink", dict(kv_lens=[260, 70], q_lens=[100, 70], H_q=8, H_kv=2, D=128, dtype=synth.BF16, contiguous=True, capacity=300, sinks=True)),
     ("f16_i8_contig", dict(kv_lens=[200, 90], q_lens=[150, 30], H_q=8, H_kv=2, D=64, dtype=synth.F16, cache_dtype=synth.I8, contiguous=True, capacity=256, sinks=True)),
