@@ -785,20 +785,26 @@ void prefill_kernel(PrefillParams P) {
 constexpr int kWinRows = 32;
 constexpr int kWinMax = 128;   // largest window this kernel takes
 
-template <int D>
+template <int D, int NW>
 struct WinLds {
   static constexpr int kMaxTiles = (kWinRows + kWinMax - 1 + kPfTile - 1) / kPfTile;
   static constexpr int kTileBytes = kPfTile * D * 2;      // K (or V) of one tile
   static constexpr int kVOff = kMaxTiles * kTileBytes;
   static constexpr int kOkOff = 2 * kMaxTiles * kTileBytes;   // one byte per span key
-  static constexpr int kTotal = kOkOff + kMaxTiles * kPfTile;
+  // each wave's 32 output rows, staged so that 16-byte lanes store whole rows; a row is
+  // padded by 16 bytes to spread the 8-byte writes of the accumulator layout over the banks
+  // (not with 4 waves at D = 64, whose 40 KB span area lets four workgroups share a CU)
+  static constexpr bool kStageOut = NW == 8 || D != 64;
+  static constexpr int kORow = D * 2 + 16;
+  static constexpr int kOOff = (kOkOff + kMaxTiles * kPfTile + 15) / 16 * 16;
+  static constexpr int kTotal = kStageOut ? kOOff + NW * kWinRows * kORow : kOkOff + kMaxTiles * kPfTile;
 };
 
 template <typename QT, int D, int NW>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<QT, D>(), 8)))
 void prefill_window_kernel(PrefillParams P) {
-  typedef WinLds<D> L;
+  typedef WinLds<D, NW> L;
   typedef typename Op32<QT>::v8 V8;
   constexpr int KC = D / 16;
   constexpr int MT = D / 32;
@@ -809,7 +815,7 @@ void prefill_window_kernel(PrefillParams P) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // (uniform: scalar)
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -1005,27 +1011,53 @@ void prefill_window_kernel(PrefillParams P) {
     }
     // finalise: sink, normalise, store (lane: row l32, dims 32m + 8(i/4) + 4h + i%4)
     l_run = half_swap_sum(l_run);
-    if (row_ok) {
-      QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
-      float f = 0.f, inv = 0.f;
-      if (m_run != kNegInf) {
-        const float ms = m_run * c_scale;
-        const float sraw = hh == wave ? sink_first : P.sinks != nullptr ? P.sinks[head] : 0.f;
-        const float sg = P.sinks != nullptr ? sraw * kLog2e : kNegInf;
-        const float M2 = fmaxf(ms, sg);
-        f = exp2_safe(ms - M2);
-        inv = f / (l_run * f + exp2_safe(sg - M2));
+    float f = 0.f, inv = 0.f;
+    if (row_ok && m_run != kNegInf) {
+      const float ms = m_run * c_scale;
+      const float sraw = hh == wave ? sink_first : P.sinks != nullptr ? P.sinks[head] : 0.f;
+      const float sg = P.sinks != nullptr ? sraw * kLog2e : kNegInf;
+      const float M2 = fmaxf(ms, sg);
+      f = exp2_safe(ms - M2);
+      inv = f / (l_run * f + exp2_safe(sg - M2));
+    }
+    // the normalised rows go to this wave's LDS rows, then out with 16 bytes a lane and
+    // D / 8 lanes a row (an 8-byte piece a lane in the accumulator layout would store each
+    // row as D / 4 separate pieces); the wave's LDS accesses complete in order, so the
+    // area is free again for its next head
+    if constexpr (!L::kStageOut) {
+      if (row_ok) {
+        QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * m + 8 * g4 + 4 * h;
+            typename Op32<QT>::v4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = from_f32<QT>(acc[m][4 * g4 + e] * inv);
+            *reinterpret_cast<typename Op32<QT>::v4*>(o + d0) = w;
+          }
       }
+      continue;
+    }
+    unsigned char* ost = smem + L::kOOff + wave * (kWinRows * L::kORow);
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * m + 8 * g4 + 4 * h;
-          typename Op32<QT>::v4 w;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * m + 8 * g4 + 4 * h;
+        typename Op32<QT>::v4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = from_f32<QT>(acc[m][4 * g4 + e] * inv);
-          *reinterpret_cast<typename Op32<QT>::v4*>(o + d0) = w;
-        }
+        for (int e = 0; e < 4; ++e) w[e] = from_f32<QT>(acc[m][4 * g4 + e] * inv);
+        *reinterpret_cast<typename Op32<QT>::v4*>(ost + l32 * L::kORow + d0 * 2) = w;
+      }
+    constexpr int kRowsPerStore = 64 / CHK;
+#pragma unroll
+    for (int i = 0; i < kWinRows / kRowsPerStore; ++i) {
+      const int r = i * kRowsPerStore + lane / CHK, ch = lane % CHK;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(ost + r * L::kORow + ch * 16);
+      if (row_base + r < q_len)
+        store16(reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + row_base + r) * P.H_q + head) * D + ch * 8, v);
     }
   }
   raise();
@@ -1068,9 +1100,9 @@ int launch_prefill_attention(const AttnArgs& a, hipStream_t stream) {
     const bool w8 = P.group >= 8;
 #define SPATTN_WIN(QT, DD)                                                                      \
   if (w8) hipLaunchKernelGGL((prefill_window_kernel<QT, DD, 8>), dim3(P.total), dim3(512),      \
-                             WinLds<DD>::kTotal, stream, P);                                    \
+                             (WinLds<DD, 8>::kTotal), stream, P);                               \
   else hipLaunchKernelGGL((prefill_window_kernel<QT, DD, 4>), dim3(P.total), dim3(256),         \
-                          WinLds<DD>::kTotal, stream, P)
+                          (WinLds<DD, 4>::kTotal), stream, P)
     if (a.D == 64) {
       if (a.dtype == SPATTN_F16) { SPATTN_WIN(f16, 64); } else { SPATTN_WIN(bf16, 64); }
     } else {
