@@ -739,30 +739,42 @@ void prefill_kernel(PrefillParams P) {
 
   // ---- finalise: sink, normalise, store (lane: row l32, dims 32m + 8(i/4) + 4h + i%4) ----
   l_run = half_swap_sum(l_run);                      // both lane halves of the row
-  if (row_ok) {
-    QT* o = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + my_row) * P.H_q + head) * D;
-    float f = 0.f, inv = 0.f;
-    if (m_run != kNegInf) {
-      const float ms = m_run * c_scale;                // log2-domain maximum
-      const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
-      const float M2 = fmaxf(ms, sg);
-      f = exp2_safe(ms - M2);
-      inv = f / (l_run * f + exp2_safe(sg - M2));
-    }
+  float f = 0.f, inv = 0.f;
+  if (row_ok && m_run != kNegInf) {
+    const float ms = m_run * c_scale;                // log2-domain maximum
+    const float sg = P.sinks != nullptr ? P.sinks[head] * kLog2e : kNegInf;
+    const float M2 = fmaxf(ms, sg);
+    f = exp2_safe(ms - M2);
+    inv = f / (l_run * f + exp2_safe(sg - M2));
+  }
+  // The wave's 32 rows go through LDS (the tile stages: every wave has passed the key
+  // loop's last barrier, so none reads them again) and out with 16 bytes a lane and D / 8
+  // lanes a row; in the accumulator layout each row would be stored as D / 4 separate
+  // 8-byte pieces.  Rows are padded by 16 bytes to spread the 8-byte writes over the banks.
+  constexpr int kORow = D * 2 + 16;
+  static_assert(L::kStages * L::kStage >= 4 * 32 * kORow, "output staging fits the tile stages");
+  unsigned char* ost = smem + wave * (32 * kORow);
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * m + 8 * g4 + 4 * h;
-        typename Op32<QT>::v4 w;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * m + 8 * g4 + 4 * h;
+      typename Op32<QT>::v4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = acc[m][4 * g4 + e] * inv;
-          if constexpr (kI8) x *= P.value_scale[c * D + d0 + e] * kUnit;
-          w[e] = from_f32<QT>(x);
-        }
-        *reinterpret_cast<typename Op32<QT>::v4*>(o + d0) = w;
+      for (int e = 0; e < 4; ++e) {
+        float x = acc[m][4 * g4 + e] * inv;
+        if constexpr (kI8) x *= P.value_scale[c * D + d0 + e] * kUnit;
+        w[e] = from_f32<QT>(x);
       }
+      *reinterpret_cast<typename Op32<QT>::v4*>(ost + l32 * kORow + d0 * 2) = w;
+    }
+  constexpr int kRowsPerStore = 64 / CH;
+#pragma unroll
+  for (int i = 0; i < 32 / kRowsPerStore; ++i) {
+    const int r = i * kRowsPerStore + lane / CH, ch = lane % CH;
+    const i32x4 v = *reinterpret_cast<const i32x4*>(ost + r * kORow + ch * 16);
+    if (head_ok && wrow0 + r < q_len)
+      store16(reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + wrow0 + r) * P.H_q + head) * D + ch * 8, v);
   }
   // flags from the loaders (keys visible to some row of the workgroup) and the row checks
   int wave_flags = 0;
