@@ -1064,12 +1064,14 @@ void prefill_window_kernel(PrefillParams P) {
         *reinterpret_cast<typename Op32<QT>::v4*>(ost + l32 * L::kORow + d0 * 2) = w;
       }
     constexpr int kRowsPerStore = 64 / CHK;
+    // (the block's first row of this head as a uniform base, each lane's place as a 32-bit
+    // element offset)
+    QT* const obase = reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + row_base) * P.H_q + head) * D;
 #pragma unroll
     for (int i = 0; i < kWinRows / kRowsPerStore; ++i) {
       const int r = i * kRowsPerStore + lane / CHK, ch = lane % CHK;
       const i32x4 v = *reinterpret_cast<const i32x4*>(ost + r * L::kORow + ch * 16);
-      if (row_base + r < q_len)
-        store16(reinterpret_cast<QT*>(P.out) + ((int64_t)(c0 + row_base + r) * P.H_q + head) * D + ch * 8, v);
+      if (row_base + r < q_len) store16(obase + (r * P.H_q * D + ch * 8), v);
     }
   }
   raise();
@@ -1103,7 +1105,9 @@ int launch_prefill_attention(const AttnArgs& a, hipStream_t stream) {
   P.scale_log2 = a.scale * kLog2e;
   // a window of at most kWinMax keys over a 16-bit cache, groups of 4 or more heads: the
   // one-span kernel (8 waves for groups of 8 or more, else 4)
-  if (a.window > 0 && a.window <= kWinMax && a.cache_dtype == a.dtype && P.group >= 4) {
+  // (the windowed kernel addresses a block's output rows by 32-bit offsets from its first)
+  if (a.window > 0 && a.window <= kWinMax && a.cache_dtype == a.dtype && P.group >= 4 &&
+      (int64_t)kWinRows * a.H_q * a.D < (int64_t(1) << 31)) {
     P.n_rt = (a.max_q + kWinRows - 1) / kWinRows;
     const long total = ((long)a.B * a.H_kv + 7) / 8 * 8 * P.n_rt;
     if (total <= 0) return SPATTN_OK;
